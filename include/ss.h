@@ -1,0 +1,180 @@
+/* ss.h -- C ABI of the structured-sparse quantised linear-layer library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the N:M structured-sparse, quantised matrix product of
+ * an LLM linear layer, Y = X W^T, with one operand in 2:4 form:
+ *   - weights: 2:4 magnitude prune along K into values plus 2-bit positions,
+ *     or a (2n-2):2n magnitude prune followed by the SlideSparse sliding-window
+ *     decomposition into n-1 overlapping stride-2 width-4 windows that each
+ *     satisfy 2:4, over an expanded K';
+ *   - activations: per-token dynamic INT8/FP8 quantisation fused with the
+ *     lift to K', or an online 2:4 prune and compress;
+ *   - the 2:4 product on the gfx950 structured-sparse matrix cores with a
+ *     per-token x per-channel rescale epilogue.
+ *
+ * Sources (page title, then section): "Deep reading of arXiv 2610.28947"
+ * (paper-daily.com) for 2:4 along the accumulate axis, the online pruning of
+ * activations and the bits accounting; "SlideSparse: layout sparse boundary"
+ * (MSRA article, 66bd.net) for the (2n-2):2n patterns, the window
+ * decomposition and activation lifting; the SlideSparse blog (omica.com.cn),
+ * sections 2.1-3.2, for the pattern table and the fused quantise-and-slide
+ * kernel; the LLM Compressor "compression schemes" guide for per-channel
+ * weight and dynamic per-token activation scales.
+ *
+ * Conventions shared by every call
+ *   Pointers: device pointers unless stated; 16-byte aligned. Matrices are
+ *   row-major with a leading dimension in ELEMENTS (metadata: in bytes); every
+ *   row start must be 16-byte aligned (ld * element size % 16 == 0).
+ *   Ownership: the caller allocates and owns every buffer; the library keeps no
+ *   device memory and no state between calls. Calls are re-entrant.
+ *   Streams: `stream` is a hipStream_t (NULL = the default stream). Work is
+ *   enqueued on it; no call synchronises.
+ *   Errors: arguments are checked on the host before anything is enqueued; on
+ *   failure nothing is launched, the status is returned and ss_last_error()
+ *   (per thread) describes it. SS_ERR_HIP reports a failed launch. Faults
+ *   inside a kernel surface at the caller's next synchronisation.
+ *   Empty problems (a zero row or column count) return SS_OK and launch
+ *   nothing.
+ *   Inputs must be finite (not checked).
+ *
+ * Pattern parameter n: (2n-2):2n, so n=2 is 2:4, n=3 is 4:6, n=4 is 6:8,
+ * n=5 is 8:10; 2 <= n <= 8.
+ *
+ * Compressed 2:4 layout (every sparse operand):
+ *   vals [rows][Kc/2] in the storage type: each 4-group of K keeps two slots,
+ *     stored in ascending position order; slots holding a zero store +0;
+ *   meta [rows][Kc/8] bytes: a group's nibble is idx0 | idx1 << 2 (idx0 <
+ *     idx1, positions 0..3 within the group); byte j holds group 2j in bits
+ *     0-3 and group 2j+1 in bits 4-7. Groups with fewer than two nonzeros fill
+ *     the second slot with the lowest free position; all-zero groups use
+ *     positions (0, 1). This is exactly the index operand of the gfx950
+ *     v_smfmac instructions, so the product reads it unchanged.
+ *   Kc = ss_lifted_k(K, n): K' rounded up to SS_KALIGN; the padding is
+ *     zero groups.
+ *
+ * Per-row symmetric quantisation (weights per output channel, activations per
+ * token), all in float32 with one rounding per step:
+ *   a = max|v| of the row; inv = Q / a (correctly rounded); t = v * inv; INT8 q = clamp(rint(t), -127, 127) (ties to even),
+ *   FP8 q = E4M3FN(clamp(t, -448, 448)) (OCP E4M3FN, nearest-even);
+ *   scale = a / Q; Q = 127 (INT8) or 448 (FP8). A zero row gives scale 0 and
+ *   zero codes.
+ */
+#ifndef SS_H
+#define SS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_VERSION 1
+#define SS_KALIGN 256 /* Kc of every sparse operand is a multiple of this */
+
+typedef enum {
+  SS_OK = 0,
+  SS_ERR_NULL = 1,        /* a required pointer is NULL */
+  SS_ERR_SHAPE = 2,       /* a size or leading dimension is invalid */
+  SS_ERR_ALIGN = 3,       /* a pointer or row start is not 16-byte aligned */
+  SS_ERR_DTYPE = 4,       /* unsupported data-type combination */
+  SS_ERR_PATTERN = 5,     /* n outside 2..8 */
+  SS_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  SS_ERR_HIP = 7          /* a HIP call or kernel launch failed */
+} ss_status;
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1, SS_I8 = 2, SS_FP8E4M3 = 3, SS_I32 = 4 } ss_dtype;
+
+typedef enum {
+  SS_SPARSE_W = 0, /* compressed operand = weights W' [N][Kc]; dense = activations [M][Kc] */
+  SS_SPARSE_X = 1  /* compressed operand = activations [M][Kc]; dense = weights W [N][Kc] */
+} ss_side;
+
+/* Kc for K original columns and pattern n: ceil(K/2n)*4(n-1) rounded up to
+ * SS_KALIGN (n = 2 gives K rounded up). Returns -1 for K < 0 or a bad n.
+ * SlideSparse article, sliding-window section (8 positions become 12). */
+int64_t ss_lifted_k(int64_t K, int n);
+/* The same without the SS_KALIGN rounding: ceil(K/2n)*4(n-1). */
+int64_t ss_lifted_k_logical(int64_t K, int n);
+
+const char* ss_status_string(int status);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* ss_last_error(void);
+int ss_version(void);
+
+/* ss_prune24 -- offline 2:4 weight preparation.
+ * Deep reading of arXiv 2610.28947 (introduction, section 2.3: magnitude
+ * pruning of the weight operand; 2:4 keeps two of every four consecutive
+ * elements along K) and the LLM Compressor guide (2:4 row: per-channel
+ * weight quantisation).
+ * W [rows][K] (F32 or BF16, row stride ldw elements), K % 4 == 0.
+ * Keeps the two largest |w| of every 4-group (ties keep the lower index),
+ * then per row: out_dt I8 / FP8E4M3 -> codes + scale[rows]; BF16 -> the kept
+ * values rounded to bf16 (from F32) or copied (from BF16), scale must be NULL.
+ * Outputs: vals [rows][Kc/2] (ldv elements), meta [rows][Kc/8] (ldm bytes),
+ * Kc = ss_lifted_k(K, 2). */
+ss_status ss_prune24(const void* W, ss_dtype w_dt, int64_t rows, int64_t K, int64_t ldw,
+                     ss_dtype out_dt, void* vals, int64_t ldv, uint8_t* meta, int64_t ldm,
+                     float* scale, void* stream);
+
+/* ss_slide_decompose -- offline (2n-2):2n weight preparation.
+ * SlideSparse article (sliding-window decomposition section; figure 2) and
+ * SlideSparse blog sections 2.2-2.3: zero-pad K to a multiple of 2n, keep the
+ * 2n-2 largest |w| of every 2n-group (ties keep the lower index), give each
+ * nonzero to one of the n-1 windows spanning positions 2w..2w+3 (each window,
+ * in order, takes the not yet taken nonzeros of its span in ascending position
+ * until it holds two), and write window w of group g as the 4-group
+ * (n-1)g + w of W' [rows][K']. Then per-row quantisation and 2:4 compression
+ * as in ss_prune24 (I8 / FP8E4M3 / BF16). n = 2 gives the same bytes as
+ * ss_prune24. Outputs span Kc = ss_lifted_k(K, n). Any K >= 1. */
+ss_status ss_slide_decompose(const void* W, ss_dtype w_dt, int64_t rows, int64_t K, int64_t ldw,
+                             int n, ss_dtype out_dt, void* vals, int64_t ldv, uint8_t* meta,
+                             int64_t ldm, float* scale, void* stream);
+
+/* ss_quant_lift_act -- online activation preparation (one fused pass).
+ * SlideSparse article (activation lifting is an index map fused into the
+ * per-token quantisation kernel) and SlideSparse blog section 3.2 (absmax,
+ * scale, quantise, clamp, slide and pack in one kernel; window base
+ * 2n*group + 2*offset). LLM Compressor guide: dynamic per-token scales.
+ * X [M][K] (BF16 or F32, ldx elements) -> per-token absmax over the original
+ * K, scale sx[M] (float32), codes q_dt (I8 or FP8E4M3) lifted to
+ * Xq [M][Kc] (ldq elements), Kc = ss_lifted_k(K, n):
+ *   Xq[m][4(n-1)g + 4w + j] = q(X[m][2n g + 2w + j]), sources >= K and the
+ *   padding columns are 0. n = 2 is plain per-token quantisation (no lift). */
+ss_status ss_quant_lift_act(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, int n,
+                            ss_dtype q_dt, void* Xq, int64_t ldq, float* sx, void* stream);
+
+/* ss_prune24_act -- online 2:4 prune and compress of activations.
+ * Deep reading of arXiv 2610.28947, section 1 (activations are produced at
+ * run time and must be pruned and compressed before every product; that time
+ * counts) and section 2.3. X [M][K] BF16, K % 4 == 0: keep the two largest
+ * bf16 magnitudes of every 4-group (ties keep the lower index). out_dt BF16:
+ * values copied, sx must be NULL; I8 / FP8E4M3: per-token scale sx[M] from
+ * the row absmax and the kept values quantised. Outputs span
+ * Kc = ss_lifted_k(K, 2). */
+ss_status ss_prune24_act(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                         ss_dtype out_dt, void* vals, int64_t ldv, uint8_t* meta, int64_t ldm,
+                         float* sx, void* stream);
+
+/* ss_spgemm -- the 2:4 sparse product with the rescale epilogue.
+ * Deep reading of arXiv 2610.28947 (introduction: one operand keeps two of
+ * every four along the accumulate axis; section 3.1: sparse-weight and
+ * sparse-activation cases) and SlideSparse blog section 2.2 step 3; the
+ * rescale follows the LLM Compressor W8A8 scheme.
+ *   side SS_SPARSE_W: sp = W' vals/meta [N][Kc], dense = X' [M][Kc].
+ *   side SS_SPARSE_X: sp = X vals/meta [M][Kc], dense = W [N][Kc].
+ *   acc[m][n] = sum_k X'[m][k] W'[n][k]  (i32 for I8; f32 for FP8E4M3/BF16)
+ *   Y[m][n] = fl32(fl32(float(acc) * sx[m]) * sw[n]) rounded to y_dt (BF16:
+ *   nearest-even); a NULL sx or sw skips that factor. y_dt SS_I32 (I8 only)
+ *   stores the raw accumulator and ignores sx/sw.
+ * ab_dt: I8, FP8E4M3 or BF16 for both operands. Kc % SS_KALIGN == 0.
+ * Y [M][N] with ldy elements; Y itself must be 16-byte aligned, its rows need
+ * not be. M, N may be any size >= 0. */
+ss_status ss_spgemm(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt,
+                    const void* sp_vals, int64_t ldsv, const uint8_t* sp_meta, int64_t ldsm,
+                    const void* dense, int64_t ldd, const float* sx, const float* sw,
+                    ss_dtype y_dt, void* Y, int64_t ldy, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SS_H */

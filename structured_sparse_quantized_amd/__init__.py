@@ -1,0 +1,169 @@
+"""Python binding of ``libss.so``, the gfx950 structured-sparse quantised GEMM library.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in ``include/ss.h``. PyTorch supplies device memory and the current
+stream. There is no CPU fallback: importing this package raises if the
+library has not been built, and every call raises ``SSError`` on a non-OK
+status.
+
+Functions keep the names of the C entry points:
+
+    lifted_k(K, n)                          -> Kc (K' rounded up to KALIGN)
+    prune24(W, out_dtype)                   -> (vals, meta, scale | None)
+    slide_decompose(W, n, out_dtype)        -> (vals, meta, scale | None)
+    quant_lift_act(X, n, q_dtype)           -> (Xq, sx)
+    prune24_act(X, out_dtype)               -> (vals, meta, sx | None)
+    spgemm(side, M, N, Kc, vals, meta, dense, sx, sw, y_dtype) -> Y [M, N]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libss.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with structured_sparse_quantized_amd.build.build()")
+lib = ctypes.CDLL(_LIB_PATH)
+
+SS_OK, SS_ERR_NULL, SS_ERR_SHAPE, SS_ERR_ALIGN, SS_ERR_DTYPE, SS_ERR_PATTERN, SS_ERR_UNSUPPORTED, SS_ERR_HIP = range(8)
+SS_F32, SS_BF16, SS_I8, SS_FP8E4M3, SS_I32 = range(5)
+SS_SPARSE_W, SS_SPARSE_X = 0, 1
+KALIGN = 256
+
+_i64, _int, _vp, _fp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p
+lib.ss_lifted_k.argtypes = [_i64, _int]
+lib.ss_lifted_k.restype = _i64
+lib.ss_lifted_k_logical.argtypes = [_i64, _int]
+lib.ss_lifted_k_logical.restype = _i64
+lib.ss_status_string.argtypes = [_int]
+lib.ss_status_string.restype = ctypes.c_char_p
+lib.ss_last_error.argtypes = []
+lib.ss_last_error.restype = ctypes.c_char_p
+lib.ss_version.restype = _int
+lib.ss_prune24.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _fp, _vp]
+lib.ss_slide_decompose.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64, _fp, _vp]
+lib.ss_quant_lift_act.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp, _i64, _fp, _vp]
+lib.ss_prune24_act.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _fp, _vp]
+lib.ss_spgemm.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
+for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm"):
+    getattr(lib, _f).restype = _int
+
+EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_error", "ss_version",
+           "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm")
+
+
+class SSError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = lib.ss_status_string(status).decode()
+        detail = lib.ss_last_error().decode()
+        super().__init__(f"{msg}: {detail}")
+
+
+def _check(status: int) -> None:
+    if status != SS_OK:
+        raise SSError(status)
+
+
+_TORCH = {
+    SS_F32: torch.float32, SS_BF16: torch.bfloat16, SS_I8: torch.int8,
+    SS_FP8E4M3: torch.float8_e4m3fn, SS_I32: torch.int32,
+}
+_NAMES = {"f32": SS_F32, "bf16": SS_BF16, "i8": SS_I8, "fp8": SS_FP8E4M3, "i32": SS_I32}
+_FROM_TORCH = {v: k for k, v in _TORCH.items()}
+
+
+def dtype_code(d) -> int:
+    if isinstance(d, int):
+        return d
+    if isinstance(d, str):
+        return _NAMES[d]
+    return _FROM_TORCH[d]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ld(t: torch.Tensor) -> int:
+    assert t.dim() == 2 and t.stride(1) == 1, "row-major 2-D tensor expected"
+    return t.stride(0)
+
+
+def lifted_k(K: int, n: int) -> int:
+    return int(lib.ss_lifted_k(K, n))
+
+
+def lifted_k_logical(K: int, n: int) -> int:
+    return int(lib.ss_lifted_k_logical(K, n))
+
+
+def _alloc_sparse(rows, Kc, out, device):
+    vals = torch.empty((rows, Kc // 2), dtype=_TORCH[out], device=device)
+    meta = torch.empty((rows, Kc // 8), dtype=torch.uint8, device=device)
+    scale = None if out == SS_BF16 else torch.empty(rows, dtype=torch.float32, device=device)
+    return vals, meta, scale
+
+
+def prune24(W: torch.Tensor, out_dtype="i8", out=None):
+    """Offline 2:4 weight prune + per-channel quantisation + compression."""
+    o = dtype_code(out_dtype)
+    rows, K = W.shape
+    Kc = lifted_k(K, 2)
+    vals, meta, scale = out if out is not None else _alloc_sparse(rows, Kc, o, W.device)
+    _check(lib.ss_prune24(_ptr(W), dtype_code(W.dtype), rows, K, _ld(W), o, _ptr(vals), _ld(vals), _ptr(meta),
+                          _ld(meta), _ptr(scale), _stream(W.device)))
+    return vals, meta, scale
+
+
+def slide_decompose(W: torch.Tensor, n: int, out_dtype="i8", out=None):
+    """Offline (2n-2):2n prune + sliding-window decomposition to 2:4 over K'."""
+    o = dtype_code(out_dtype)
+    rows, K = W.shape
+    Kc = lifted_k(K, n)
+    vals, meta, scale = out if out is not None else _alloc_sparse(rows, Kc, o, W.device)
+    _check(lib.ss_slide_decompose(_ptr(W), dtype_code(W.dtype), rows, K, _ld(W), n, o, _ptr(vals), _ld(vals),
+                                  _ptr(meta), _ld(meta), _ptr(scale), _stream(W.device)))
+    return vals, meta, scale
+
+
+def quant_lift_act(X: torch.Tensor, n: int = 2, q_dtype="i8", out=None):
+    """Fused per-token quantisation and lift to K' (n = 2: no lift)."""
+    q = dtype_code(q_dtype)
+    M, K = X.shape
+    Kc = lifted_k(K, n)
+    if out is None:
+        Xq = torch.empty((M, Kc), dtype=_TORCH[q], device=X.device)
+        sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    else:
+        Xq, sx = out
+    _check(lib.ss_quant_lift_act(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), n, q, _ptr(Xq), _ld(Xq), _ptr(sx),
+                                 _stream(X.device)))
+    return Xq, sx
+
+
+def prune24_act(X: torch.Tensor, out_dtype="bf16", out=None):
+    """Online 2:4 prune + compress of bf16 activations (optionally quantised)."""
+    o = dtype_code(out_dtype)
+    M, K = X.shape
+    Kc = lifted_k(K, 2)
+    vals, meta, sx = out if out is not None else _alloc_sparse(M, Kc, o, X.device)
+    _check(lib.ss_prune24_act(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), o, _ptr(vals), _ld(vals), _ptr(meta),
+                              _ld(meta), _ptr(sx), _stream(X.device)))
+    return vals, meta, sx
+
+
+def spgemm(side: int, M: int, N: int, Kc: int, vals: torch.Tensor, meta: torch.Tensor, dense: torch.Tensor,
+           sx=None, sw=None, y_dtype="bf16", out=None):
+    """Y [M, N] = sparse x dense product with the per-token x per-channel rescale."""
+    y = dtype_code(y_dtype)
+    Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
+    _check(lib.ss_spgemm(side, M, N, Kc, dtype_code(vals.dtype), _ptr(vals), _ld(vals), _ptr(meta), _ld(meta),
+                         _ptr(dense), _ld(dense), _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _stream(dense.device)))
+    return Y

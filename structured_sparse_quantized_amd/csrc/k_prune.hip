@@ -1,0 +1,168 @@
+// 2:4 magnitude prune + compress along K, for weights (offline; per-channel
+// scales) and activations (online; per-token scales). Deep reading of arXiv
+// 2610.28947, introduction and sections 1 and 2.3; LLM Compressor guide for
+// the scale granularity.
+//
+// One workgroup per row. A "unit" is 4 consecutive 4-groups (16 input
+// elements) and produces 8 kept values and 2 metadata bytes. When quantised
+// output is requested the row absmax is reduced first; units that fit in the
+// per-thread register budget are read from HBM only once.
+#include "ss_device.h"
+#include "ss_kernels.h"
+
+namespace ss {
+
+template <typename TIn> struct Unit;
+template <> struct Unit<uint16_t> {  // 16 bf16 = 2 x 16 bytes
+  uint4 a, b;
+  __device__ void load(const uint16_t* p) {
+    a = reinterpret_cast<const uint4*>(p)[0];
+    b = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ uint32_t bits(int i) const {
+    const uint4& v = (i < 8) ? a : b;
+    const uint32_t w = (&v.x)[(i & 7) >> 1];
+    return (i & 1) ? (w >> 16) : (w & 0xFFFF);
+  }
+  __device__ float val(int i) const { return bf16_to_f32((uint16_t)bits(i)); }
+  __device__ uint32_t key(int i) const { return mag_key_bf16((uint16_t)bits(i)); }
+};
+template <> struct Unit<float> {  // 16 float = 4 x 16 bytes
+  uint4 q[4];
+  __device__ void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = reinterpret_cast<const uint4*>(p)[i];
+  }
+  __device__ float val(int i) const { return __uint_as_float((&q[i >> 2].x)[i & 3]); }
+  __device__ uint32_t key(int i) const { return mag_key_f32(val(i)); }
+};
+
+// OUT: 0 = int8, 1 = fp8, 2 = bf16
+template <typename TIn, int OUT>
+__device__ __forceinline__ void emit_unit(const Unit<TIn>& u, bool zero_row, float inv, uint8_t* vrow,
+                                          uint8_t* mrow, int64_t unit) {
+  uint32_t meta = 0;
+  float kv[8];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t nib = top2_nibble(u.key(4 * g), u.key(4 * g + 1), u.key(4 * g + 2), u.key(4 * g + 3));
+    meta |= nib << (4 * g);
+    const float v0 = u.val(4 * g + (nib & 3)), v1 = u.val(4 * g + (nib >> 2));
+    kv[2 * g] = (v0 == 0.0f) ? 0.0f : v0;  // zeros are stored as +0
+    kv[2 * g + 1] = (v1 == 0.0f) ? 0.0f : v1;
+  }
+  *reinterpret_cast<uint16_t*>(mrow + unit * 2) = (uint16_t)meta;
+  if constexpr (OUT == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(kv[2 * i]) | ((uint32_t)f32_to_bf16(kv[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(vrow + unit * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    uint32_t w[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = zero_row ? 0u : (uint32_t)Quant<OUT == 1>::code(kv[i], inv);
+      w[i >> 2] |= c << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint2*>(vrow + unit * 8) = make_uint2(w[0], w[1]);
+  }
+}
+
+template <typename TIn> __device__ __forceinline__ void load_unit(Unit<TIn>& u, const TIn* xr, int64_t unit, int64_t K) {
+  const int64_t e0 = unit * 16;
+  if (e0 + 16 <= K) {
+    u.load(xr + e0);
+  } else {  // ragged end of the row (K % 16 != 0) and padding units: zeros beyond K
+    alignas(16) TIn tmp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmp[i] = (e0 + i < K) ? xr[e0 + i] : (TIn)0;
+    u.load(tmp);
+  }
+}
+
+template <typename TIn> __device__ __forceinline__ float unit_absmax(const Unit<TIn>& u) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(u.val(i)));
+  return m;
+}
+
+constexpr int kUPT = 4;  // units per thread kept in registers
+
+template <typename TIn, int OUT>
+__global__ __launch_bounds__(kBlock) void prune24_kernel(const TIn* __restrict__ X, int64_t ldx, int64_t K,
+                                                         uint8_t* __restrict__ vals, int64_t ldv_bytes,
+                                                         uint8_t* __restrict__ meta, int64_t ldm,
+                                                         int64_t Kc, float* __restrict__ scale) {
+  __shared__ float red[kBlock / 64];
+  const int64_t row = blockIdx.x;
+  const TIn* xr = X + row * ldx;
+  uint8_t* vr = vals + row * ldv_bytes;
+  uint8_t* mr = meta + row * ldm;
+  const int tid = threadIdx.x;
+  const int64_t units = Kc / 16;         // includes padding units (all zero)
+  const int64_t data_units = (K + 15) / 16;
+
+  Unit<TIn> u[kUPT];
+  float amax = 0.0f;
+  bool zero_row = false;
+  float inv = 0.0f;
+  if constexpr (OUT != 2) {
+#pragma unroll
+    for (int i = 0; i < kUPT; ++i) {
+      const int64_t un = tid + (int64_t)i * kBlock;
+      if (un < data_units) {
+        load_unit(u[i], xr, un, K);
+        amax = fmaxf(amax, unit_absmax(u[i]));
+      }
+    }
+    for (int64_t un = tid + (int64_t)kUPT * kBlock; un < data_units; un += kBlock) {
+      Unit<TIn> t;
+      load_unit(t, xr, un, K);
+      amax = fmaxf(amax, unit_absmax(t));
+    }
+    amax = block_max(amax, red);
+    constexpr float Q = (OUT == 1) ? 448.0f : 127.0f;
+    zero_row = (amax == 0.0f);
+    inv = zero_row ? 0.0f : Q / amax;
+    if (tid == 0) scale[row] = zero_row ? 0.0f : amax / Q;
+  }
+#pragma unroll
+  for (int i = 0; i < kUPT; ++i) {
+    const int64_t un = tid + (int64_t)i * kBlock;
+    if (un < units) {
+      if (OUT == 2 || un >= data_units) {
+        if (un < data_units) load_unit(u[i], xr, un, K);
+        else u[i] = Unit<TIn>{};
+      }
+      emit_unit<TIn, OUT>(u[i], zero_row, inv, vr, mr, un);
+    }
+  }
+  for (int64_t un = tid + (int64_t)kUPT * kBlock; un < units; un += kBlock) {
+    Unit<TIn> t{};
+    if (un < data_units) load_unit(t, xr, un, K);
+    emit_unit<TIn, OUT>(t, zero_row, inv, vr, mr, un);
+  }
+}
+
+template <typename TIn>
+static hipError_t launch_p24(int out, const TIn* X, int64_t ldx, int64_t M, int64_t K, void* vals, int64_t ldv_bytes,
+                             uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
+  dim3 grid((unsigned)M), block(kBlock);
+  uint8_t* v = static_cast<uint8_t*>(vals);
+  switch (out) {
+    case 0: hipLaunchKernelGGL((prune24_kernel<TIn, 0>), grid, block, 0, st, X, ldx, K, v, ldv_bytes, meta, ldm, Kc, scale); break;
+    case 1: hipLaunchKernelGGL((prune24_kernel<TIn, 1>), grid, block, 0, st, X, ldx, K, v, ldv_bytes, meta, ldm, Kc, scale); break;
+    default: hipLaunchKernelGGL((prune24_kernel<TIn, 2>), grid, block, 0, st, X, ldx, K, v, ldv_bytes, meta, ldm, Kc, scale); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prune24(bool in_bf16, int out, const void* X, int64_t ldx, int64_t M, int64_t K, void* vals,
+                          int64_t ldv_bytes, uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
+  if (in_bf16)
+    return launch_p24<uint16_t>(out, static_cast<const uint16_t*>(X), ldx, M, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+  return launch_p24<float>(out, static_cast<const float*>(X), ldx, M, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+}
+
+}  // namespace ss

@@ -1,0 +1,197 @@
+// C ABI of the library: host-side argument validation, then one kernel launch
+// per call on the caller's stream. Nothing is enqueued when validation fails.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "ss.h"
+#include "ss_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ss_status fail(ss_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ss_status ok() {
+  g_err[0] = 0;
+  return SS_OK;
+}
+
+ss_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int esize(ss_dtype t) {
+  switch (t) {
+    case SS_F32: case SS_I32: return 4;
+    case SS_BF16: return 2;
+    case SS_I8: case SS_FP8E4M3: return 1;
+  }
+  return 0;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Row starts of a [rows x cols] matrix with leading dimension ld (elements).
+ss_status check_mat(const char* name, const void* p, int64_t rows, int64_t cols, int64_t ld, int es) {
+  if (!p) return fail(SS_ERR_NULL, "%s is NULL", name);
+  if (ld < cols) return fail(SS_ERR_SHAPE, "%s: leading dimension %lld < %lld columns", name, (long long)ld, (long long)cols);
+  if (!aligned16(p)) return fail(SS_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  if (rows > 1 && (ld * es) % 16 != 0)
+    return fail(SS_ERR_ALIGN, "%s: row stride of %lld bytes is not a multiple of 16", name, (long long)(ld * es));
+  return SS_OK;
+}
+
+int out_code(ss_dtype t) { return t == SS_I8 ? 0 : t == SS_FP8E4M3 ? 1 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t ss_lifted_k_logical(int64_t K, int n) {
+  if (K < 0 || n < 2 || n > 8) return -1;
+  return (K + 2 * n - 1) / (2 * n) * 4 * (n - 1);
+}
+
+int64_t ss_lifted_k(int64_t K, int n) {
+  const int64_t k = ss_lifted_k_logical(K, n);
+  if (k < 0) return -1;
+  return (k + SS_KALIGN - 1) / SS_KALIGN * SS_KALIGN;
+}
+
+const char* ss_status_string(int s) {
+  switch (s) {
+    case SS_OK: return "SS_OK";
+    case SS_ERR_NULL: return "SS_ERR_NULL";
+    case SS_ERR_SHAPE: return "SS_ERR_SHAPE";
+    case SS_ERR_ALIGN: return "SS_ERR_ALIGN";
+    case SS_ERR_DTYPE: return "SS_ERR_DTYPE";
+    case SS_ERR_PATTERN: return "SS_ERR_PATTERN";
+    case SS_ERR_UNSUPPORTED: return "SS_ERR_UNSUPPORTED";
+    case SS_ERR_HIP: return "SS_ERR_HIP";
+  }
+  return "unknown status";
+}
+
+const char* ss_last_error(void) { return g_err; }
+int ss_version(void) { return SS_VERSION; }
+
+static ss_status check_weight_prep(const void* W, ss_dtype w_dt, int64_t rows, int64_t K, int64_t ldw,
+                                   ss_dtype out_dt, void* vals, int64_t ldv, uint8_t* meta, int64_t ldm,
+                                   float* scale, int64_t Kc) {
+  if (w_dt != SS_F32 && w_dt != SS_BF16) return fail(SS_ERR_DTYPE, "input must be F32 or BF16");
+  if (out_dt != SS_I8 && out_dt != SS_FP8E4M3 && out_dt != SS_BF16)
+    return fail(SS_ERR_DTYPE, "output must be I8, FP8E4M3 or BF16");
+  if (rows < 0 || K < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (rows > 0x7FFFFFFF) return fail(SS_ERR_SHAPE, "too many rows");
+  if (rows == 0 || K == 0) return SS_OK;
+  ss_status s;
+  if ((s = check_mat("input", W, rows, K, ldw, esize(w_dt))) != SS_OK) return s;
+  if ((s = check_mat("vals", vals, rows, Kc / 2, ldv, esize(out_dt))) != SS_OK) return s;
+  if ((s = check_mat("meta", meta, rows, Kc / 8, ldm, 1)) != SS_OK) return s;
+  if (out_dt == SS_BF16) {
+    if (scale) return fail(SS_ERR_DTYPE, "BF16 output takes no scale (pass NULL)");
+  } else if (!scale) {
+    return fail(SS_ERR_NULL, "scale is NULL");
+  }
+  return SS_OK;
+}
+
+ss_status ss_prune24(const void* W, ss_dtype w_dt, int64_t rows, int64_t K, int64_t ldw, ss_dtype out_dt,
+                     void* vals, int64_t ldv, uint8_t* meta, int64_t ldm, float* scale, void* stream) {
+  if (K % 4 != 0) return fail(SS_ERR_SHAPE, "K=%lld is not a multiple of 4", (long long)K);
+  const int64_t Kc = ss_lifted_k(K, 2);
+  ss_status s = check_weight_prep(W, w_dt, rows, K, ldw, out_dt, vals, ldv, meta, ldm, scale, Kc);
+  if (s != SS_OK) return s;
+  if (rows == 0 || K == 0) return ok();
+  return hip_status(ss::launch_prune24(w_dt == SS_BF16, out_code(out_dt), W, ldw, rows, K, vals, ldv * esize(out_dt),
+                                       meta, ldm, Kc, scale, (hipStream_t)stream),
+                    "ss_prune24 launch");
+}
+
+ss_status ss_slide_decompose(const void* W, ss_dtype w_dt, int64_t rows, int64_t K, int64_t ldw, int n,
+                             ss_dtype out_dt, void* vals, int64_t ldv, uint8_t* meta, int64_t ldm, float* scale,
+                             void* stream) {
+  if (n < 2 || n > 8) return fail(SS_ERR_PATTERN, "n=%d outside 2..8", n);
+  const int64_t Kc = ss_lifted_k(K, n);
+  ss_status s = check_weight_prep(W, w_dt, rows, K, ldw, out_dt, vals, ldv, meta, ldm, scale, Kc);
+  if (s != SS_OK) return s;
+  if (rows == 0 || K == 0) return ok();
+  return hip_status(ss::launch_slide(w_dt == SS_BF16, out_code(out_dt), W, ldw, rows, K, n, vals, ldv * esize(out_dt),
+                                     meta, ldm, Kc, scale, (hipStream_t)stream),
+                    "ss_slide_decompose launch");
+}
+
+ss_status ss_quant_lift_act(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, int n, ss_dtype q_dt,
+                            void* Xq, int64_t ldq, float* sx, void* stream) {
+  if (n < 2 || n > 8) return fail(SS_ERR_PATTERN, "n=%d outside 2..8", n);
+  if (x_dt != SS_F32 && x_dt != SS_BF16) return fail(SS_ERR_DTYPE, "input must be F32 or BF16");
+  if (q_dt != SS_I8 && q_dt != SS_FP8E4M3) return fail(SS_ERR_DTYPE, "output must be I8 or FP8E4M3");
+  if (M < 0 || K < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (M > 0x7FFFFFFF) return fail(SS_ERR_SHAPE, "too many rows");
+  if (M == 0 || K == 0) return ok();
+  const int64_t Kc = ss_lifted_k(K, n);
+  ss_status s;
+  if ((s = check_mat("X", X, M, K, ldx, esize(x_dt))) != SS_OK) return s;
+  if ((s = check_mat("Xq", Xq, M, Kc, ldq, 1)) != SS_OK) return s;
+  if (!sx) return fail(SS_ERR_NULL, "sx is NULL");
+  return hip_status(ss::launch_quant_lift(x_dt == SS_BF16, q_dt == SS_FP8E4M3, X, ldx, M, K, n, Xq, ldq, Kc, sx,
+                                          (hipStream_t)stream),
+                    "ss_quant_lift_act launch");
+}
+
+ss_status ss_prune24_act(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, ss_dtype out_dt, void* vals,
+                         int64_t ldv, uint8_t* meta, int64_t ldm, float* sx, void* stream) {
+  if (x_dt != SS_BF16) return fail(SS_ERR_DTYPE, "activations must be BF16");
+  if (K % 4 != 0) return fail(SS_ERR_SHAPE, "K=%lld is not a multiple of 4", (long long)K);
+  const int64_t Kc = ss_lifted_k(K, 2);
+  ss_status s = check_weight_prep(X, x_dt, M, K, ldx, out_dt, vals, ldv, meta, ldm, sx, Kc);
+  if (s != SS_OK) return s;
+  if (M == 0 || K == 0) return ok();
+  return hip_status(ss::launch_prune24(true, out_code(out_dt), X, ldx, M, K, vals, ldv * esize(out_dt), meta, ldm, Kc,
+                                       sx, (hipStream_t)stream),
+                    "ss_prune24_act launch");
+}
+
+ss_status ss_spgemm(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* sp_vals, int64_t ldsv,
+                    const uint8_t* sp_meta, int64_t ldsm, const void* dense, int64_t ldd, const float* sx,
+                    const float* sw, ss_dtype y_dt, void* Y, int64_t ldy, void* stream) {
+  if (side != SS_SPARSE_W && side != SS_SPARSE_X) return fail(SS_ERR_SHAPE, "bad side");
+  if (ab_dt != SS_I8 && ab_dt != SS_FP8E4M3 && ab_dt != SS_BF16)
+    return fail(SS_ERR_DTYPE, "operands must be I8, FP8E4M3 or BF16");
+  if (y_dt != SS_BF16 && y_dt != SS_F32 && y_dt != SS_I32) return fail(SS_ERR_DTYPE, "output must be BF16, F32 or I32");
+  if (y_dt == SS_I32 && ab_dt != SS_I8) return fail(SS_ERR_DTYPE, "I32 output needs I8 operands");
+  if (M < 0 || N < 0 || Kc < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (Kc % SS_KALIGN != 0) return fail(SS_ERR_SHAPE, "Kc=%lld is not a multiple of %d", (long long)Kc, SS_KALIGN);
+  if (M > 0x7FFFFFFFLL * 128 || N > 0x7FFFFFFFLL * 128) return fail(SS_ERR_SHAPE, "too many rows");
+  if (M == 0 || N == 0) return ok();
+  const bool sx_side = (side == SS_SPARSE_X);
+  const int64_t R = sx_side ? M : N, C = sx_side ? N : M;
+  const int es = esize(ab_dt);
+  ss_status s;
+  if ((s = check_mat("sp_vals", sp_vals, R, Kc / 2, ldsv, es)) != SS_OK) return s;
+  if ((s = check_mat("sp_meta", sp_meta, R, Kc / 8, ldsm, 1)) != SS_OK) return s;
+  if ((s = check_mat("dense", dense, C, Kc, ldd, es)) != SS_OK) return s;
+  // Y needs only an aligned base; rows are stored with vector writes when
+  // ldy % 4 == 0 and element by element otherwise
+  if ((s = check_mat("Y", Y, 1, N, ldy, esize(y_dt))) != SS_OK) return s;
+  if (ab_dt != SS_BF16 && y_dt != SS_I32 && (!sx || !sw))
+    return fail(SS_ERR_NULL, "INT8/FP8 products need both scales");
+  const int ab = ab_dt == SS_I8 ? 0 : ab_dt == SS_FP8E4M3 ? 1 : 2;
+  const int yt = y_dt == SS_BF16 ? 0 : y_dt == SS_F32 ? 1 : 2;
+  return hip_status(ss::launch_spgemm(sx_side, ab, yt, R, C, Kc, sp_vals, ldsv * es, sp_meta, ldsm, dense, ldd * es,
+                                      y_dt == SS_I32 ? nullptr : sx, y_dt == SS_I32 ? nullptr : sw, Y, ldy,
+                                      (hipStream_t)stream),
+                    "ss_spgemm launch");
+}
+
+}  // extern "C"

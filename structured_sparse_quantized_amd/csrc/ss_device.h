@@ -1,0 +1,81 @@
+// Device-side helpers shared by the gfx950 kernels: element codecs, the
+// per-row symmetric quantiser, the 2:4 selection network and block reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+constexpr int kBlock = 256;  // threads per workgroup for the streaming kernels
+
+// ---- element codecs --------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float32 -> bfloat16, nearest with ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Magnitude key: for finite floats the unsigned order of the bits without the
+// sign is the order of |v|, and +0 / -0 share key 0.
+__device__ __forceinline__ uint32_t mag_key_f32(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+__device__ __forceinline__ uint32_t mag_key_bf16(uint16_t b) { return (uint32_t)(b & 0x7FFFu); }
+
+// ---- per-row symmetric quantisation ----------------------------------------
+// Q = 127 (INT8) or 448 (FP8 E4M3FN). inv = Q / a is correctly rounded (HIP's
+// default single-precision division); products use __fmul_rn so nothing fuses.
+template <bool FP8> struct Quant {
+  static constexpr float Q = FP8 ? 448.0f : 127.0f;
+  __device__ __forceinline__ static uint8_t code(float v, float inv) {
+    float t = __fmul_rn(v, inv);
+    if constexpr (FP8) {
+      t = fminf(fmaxf(t, -448.0f), 448.0f);
+      // OCP E4M3FN, nearest-even (gfx950 conversion unit)
+      return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(t, 0.0f, 0, false) & 0xFF);
+    } else {
+      float r = rintf(t);  // ties to even
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      return (uint8_t)(int8_t)(int)r;
+    }
+  }
+};
+
+// ---- 2:4 selection ----------------------------------------------------------
+// Keep the two largest keys of a 4-group; equal keys keep the lower index.
+// Returns the nibble idx0 | idx1 << 2 with idx0 < idx1.
+__device__ __forceinline__ uint32_t top2_nibble(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3) {
+  // rank = number of elements that outrank this one
+  const int r0 = (k1 > k0) + (k2 > k0) + (k3 > k0);
+  const int r1 = (k0 >= k1) + (k2 > k1) + (k3 > k1);
+  const int r2 = (k0 >= k2) + (k1 >= k2) + (k3 > k2);
+  const int r3 = (k0 >= k3) + (k1 >= k3) + (k2 >= k3);
+  const uint32_t m = (uint32_t)(r0 < 2) | ((uint32_t)(r1 < 2) << 1) | ((uint32_t)(r2 < 2) << 2) |
+                     ((uint32_t)(r3 < 2) << 3);
+  const uint32_t i0 = __builtin_ctz(m);
+  const uint32_t i1 = __builtin_ctz(m & (m - 1));
+  return i0 | (i1 << 2);
+}
+
+// ---- reductions ---------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide max over kBlock threads; every thread gets the result.
+__device__ __forceinline__ float block_max(float v, float* red /* >= kBlock/64 floats */) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kBlock / 64; ++i) r = fmaxf(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+}  // namespace ss

@@ -1,0 +1,23 @@
+// Host-callable launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+hipError_t launch_quant_lift(bool x_bf16, bool fp8, const void* X, int64_t ldx, int64_t M, int64_t K, int n,
+                             void* Xq, int64_t ldq, int64_t Kc, float* sx, hipStream_t st);
+
+// out: 0 = int8, 1 = fp8, 2 = bf16
+hipError_t launch_prune24(bool in_bf16, int out, const void* X, int64_t ldx, int64_t M, int64_t K, void* vals,
+                          int64_t ldv_bytes, uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st);
+
+hipError_t launch_slide(bool in_bf16, int out, const void* W, int64_t ldw, int64_t rows, int64_t K, int n, void* vals,
+                        int64_t ldv_bytes, uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st);
+
+// ab: 0 = int8, 1 = fp8, 2 = bf16; yt: 0 = bf16, 1 = f32, 2 = i32
+hipError_t launch_spgemm(bool side_x, int ab, int yt, int64_t R, int64_t C, int64_t Kc, const void* av,
+                         int64_t lda_bytes, const uint8_t* am, int64_t ldm, const void* bd, int64_t ldb_bytes,
+                         const float* sx, const float* sw, void* Y, int64_t ldy, hipStream_t st);
+
+}  // namespace ss

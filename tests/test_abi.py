@@ -1,0 +1,84 @@
+"""The C ABI: the library loads, exports what include/ss.h declares, and rejects
+bad arguments on the host before anything is enqueued (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "structured_sparse_quantized_amd", "libss.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libss.so not built")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ss.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ss_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    import structured_sparse_quantized_amd as ss
+    names = _declared()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(ss.lib, name), name
+    assert set(names) == set(ss.EXPORTS)
+
+
+def test_lifted_k_matches_oracle():
+    import structured_sparse_quantized_amd as ss
+    for n in range(2, 9):
+        for K in (0, 1, 4, 7, 8, 12, 240, 250, 512, 3584, 4096, 14336, 18944):
+            assert ss.lifted_k_logical(K, n) == oracle.lifted_k(K, n)
+            assert ss.lifted_k(K, n) == oracle.lifted_k_alloc(K, n)
+    assert ss.lifted_k(10, 1) == -1 and ss.lifted_k(10, 9) == -1 and ss.lifted_k(-1, 2) == -1
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+
+
+def test_host_validation_statuses():
+    import structured_sparse_quantized_amd as ss
+    L = ss.lib
+    # NULL input
+    assert L.ss_prune24(None, ss.SS_F32, 4, 8, 8, ss.SS_I8, FAKE, 16, FAKE, 16, FAKE, None) == ss.SS_ERR_NULL
+    assert b"NULL" in L.ss_last_error()
+    # K not a multiple of 4
+    assert L.ss_prune24(FAKE, ss.SS_F32, 4, 6, 8, ss.SS_I8, FAKE, 16, FAKE, 16, FAKE, None) == ss.SS_ERR_SHAPE
+    # bad dtypes
+    assert L.ss_prune24(FAKE, ss.SS_I8, 4, 8, 8, ss.SS_I8, FAKE, 256, FAKE, 32, FAKE, None) == ss.SS_ERR_DTYPE
+    assert L.ss_quant_lift_act(FAKE, ss.SS_BF16, 4, 8, 8, 2, ss.SS_BF16, FAKE, 256, FAKE, None) == ss.SS_ERR_DTYPE
+    # bad pattern
+    assert L.ss_slide_decompose(FAKE, ss.SS_F32, 4, 8, 8, 1, ss.SS_I8, FAKE, 256, FAKE, 32, FAKE, None) == ss.SS_ERR_PATTERN
+    assert L.ss_quant_lift_act(FAKE, ss.SS_BF16, 4, 8, 8, 9, ss.SS_I8, FAKE, 256, FAKE, None) == ss.SS_ERR_PATTERN
+    # misaligned pointer and row stride
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    assert L.ss_quant_lift_act(odd, ss.SS_BF16, 4, 8, 8, 2, ss.SS_I8, FAKE, 256, FAKE, None) == ss.SS_ERR_ALIGN
+    assert L.ss_quant_lift_act(FAKE, ss.SS_BF16, 4, 12, 12, 2, ss.SS_I8, FAKE, 256, FAKE, None) == ss.SS_ERR_ALIGN
+    # leading dimension smaller than the row
+    assert L.ss_quant_lift_act(FAKE, ss.SS_BF16, 4, 16, 8, 2, ss.SS_I8, FAKE, 256, FAKE, None) == ss.SS_ERR_SHAPE
+    # spgemm: Kc not aligned, I32 with fp8, missing scales, bad side
+    args = (FAKE, 128, FAKE, 32, FAKE, 256, FAKE, FAKE)
+    assert L.ss_spgemm(0, 4, 4, 100, ss.SS_I8, *args, ss.SS_I32, FAKE, 16, None) == ss.SS_ERR_SHAPE
+    assert L.ss_spgemm(0, 4, 4, 256, ss.SS_FP8E4M3, *args, ss.SS_I32, FAKE, 16, None) == ss.SS_ERR_DTYPE
+    assert L.ss_spgemm(0, 4, 4, 256, ss.SS_I8, FAKE, 128, FAKE, 32, FAKE, 256, None, FAKE, ss.SS_BF16, FAKE, 8,
+                       None) == ss.SS_ERR_NULL
+    assert L.ss_spgemm(5, 4, 4, 256, ss.SS_I8, *args, ss.SS_BF16, FAKE, 8, None) == ss.SS_ERR_SHAPE
+    # BF16 output with a scale pointer
+    assert L.ss_prune24_act(FAKE, ss.SS_BF16, 4, 8, 8, ss.SS_BF16, FAKE, 128, FAKE, 32, FAKE, None) == ss.SS_ERR_DTYPE
+    # prune24_act needs BF16 activations
+    assert L.ss_prune24_act(FAKE, ss.SS_F32, 4, 8, 8, ss.SS_BF16, FAKE, 128, FAKE, 32, None, None) == ss.SS_ERR_DTYPE
+
+
+def test_empty_problems_are_ok_without_launch():
+    import structured_sparse_quantized_amd as ss
+    L = ss.lib
+    assert L.ss_quant_lift_act(FAKE, ss.SS_BF16, 0, 64, 64, 4, ss.SS_I8, FAKE, 256, FAKE, None) == ss.SS_OK
+    assert L.ss_prune24(FAKE, ss.SS_F32, 0, 64, 64, ss.SS_I8, FAKE, 128, FAKE, 32, FAKE, None) == ss.SS_OK
+    assert L.ss_spgemm(0, 0, 16, 256, ss.SS_I8, FAKE, 128, FAKE, 32, FAKE, 256, FAKE, FAKE, ss.SS_BF16, FAKE, 16,
+                       None) == ss.SS_OK
+    assert L.ss_last_error() == b""
