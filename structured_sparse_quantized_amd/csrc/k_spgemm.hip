@@ -68,6 +68,33 @@ template <> struct Mma<2> {
   }
 };
 
+
+// Store one lane's 4 results: rows ar..ar+3 of the sparse operand, one dense row bc.
+template <int YT, bool SIDE_X>
+__device__ __forceinline__ void store_out(void* Y, int64_t ldy, int64_t ar, int64_t bc, int64_t R, const float* y,
+                                          const int32_t* yi) {
+  if (!SIDE_X && (ldy & 3) == 0 && ar + 3 < R) {  // Y[bc][ar .. ar+3] is one aligned vector
+    if constexpr (YT == 0) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + bc * ldy + ar) = make_uint2(lo, hi);
+    } else if constexpr (YT == 1) {
+      *reinterpret_cast<float4*>(static_cast<float*>(Y) + bc * ldy + ar) = make_float4(y[0], y[1], y[2], y[3]);
+    } else {
+      *reinterpret_cast<int4*>(static_cast<int32_t*>(Y) + bc * ldy + ar) = make_int4(yi[0], yi[1], yi[2], yi[3]);
+    }
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (ar + q >= R) break;
+    const int64_t off = SIDE_X ? (ar + q) * ldy + bc : bc * ldy + ar + q;
+    if constexpr (YT == 0) static_cast<uint16_t*>(Y)[off] = f32_to_bf16(y[q]);
+    else if constexpr (YT == 1) static_cast<float*>(Y)[off] = y[q];
+    else static_cast<int32_t*>(Y)[off] = yi[q];
+  }
+}
+
 template <int AB, int YT, bool SIDE_X>
 __global__ __launch_bounds__(256, 2) void spgemm_kernel(int64_t R, int64_t C, int64_t Kc,
                                                         const uint8_t* __restrict__ av, int64_t lda,  // bytes
@@ -227,10 +254,205 @@ __global__ __launch_bounds__(256, 2) void spgemm_kernel(int64_t R, int64_t C, in
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// 8-bit operands (int8, fp8): pipelined kernel.
+//
+// Each workgroup (8 waves, 4 x 2, wave tile 64 x 64) owns a 256 (sparse rows)
+// x 128 (dense rows) output tile. The K loop runs in stages of two instruction
+// steps (256 dense K): per sparse row 128 B of values (one cache line) and 32 B
+// of metadata, per dense row 256 B (two lines). Operands move HBM/L2 -> LDS with
+// global_load_lds_dwordx4 (no register round trip); each wave-load covers 8 rows
+// x 128 B so every request is a full cache line (16 rows x 64 B halves the L2
+// throughput on gfx950). Inside a line the 16-byte chunks are XOR-swizzled by
+// row so the fragment reads are nearly free of LDS bank conflicts. Two LDS
+// buffers: stage t+1 streams in while stage t is multiplied; within a stage the
+// reads of step 1 are interleaved with the smfmacs of step 0.
+// Rows past the matrix edge are clamped to the last row for loading; their
+// results are never stored.
+namespace pipe8 {
+
+constexpr int BM = 256, BN = 128, WGM = 4, WGN = 2, NW = WGM * WGN;
+constexpr int TI = BM / WGM / 16, TJ = BN / WGN / 16;  // 4 x 4 instructions per wave per step
+constexpr int A_BYTES = BM * 128, M_BYTES = BM * 32, B_BYTES = BN * 256;
+constexpr int STAGE = A_BYTES + M_BYTES + B_BYTES;     // 72 KB
+constexpr int LDS = 2 * STAGE;                         // 144 KB
+constexpr int NA = BM / 8, NMETA = BM / 32, NB = BN / 8 * 2;
+constexpr int PA = NA / NW, PB = NB / NW;
+static_assert(NA % NW == 0 && NB % NW == 0 && NMETA <= NW, "load split");
+#define SS_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int swz(int c, int r16) { return c ^ ((r16 >> 1) & 7); }
+
+template <int AB, int YT, bool SIDE_X>
+__global__ __launch_bounds__(64 * NW, 1) void spgemm8_kernel(int R, int C, int KT, const uint8_t* __restrict__ av, int lda,
+                                                             const uint8_t* __restrict__ am, int ldm,
+                                                             const uint8_t* __restrict__ bd, int ldb,
+                                                             const float* __restrict__ sx, const float* __restrict__ sw,
+                                                             void* __restrict__ Y, int ldy, int tiles_r, int tiles_c) {
+  using Acc = typename Mma<AB>::Acc;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  // Tile order: the dispatcher deals workgroups to the 8 XCDs round-robin; give
+  // each XCD a contiguous run of tiles, walked in groups of 4 sparse-row tiles,
+  // so the tiles sharing operands also share an L2.
+  const int nb = gridDim.x;
+  int bid = blockIdx.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  constexpr int GR = 4;
+  const int group = bid / (GR * tiles_c);
+  const int first_r = group * GR;
+  const int gsize = min(tiles_r - first_r, GR);
+  const int tr = first_r + (bid % (GR * tiles_c)) % gsize;
+  const int tc = (bid % (GR * tiles_c)) / gsize;
+  const int r0 = tr * BM, c0 = tc * BN;
+
+  // per-lane source offsets of this wave's loads (stage 0)
+  uint32_t offa[PA], offb[PB], offm = 0;
+  const int r8 = lane >> 3, p = lane & 7;
+#pragma unroll
+  for (int q = 0; q < PA; ++q) {
+    const int a = (wave + q * NW) * 8 + r8;
+    offa[q] = (uint32_t)min(r0 + a, R - 1) * lda + swz(p, a & 15) * 16;
+  }
+#pragma unroll
+  for (int q = 0; q < PB; ++q) {
+    const int blk = wave + q * NW, b = (blk >> 1) * 8 + r8;
+    offb[q] = (uint32_t)min(c0 + b, C - 1) * ldb + (blk & 1) * 128 + swz(p, b & 15) * 16;
+  }
+  if (wave < NMETA) offm = (uint32_t)min(r0 + wave * 32 + (lane >> 1), R - 1) * ldm + (lane & 1) * 16;
+
+  auto issue = [&](int t) {
+    SS_LDS uint8_t* base = (SS_LDS uint8_t*)smem + (t & 1) * STAGE;
+#pragma unroll
+    for (int q = 0; q < PA; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(av + offa[q] + t * 128), (SS_LDS void*)(base + (wave + q * NW) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < PB; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(bd + offb[q] + t * 256),
+                                       (SS_LDS void*)(base + A_BYTES + M_BYTES + (wave + q * NW) * 1024), 16, 0, 0);
+    if (wave < NMETA)
+      __builtin_amdgcn_global_load_lds((const void*)(am + offm + t * 32), (SS_LDS void*)(base + A_BYTES + wave * 1024), 16, 0, 0);
+  };
+
+  uint4 fa[2][TI], fb[2][TJ][2];
+  uint32_t fi[2][TI];
+  const int r16 = lane & 15, j = lane >> 4;
+  auto read_frags = [&](int buf, int t, int s) {
+    const uint8_t* st = smem + (t & 1) * STAGE;
+#pragma unroll
+    for (int u = 0; u < TI; ++u) {
+      const int i = wm * TI + u, a = i * 16 + r16;
+      fa[buf][u] = *reinterpret_cast<const uint4*>(st + (2 * i + (r16 >> 3)) * 1024 + (r16 & 7) * 128 + swz(s * 4 + j, r16) * 16);
+      fi[buf][u] = *reinterpret_cast<const uint32_t*>(st + A_BYTES + (a >> 5) * 1024 + (a & 31) * 32 + s * 16 + j * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) {
+      const int jt = wn * TJ + u;
+      const uint8_t* bb = st + A_BYTES + M_BYTES + ((jt * 2 + (r16 >> 3)) * 2 + s) * 1024 + (r16 & 7) * 128;
+      fb[buf][u][0] = *reinterpret_cast<const uint4*>(bb + swz(j, r16) * 16);
+      fb[buf][u][1] = *reinterpret_cast<const uint4*>(bb + swz(4 + j, r16) * 16);
+    }
+  };
+  Acc acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) acc[i][u] = Acc{0, 0, 0, 0};
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < TJ; ++u)
+#pragma unroll
+      for (int i = 0; i < TI; ++i) acc[i][u] = Mma<AB>::run(fa[buf][i], fb[buf][u][0], fb[buf][u][1], acc[i][u], fi[buf][i]);
+  };
+
+  if (KT > 0) issue(0);
+  for (int t = 0; t < KT; ++t) {
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0): this wave's loads of stage t landed
+    __builtin_amdgcn_s_barrier();                         // everyone's landed; stage t-1 fully read
+    if (t + 1 < KT) issue(t + 1);
+    read_frags(0, t, 0);
+    read_frags(1, t, 1);
+    mma(0);
+    mma(1);
+    // step-0 reads, then step-0 smfmacs interleaved with step-1 reads, then the rest
+    constexpr int RD = TI + TI / 2 + 2 * TJ;  // read instructions per step (metadata words pair up)
+    constexpr int MF = TI * TJ;
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+    for (int q = 0; q < MF; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (q < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+  }
+
+  // Epilogue: y = fl32(fl32(float(acc) * sx[m]) * sw[n]). All scales are loaded
+  // up front (indices clamped; out-of-range results are never stored).
+  float s_a[TI][4], s_b[TJ];
+  const float* sa = SIDE_X ? sx : sw;  // scale indexed by sparse row
+  const float* sb = SIDE_X ? sw : sx;  // scale indexed by dense row
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_a[i][q] = sa ? sa[min(r0 + (wm * TI + i) * 16 + 4 * j + q, R - 1)] : 1.0f;
+#pragma unroll
+  for (int u = 0; u < TJ; ++u) s_b[u] = sb ? sb[min(c0 + (wn * TJ + u) * 16 + r16, C - 1)] : 1.0f;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) {
+      const int ar = r0 + (wm * TI + i) * 16 + 4 * j;  // 4 consecutive sparse rows
+      const int bc = c0 + (wn * TJ + u) * 16 + r16;    // one dense row
+      if (bc >= C) continue;
+      float y[4];
+      int32_t yi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (YT == 2) {
+          yi[q] = (int32_t)acc[i][u][q];
+        } else {
+          float f = (float)acc[i][u][q];
+          // the token scale is applied first, then the channel scale
+          const float s1 = SIDE_X ? s_a[i][q] : s_b[u], s2 = SIDE_X ? s_b[u] : s_a[i][q];
+          if (sx) f = __fmul_rn(f, s1);
+          if (sw) f = __fmul_rn(f, s2);
+          y[q] = f;
+        }
+      }
+      store_out<YT, SIDE_X>(Y, ldy, ar, bc, R, y, yi);
+    }
+  }
+}
+
+}  // namespace pipe8
+
 template <int AB, int YT>
 static hipError_t launch_sg2(bool side_x, int64_t R, int64_t C, int64_t Kc, const uint8_t* av, int64_t lda,
                              const uint8_t* am, int64_t ldm, const uint8_t* bd, int64_t ldb, const float* sx,
                              const float* sw, void* Y, int64_t ldy, hipStream_t st) {
+  const bool fits32 = (uint64_t)R * lda < (1ull << 32) && (uint64_t)R * ldm < (1ull << 32) &&
+                      (uint64_t)C * ldb < (1ull << 32);
+  if constexpr (AB != 2) {
+   if (fits32) {
+    // 8-bit pipelined kernel (32-bit operand offsets)
+    const int tr = (int)((R + pipe8::BM - 1) / pipe8::BM), tc = (int)((C + pipe8::BN - 1) / pipe8::BN);
+    const int KT = (int)(Kc / 256);
+    auto kern = side_x ? pipe8::spgemm8_kernel<AB, YT, true> : pipe8::spgemm8_kernel<AB, YT, false>;
+    static bool attr_set[2] = {false, false};
+    if (!attr_set[side_x]) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, pipe8::LDS);
+      if (e != hipSuccess) return e;
+      attr_set[side_x] = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * pipe8::NW), pipe8::LDS, st, (int)R, (int)C, KT, av, (int)lda, am,
+                       (int)ldm, bd, (int)ldb, sx, sw, Y, (int)ldy, tr, tc);
+    return hipGetLastError();
+     }
+  }
   dim3 grid((unsigned)((C + BN - 1) / BN), (unsigned)((R + BM - 1) / BM)), block(256);
   if (side_x)
     hipLaunchKernelGGL((spgemm_kernel<AB, YT, true>), grid, block, 0, st, R, C, Kc, av, lda, am, ldm, bd, ldb, sx, sw, Y, ldy, (ldy % 4) == 0);
