@@ -43,7 +43,25 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernels-only", action="store_true", help="skip the dense comparator and CPU baseline")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 256 MiB device copy (the reference for HBM byte counters)")
     return p.parse_args()
+
+
+def traffic_record(kernel):
+    """HBM traffic per launch measured with rocprofv3 counters, if it was taken
+    on the current source of the kernel (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, "structured_sparse_quantized_amd", "csrc", f), "rb").read())
+    return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
 
 
 def kernel_work(name, Kc68, Kc24):
@@ -172,7 +190,7 @@ def main():
         "achieved": dk["GB/s"] if dk["bound"] == "hbm" else dk["TOPS"],
         "peak": HBM_PEAK_GBS if dk["bound"] == "hbm" else INT8_DENSE_PEAK_TOPS,
         "unit": "GB/s" if dk["bound"] == "hbm" else "TFLOP/s",
-        "frac": dk["frac"], "traffic": None,
+        "frac": dk["frac"], "traffic": traffic_record(dom),
     }
     online68_s = (per_kernel_ms["quant_lift_68"] + per_kernel_ms["spgemm_68"]) * 1e-3
     online24_s = (per_kernel_ms["quant_lift_24"] + per_kernel_ms["spgemm_24"]) * 1e-3
@@ -201,6 +219,13 @@ def main():
                      "speedup_68": (t_mm + t_q) / online68_s, "speedup_24": (t_mm + t_q) / online24_s}
         except Exception as e:  # comparator unavailable on this stack
             dense = {"error": repr(e)[:200]}
+
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     cpu = None
     if not (args.no_cpu or args.kernels_only):

@@ -3,12 +3,13 @@
 // 2610.28947, introduction and sections 1 and 2.3; LLM Compressor guide for
 // the scale granularity.
 //
-// One workgroup per row. A "unit" is 4 consecutive 4-groups (16 input
-// elements) and produces 8 kept values and 2 metadata bytes. When quantised
-// output is requested the row absmax is reduced first; units that fit in the
-// per-thread register budget are read from HBM only once.
+// A "unit" is 4 consecutive 4-groups (16 input elements) and produces 8 kept
+// values and 2 metadata bytes. When quantised output is requested the row
+// absmax is reduced first.
 #include "ss_device.h"
 #include "ss_kernels.h"
+
+#include <algorithm>
 
 namespace ss {
 
@@ -47,7 +48,11 @@ __device__ __forceinline__ void emit_unit(const Unit<TIn>& u, bool zero_row, flo
   for (int g = 0; g < 4; ++g) {
     const uint32_t nib = top2_nibble(u.key(4 * g), u.key(4 * g + 1), u.key(4 * g + 2), u.key(4 * g + 3));
     meta |= nib << (4 * g);
-    const float v0 = u.val(4 * g + (nib & 3)), v1 = u.val(4 * g + (nib >> 2));
+    // select among compile-time indices (a runtime index would put the unit in scratch memory)
+    const float c0 = u.val(4 * g), c1 = u.val(4 * g + 1), c2 = u.val(4 * g + 2), c3 = u.val(4 * g + 3);
+    const uint32_t i0 = nib & 3, i1 = nib >> 2;  // i0 < i1
+    const float v0 = i0 == 0 ? c0 : i0 == 1 ? c1 : c2;
+    const float v1 = i1 == 1 ? c1 : i1 == 2 ? c2 : c3;
     kv[2 * g] = (v0 == 0.0f) ? 0.0f : v0;  // zeros are stored as +0
     kv[2 * g + 1] = (v1 == 0.0f) ? 0.0f : v1;
   }
@@ -87,36 +92,76 @@ template <typename TIn> __device__ __forceinline__ float unit_absmax(const Unit<
   return m;
 }
 
-constexpr int kUPT = 4;  // units per thread kept in registers
-
-template <typename TIn, int OUT>
-__global__ __launch_bounds__(kBlock) void prune24_kernel(const TIn* __restrict__ X, int64_t ldx, int64_t K,
+// Persistent workgroups walk rows r, r + grid, ...; UPT units per thread are
+// held in registers and the next row is loaded before the current one is
+// reduced and written, so HBM reads and writes overlap.
+template <typename TIn, int OUT, int UPT, bool PIPE>
+__global__ __launch_bounds__(kBlock, (PIPE || UPT > 2) ? 2 : (UPT > 1 ? 4 : 8)) void prune24_kernel(const TIn* __restrict__ X, int64_t ldx, int M, int K,
                                                          uint8_t* __restrict__ vals, int64_t ldv_bytes,
-                                                         uint8_t* __restrict__ meta, int64_t ldm,
-                                                         int64_t Kc, float* __restrict__ scale) {
+                                                         uint8_t* __restrict__ meta, int64_t ldm, int Kc,
+                                                         float* __restrict__ scale) {
+  __shared__ float red[kBlock / 64];
+  const int tid = threadIdx.x;
+  const int units = Kc / 16;              // includes padding units (all zero)
+  const int data_units = (K + 15) / 16;
+  Unit<TIn> cur[UPT], nxt[PIPE ? UPT : 1];
+  auto load = [&](Unit<TIn>* u, int r) {
+    const TIn* xr = X + (int64_t)r * ldx;
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int un = tid + i * kBlock;
+      if (un < data_units) load_unit(u[i], xr, un, K);
+      else u[i] = Unit<TIn>{};
+    }
+  };
+  int r = blockIdx.x;
+  if (r < M) load(cur, r);
+  for (; r < M; r += gridDim.x) {
+    const int rn = r + gridDim.x;
+    if (PIPE && rn < M) load(nxt, rn);
+    bool zero_row = false;
+    float inv = 0.0f;
+    if constexpr (OUT != 2) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < UPT; ++i) amax = fmaxf(amax, unit_absmax(cur[i]));
+      amax = block_max(amax, red);
+      constexpr float Q = (OUT == 1) ? 448.0f : 127.0f;
+      zero_row = (amax == 0.0f);
+      inv = zero_row ? 0.0f : Q / amax;
+      if (tid == 0) scale[r] = zero_row ? 0.0f : amax / Q;
+    }
+    uint8_t* vr = vals + (int64_t)r * ldv_bytes;
+    uint8_t* mr = meta + (int64_t)r * ldm;
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int un = tid + i * kBlock;
+      if (un < units) emit_unit<TIn, OUT>(cur[i], zero_row, inv, vr, mr, un);
+    }
+    if constexpr (PIPE) {
+#pragma unroll
+      for (int i = 0; i < UPT; ++i) cur[i] = nxt[i];
+    } else if (rn < M) {
+      load(cur, rn);
+    }
+  }
+}
+
+// Rows longer than kBlock * 4 units: absmax pass, then a second read.
+template <typename TIn, int OUT>
+__global__ __launch_bounds__(kBlock) void prune24_long_kernel(const TIn* __restrict__ X, int64_t ldx, int64_t K,
+                                                              uint8_t* __restrict__ vals, int64_t ldv_bytes,
+                                                              uint8_t* __restrict__ meta, int64_t ldm, int64_t Kc,
+                                                              float* __restrict__ scale) {
   __shared__ float red[kBlock / 64];
   const int64_t row = blockIdx.x;
   const TIn* xr = X + row * ldx;
-  uint8_t* vr = vals + row * ldv_bytes;
-  uint8_t* mr = meta + row * ldm;
-  const int tid = threadIdx.x;
-  const int64_t units = Kc / 16;         // includes padding units (all zero)
-  const int64_t data_units = (K + 15) / 16;
-
-  Unit<TIn> u[kUPT];
-  float amax = 0.0f;
+  const int64_t units = Kc / 16, data_units = (K + 15) / 16;
   bool zero_row = false;
   float inv = 0.0f;
   if constexpr (OUT != 2) {
-#pragma unroll
-    for (int i = 0; i < kUPT; ++i) {
-      const int64_t un = tid + (int64_t)i * kBlock;
-      if (un < data_units) {
-        load_unit(u[i], xr, un, K);
-        amax = fmaxf(amax, unit_absmax(u[i]));
-      }
-    }
-    for (int64_t un = tid + (int64_t)kUPT * kBlock; un < data_units; un += kBlock) {
+    float amax = 0.0f;
+    for (int64_t un = threadIdx.x; un < data_units; un += kBlock) {
       Unit<TIn> t;
       load_unit(t, xr, un, K);
       amax = fmaxf(amax, unit_absmax(t));
@@ -125,37 +170,55 @@ __global__ __launch_bounds__(kBlock) void prune24_kernel(const TIn* __restrict__
     constexpr float Q = (OUT == 1) ? 448.0f : 127.0f;
     zero_row = (amax == 0.0f);
     inv = zero_row ? 0.0f : Q / amax;
-    if (tid == 0) scale[row] = zero_row ? 0.0f : amax / Q;
+    if (threadIdx.x == 0) scale[row] = zero_row ? 0.0f : amax / Q;
   }
-#pragma unroll
-  for (int i = 0; i < kUPT; ++i) {
-    const int64_t un = tid + (int64_t)i * kBlock;
-    if (un < units) {
-      if (OUT == 2 || un >= data_units) {
-        if (un < data_units) load_unit(u[i], xr, un, K);
-        else u[i] = Unit<TIn>{};
-      }
-      emit_unit<TIn, OUT>(u[i], zero_row, inv, vr, mr, un);
-    }
-  }
-  for (int64_t un = tid + (int64_t)kUPT * kBlock; un < units; un += kBlock) {
+  for (int64_t un = threadIdx.x; un < units; un += kBlock) {
     Unit<TIn> t{};
     if (un < data_units) load_unit(t, xr, un, K);
-    emit_unit<TIn, OUT>(t, zero_row, inv, vr, mr, un);
+    emit_unit<TIn, OUT>(t, zero_row, inv, vals + row * ldv_bytes, meta + row * ldm, un);
   }
+}
+
+int num_cus_p() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0;
+    hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  }
+  return n;
+}
+
+template <typename TIn, int OUT>
+static hipError_t launch_out(const TIn* X, int64_t ldx, int64_t M, int64_t K, uint8_t* v, int64_t ldv_bytes,
+                             uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
+  const int64_t upt = (Kc / 16 + kBlock - 1) / kBlock;
+  if (upt > 4 || K >= (1 << 30) || Kc >= (1 << 30) || M >= (1 << 30)) {
+    hipLaunchKernelGGL((prune24_long_kernel<TIn, OUT>), dim3((unsigned)M), dim3(kBlock), 0, st, X, ldx, K, v, ldv_bytes,
+                       meta, ldm, Kc, scale);
+    return hipGetLastError();
+  }
+  const bool pipe = M > 16 * (int64_t)num_cus_p();
+  const unsigned grid = (unsigned)(pipe ? 8 * (int64_t)num_cus_p() : M);
+  const int m = (int)M, k = (int)K, kc = (int)Kc;
+#define SS_P(U_) \
+  do { if (pipe) hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k, v, ldv_bytes, meta, ldm, kc, scale); else hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, false>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k, v, ldv_bytes, meta, ldm, kc, scale); } while (0)
+  if (upt <= 1) SS_P(1);
+  else if (upt <= 2) SS_P(2);
+  else SS_P(4);
+#undef SS_P
+  return hipGetLastError();
 }
 
 template <typename TIn>
 static hipError_t launch_p24(int out, const TIn* X, int64_t ldx, int64_t M, int64_t K, void* vals, int64_t ldv_bytes,
                              uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
-  dim3 grid((unsigned)M), block(kBlock);
   uint8_t* v = static_cast<uint8_t*>(vals);
   switch (out) {
-    case 0: hipLaunchKernelGGL((prune24_kernel<TIn, 0>), grid, block, 0, st, X, ldx, K, v, ldv_bytes, meta, ldm, Kc, scale); break;
-    case 1: hipLaunchKernelGGL((prune24_kernel<TIn, 1>), grid, block, 0, st, X, ldx, K, v, ldv_bytes, meta, ldm, Kc, scale); break;
-    default: hipLaunchKernelGGL((prune24_kernel<TIn, 2>), grid, block, 0, st, X, ldx, K, v, ldv_bytes, meta, ldm, Kc, scale); break;
+    case 0: return launch_out<TIn, 0>(X, ldx, M, K, v, ldv_bytes, meta, ldm, Kc, scale, st);
+    case 1: return launch_out<TIn, 1>(X, ldx, M, K, v, ldv_bytes, meta, ldm, Kc, scale, st);
+    default: return launch_out<TIn, 2>(X, ldx, M, K, v, ldv_bytes, meta, ldm, Kc, scale, st);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_prune24(bool in_bf16, int out, const void* X, int64_t ldx, int64_t M, int64_t K, void* vals,

@@ -1,15 +1,20 @@
 // Fused per-token quantisation + activation lift (SlideSparse article,
-// activation-lifting paragraph; SlideSparse blog section 3.2): one pass reads
-// a token row, reduces its absmax, quantises, and writes the row gathered into
+// activation-lifting paragraph; SlideSparse blog section 3.2): one pass reads a
+// token row, reduces its absmax, quantises, and writes the row gathered into
 // window order X'[4(n-1)g + 4w + j] = q(X[2n g + 2w + j]), zero-padded to Kc.
 //
-// One workgroup per token row. The row is held in registers between the
-// absmax reduction and the quantisation, so X is read from HBM once; for the
-// lift the codes are staged in LDS and gathered into 16-byte output chunks.
+// Persistent workgroups walk rows r, r + grid, ...; the next row is loaded
+// into registers before the current one is reduced and written, so HBM reads
+// and writes overlap. For n > 2 the codes of a row are staged in LDS and
+// gathered into 16-byte output chunks (the blog's output-oriented iteration:
+// one output window per index, base 2n*group + 2*offset).
 #include "ss_device.h"
 #include "ss_kernels.h"
 
+#include <algorithm>
+
 namespace ss {
+namespace {
 
 template <typename TIn> struct InVec;
 template <> struct InVec<uint16_t> {  // 8 bf16 per 16-byte vector
@@ -26,107 +31,124 @@ template <> struct InVec<float> {  // 4 float per 16-byte vector
   __device__ static float scalar(const float* p) { return *p; }
 };
 
-// VPT = 16-byte vectors per thread held in registers (row fits when
-// K <= kBlock * VPT * E; the host picks VPT).
-template <typename TIn, bool FP8, int VPT>
-__global__ __launch_bounds__(kBlock) void quant_lift_kernel(const TIn* __restrict__ X, int64_t ldx, int64_t K,
-                                                            int n, uint8_t* __restrict__ Xq, int64_t ldq,
-                                                            int64_t Kc, float* __restrict__ sx) {
+int num_cus() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0;
+    hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  }
+  return n;
+}
+
+// VPT = 16-byte vectors per thread (the row fits when K <= kBlock*VPT*E).
+template <typename TIn, bool FP8, int N, int VPT, bool PIPE>
+__global__ __launch_bounds__(kBlock, (PIPE || VPT > 4) ? 2 : (VPT > 2 ? 4 : 8)) void quant_lift_kernel(const TIn* __restrict__ X, int64_t ldx, int M, int K,
+                                                            uint8_t* __restrict__ Xq, int64_t ldq, int Kc,
+                                                            float* __restrict__ sx) {
   using V = InVec<TIn>;
   constexpr int E = V::E;
-  extern __shared__ __align__(16) uint8_t lds[];  // [Kpad] codes (lift only)
-  __shared__ float red[kBlock / 64];
-
-  const int64_t row = blockIdx.x;
-  const TIn* xr = X + row * ldx;
-  uint8_t* qr = Xq + row * ldq;
-  const int tid = threadIdx.x;
-  const int64_t nvec = K / E;  // full vectors; the K % E tail is read scalar
-
-  uint4 v[VPT];
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int64_t vi = tid + (int64_t)i * kBlock;
-    if (vi < nvec) {
-      v[i] = reinterpret_cast<const uint4*>(xr)[vi];
-#pragma unroll
-      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(V::get(v[i], e)));
-    } else {
-      v[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  const int64_t tail0 = nvec * E;
-  float tailv = 0.0f;
-  if (tail0 + tid < K) {
-    tailv = V::scalar(xr + tail0 + tid);
-    amax = fmaxf(amax, fabsf(tailv));
-  }
-  amax = block_max(amax, red);
-
   using Qz = Quant<FP8>;
-  const bool zero_row = (amax == 0.0f);
-  const float inv = zero_row ? 0.0f : Qz::Q / amax;
-  if (tid == 0) sx[row] = zero_row ? 0.0f : amax / Qz::Q;
+  extern __shared__ __align__(16) uint8_t lds[];  // codes of one padded row (lift only)
+  __shared__ float red[kBlock / 64];
+  const int tid = threadIdx.x;
+  const int nvec = K / E, tail0 = nvec * E;
+  const int Kpad = (K + 2 * N - 1) / (2 * N) * (2 * N);
+  const int kl = Kpad / (2 * N) * 4 * (N - 1);  // logical K'
 
-  auto code = [&](float f) -> uint32_t { return zero_row ? 0u : (uint32_t)Qz::code(f, inv); };
-
-  if (n == 2) {
-    // no lift: codes go straight out; then zero padding up to Kc
+  uint4 cur[VPT], nxt[PIPE ? VPT : 1];
+  float ctail = 0.0f, ntail = 0.0f;
+  auto load = [&](uint4* v, float& tl, int r) {
+    const TIn* xr = X + (int64_t)r * ldx;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int64_t vi = tid + (int64_t)i * kBlock;
-      if (vi < nvec) {
-        if constexpr (E == 8) {
-          uint2 o;
-          o.x = code(V::get(v[i], 0)) | code(V::get(v[i], 1)) << 8 | code(V::get(v[i], 2)) << 16 |
-                code(V::get(v[i], 3)) << 24;
-          o.y = code(V::get(v[i], 4)) | code(V::get(v[i], 5)) << 8 | code(V::get(v[i], 6)) << 16 |
-                code(V::get(v[i], 7)) << 24;
-          *reinterpret_cast<uint2*>(qr + vi * 8) = o;
-        } else {
-          const uint32_t o = code(V::get(v[i], 0)) | code(V::get(v[i], 1)) << 8 | code(V::get(v[i], 2)) << 16 |
-                             code(V::get(v[i], 3)) << 24;
-          *reinterpret_cast<uint32_t*>(qr + vi * 4) = o;
+      const int vi = tid + i * kBlock;
+      v[i] = vi < nvec ? reinterpret_cast<const uint4*>(xr)[vi] : make_uint4(0, 0, 0, 0);
+    }
+    tl = (tail0 + tid < K) ? V::scalar(xr + tail0 + tid) : 0.0f;
+  };
+
+  int r = blockIdx.x;
+  if (r < M) load(cur, ctail, r);
+  for (; r < M; r += gridDim.x) {
+    const int rn = r + gridDim.x;
+    if (PIPE && rn < M) load(nxt, ntail, rn);
+
+    float amax = fabsf(ctail);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+#pragma unroll
+      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(V::get(cur[i], e)));
+    amax = block_max(amax, red);
+    const bool zero_row = (amax == 0.0f);
+    const float inv = zero_row ? 0.0f : Qz::Q / amax;
+    if (tid == 0) sx[r] = zero_row ? 0.0f : amax / Qz::Q;
+    auto code = [&](float f) -> uint32_t { return zero_row ? 0u : (uint32_t)Qz::code(f, inv); };
+    uint8_t* qr = Xq + (int64_t)r * ldq;
+
+    if constexpr (N == 2) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int vi = tid + i * kBlock;
+        if (vi < nvec) {
+          if constexpr (E == 8) {
+            uint2 o;
+            o.x = code(V::get(cur[i], 0)) | code(V::get(cur[i], 1)) << 8 | code(V::get(cur[i], 2)) << 16 | code(V::get(cur[i], 3)) << 24;
+            o.y = code(V::get(cur[i], 4)) | code(V::get(cur[i], 5)) << 8 | code(V::get(cur[i], 6)) << 16 | code(V::get(cur[i], 7)) << 24;
+            *reinterpret_cast<uint2*>(qr + vi * 8) = o;
+          } else {
+            *reinterpret_cast<uint32_t*>(qr + vi * 4) =
+                code(V::get(cur[i], 0)) | code(V::get(cur[i], 1)) << 8 | code(V::get(cur[i], 2)) << 16 | code(V::get(cur[i], 3)) << 24;
+          }
         }
       }
-    }
-    if (tail0 + tid < K) qr[tail0 + tid] = (uint8_t)code(tailv);
-    for (int64_t c = K + tid; c < Kc; c += kBlock) qr[c] = 0;
-    return;
-  }
-
-  // lift: stage codes of the (zero-padded) row in LDS, then gather windows
-  const int64_t Kpad = (K + 2 * n - 1) / (2 * n) * (2 * n);
+      if (tail0 + tid < K) qr[tail0 + tid] = (uint8_t)code(ctail);
+      for (int c = K + tid; c < Kc; c += kBlock) qr[c] = 0;
+    } else {
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int64_t vi = tid + (int64_t)i * kBlock;
-    if (vi < nvec) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) lds[vi * E + e] = (uint8_t)code(V::get(v[i], e));
-    }
-  }
-  if (tail0 + tid < K) lds[tail0 + tid] = (uint8_t)code(tailv);
-  for (int64_t c = K + tid; c < Kpad; c += kBlock) lds[c] = 0;
-  __syncthreads();
-
-  const int64_t kl = Kpad / (2 * n) * 4 * (n - 1);  // logical K'
-  const int64_t nchunk = Kc / 16;
-  const uint16_t* l16 = reinterpret_cast<const uint16_t*>(lds);
-  for (int64_t c = tid; c < nchunk; c += kBlock) {
-    uint32_t w4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t t = c * 4 + q;  // flat window index
-      if (4 * t < kl) {
-        const int64_t g = t / (n - 1), w = t - g * (n - 1);
-        const int64_t base = 2 * n * g + 2 * w;  // even, so two aligned halves
-        w4[q] = (uint32_t)l16[base >> 1] | ((uint32_t)l16[(base >> 1) + 1] << 16);
-      } else {
-        w4[q] = 0;
+      for (int i = 0; i < VPT; ++i) {
+        const int vi = tid + i * kBlock;
+        if (vi < nvec) {
+          if constexpr (E == 8) {
+            uint2 o;
+            o.x = code(V::get(cur[i], 0)) | code(V::get(cur[i], 1)) << 8 | code(V::get(cur[i], 2)) << 16 | code(V::get(cur[i], 3)) << 24;
+            o.y = code(V::get(cur[i], 4)) | code(V::get(cur[i], 5)) << 8 | code(V::get(cur[i], 6)) << 16 | code(V::get(cur[i], 7)) << 24;
+            *reinterpret_cast<uint2*>(lds + vi * 8) = o;
+          } else {
+            *reinterpret_cast<uint32_t*>(lds + vi * 4) =
+                code(V::get(cur[i], 0)) | code(V::get(cur[i], 1)) << 8 | code(V::get(cur[i], 2)) << 16 | code(V::get(cur[i], 3)) << 24;
+          }
+        }
       }
+      if (tail0 + tid < K) lds[tail0 + tid] = (uint8_t)code(ctail);
+      for (int c = K + tid; c < Kpad + 4; c += kBlock) lds[c] = 0;
+      __syncthreads();
+      const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds);
+      for (int c = tid; c < Kc / 16; c += kBlock) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = c * 4 + q;  // flat window index
+          if (4 * t < kl) {
+            const int g = t / (N - 1), w = t - g * (N - 1);
+            const int base = 2 * N * g + 2 * w;  // even
+            const uint32_t lo = l32[base >> 2], hi = l32[(base >> 2) + 1];
+            w4[q] = (base & 2) ? ((lo >> 16) | (hi << 16)) : lo;
+          } else {
+            w4[q] = 0;
+          }
+        }
+        *reinterpret_cast<uint4*>(qr + c * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+      __syncthreads();  // the LDS row is rewritten for the next row
     }
-    *reinterpret_cast<uint4*>(qr + c * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    if constexpr (PIPE) {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
+      ctail = ntail;
+    } else if (rn < M) {
+      load(cur, ctail, rn);
+    }
   }
 }
 
@@ -161,24 +183,49 @@ __global__ __launch_bounds__(kBlock) void quant_lift_long_kernel(const TIn* __re
   }
 }
 
-template <typename TIn, bool FP8>
-static hipError_t launch_ql(const TIn* X, int64_t ldx, int64_t M, int64_t K, int n, uint8_t* Xq, int64_t ldq,
-                            int64_t Kc, float* sx, hipStream_t st) {
+template <typename TIn, bool FP8, int N>
+hipError_t launch_n(const TIn* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq, int64_t ldq, int64_t Kc, float* sx,
+                    hipStream_t st) {
   constexpr int E = InVec<TIn>::E;
-  const int64_t nvec = K / E;
-  const int64_t vpt = (nvec + kBlock - 1) / kBlock;
-  const size_t lds = (n == 2) ? 0 : (size_t)(((K + 2 * n - 1) / (2 * n) * (2 * n) + 15) / 16 * 16);
-  dim3 grid((unsigned)M), block(kBlock);
-  if (lds <= 64 * 1024) {
-    if (vpt <= 1) { hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, 1>), grid, block, lds, st, X, ldx, K, n, Xq, ldq, Kc, sx); return hipGetLastError(); }
-    if (vpt <= 2) { hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, 2>), grid, block, lds, st, X, ldx, K, n, Xq, ldq, Kc, sx); return hipGetLastError(); }
-    if (vpt <= 4) { hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, 4>), grid, block, lds, st, X, ldx, K, n, Xq, ldq, Kc, sx); return hipGetLastError(); }
-    if (vpt <= 8) { hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, 8>), grid, block, lds, st, X, ldx, K, n, Xq, ldq, Kc, sx); return hipGetLastError(); }
-    if (vpt <= 12) { hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, 12>), grid, block, lds, st, X, ldx, K, n, Xq, ldq, Kc, sx); return hipGetLastError(); }
+  const int64_t vpt = (K / E + kBlock - 1) / kBlock;
+  const int64_t kpad = (K + 2 * N - 1) / (2 * N) * (2 * N);
+  const size_t lds = (N == 2) ? 0 : (size_t)((kpad + 4 + 15) / 16 * 16);
+  const bool fits = K < (1 << 30) && Kc < (1 << 30) && M < (1 << 30) && lds <= 64 * 1024 && vpt <= 12;
+  if (!fits) {
+    hipLaunchKernelGGL((quant_lift_long_kernel<TIn, FP8>), dim3((unsigned)M), dim3(kBlock), 0, st, X, ldx, K, N, Xq, ldq, Kc, sx);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((quant_lift_long_kernel<TIn, FP8>), grid, block, 0, st, X, ldx, K, n, Xq, ldq, Kc, sx);
+  // One row per workgroup keeps the most loads in flight for batches up to a few
+  // thousand rows; larger batches use persistent workgroups that prefetch.
+  const bool pipe = M > 16 * (int64_t)num_cus();
+  const unsigned grid = (unsigned)(pipe ? 8 * (int64_t)num_cus() : M);
+  const int m = (int)M, k = (int)K, kc = (int)Kc;
+#define SS_QL(V_) \
+  do { if (pipe) hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, true>), dim3(grid), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); else hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, false>), dim3(grid), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); } while (0)
+  if (vpt <= 1) SS_QL(1);
+  else if (vpt <= 2) SS_QL(2);
+  else if (vpt <= 4) SS_QL(4);
+  else if (vpt <= 8) SS_QL(8);
+  else SS_QL(12);
+#undef SS_QL
   return hipGetLastError();
 }
+
+template <typename TIn, bool FP8>
+hipError_t launch_ql(const TIn* X, int64_t ldx, int64_t M, int64_t K, int n, uint8_t* Xq, int64_t ldq, int64_t Kc,
+                     float* sx, hipStream_t st) {
+  switch (n) {
+    case 2: return launch_n<TIn, FP8, 2>(X, ldx, M, K, Xq, ldq, Kc, sx, st);
+    case 3: return launch_n<TIn, FP8, 3>(X, ldx, M, K, Xq, ldq, Kc, sx, st);
+    case 4: return launch_n<TIn, FP8, 4>(X, ldx, M, K, Xq, ldq, Kc, sx, st);
+    case 5: return launch_n<TIn, FP8, 5>(X, ldx, M, K, Xq, ldq, Kc, sx, st);
+    case 6: return launch_n<TIn, FP8, 6>(X, ldx, M, K, Xq, ldq, Kc, sx, st);
+    case 7: return launch_n<TIn, FP8, 7>(X, ldx, M, K, Xq, ldq, Kc, sx, st);
+    default: return launch_n<TIn, FP8, 8>(X, ldx, M, K, Xq, ldq, Kc, sx, st);
+  }
+}
+
+}  // namespace
 
 hipError_t launch_quant_lift(bool x_bf16, bool fp8, const void* X, int64_t ldx, int64_t M, int64_t K, int n,
                              void* Xq, int64_t ldq, int64_t Kc, float* sx, hipStream_t st) {
