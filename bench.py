@@ -88,7 +88,7 @@ def kernel_work(name, Kc68, Kc24):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "bench.py measures one GPU; run with --gpus 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
     import numpy as np

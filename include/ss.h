@@ -78,7 +78,7 @@ typedef enum {
   SS_ERR_ALIGN = 3,       /* a pointer or row start is not 16-byte aligned */
   SS_ERR_DTYPE = 4,       /* unsupported data-type combination */
   SS_ERR_PATTERN = 5,     /* n outside 2..8 */
-  SS_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  SS_ERR_UNSUPPORTED = 6, /* valid request the library does not implement */
   SS_ERR_HIP = 7          /* a HIP call or kernel launch failed */
 } ss_status;
 
