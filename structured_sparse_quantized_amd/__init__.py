@@ -14,6 +14,9 @@ Functions keep the names of the C entry points:
     quant_lift_act(X, n, q_dtype)           -> (Xq, sx)
     prune24_act(X, out_dtype)               -> (vals, meta, sx | None)
     spgemm(side, M, N, Kc, vals, meta, dense, sx, sw, y_dtype) -> Y [M, N]
+    tiled_bytes(rows, Kc)                   -> (tvals bytes, tmeta bytes)
+    pack_sparse(vals, meta)                 -> (tvals, tmeta)  8-bit tiled operand
+    spgemm_tiled(side, M, N, Kc, tvals, tmeta, dense, sx, sw, y_dtype) -> Y [M, N]
 """
 from __future__ import annotations
 
@@ -47,11 +50,19 @@ lib.ss_slide_decompose.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp,
 lib.ss_quant_lift_act.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp, _i64, _fp, _vp]
 lib.ss_prune24_act.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _fp, _vp]
 lib.ss_spgemm.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
-for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm"):
+lib.ss_tiled_vals_bytes.argtypes = [_i64, _i64]
+lib.ss_tiled_vals_bytes.restype = _i64
+lib.ss_tiled_meta_bytes.argtypes = [_i64, _i64]
+lib.ss_tiled_meta_bytes.restype = _i64
+lib.ss_pack_sparse.argtypes = [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _vp, _vp]
+lib.ss_spgemm_tiled.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
+for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm", "ss_pack_sparse",
+           "ss_spgemm_tiled"):
     getattr(lib, _f).restype = _int
 
 EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_error", "ss_version",
-           "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm")
+           "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm",
+           "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_spgemm_tiled")
 
 
 class SSError(RuntimeError):
@@ -166,4 +177,35 @@ def spgemm(side: int, M: int, N: int, Kc: int, vals: torch.Tensor, meta: torch.T
     Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
     _check(lib.ss_spgemm(side, M, N, Kc, dtype_code(vals.dtype), _ptr(vals), _ld(vals), _ptr(meta), _ld(meta),
                          _ptr(dense), _ld(dense), _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _stream(dense.device)))
+    return Y
+
+
+def tiled_bytes(rows: int, Kc: int):
+    return int(lib.ss_tiled_vals_bytes(rows, Kc)), int(lib.ss_tiled_meta_bytes(rows, Kc))
+
+
+def pack_sparse(vals: torch.Tensor, meta: torch.Tensor, out=None):
+    """Row-major compressed 8-bit operand -> tiled operand (flat uint8 tensors)."""
+    rows, half = vals.shape
+    Kc = 2 * half
+    if out is None:
+        nv, nm = tiled_bytes(rows, Kc)
+        if nv < 0:
+            raise SSError(SS_ERR_SHAPE)
+        tv = torch.empty(nv, dtype=torch.uint8, device=vals.device)
+        tm = torch.empty(nm, dtype=torch.uint8, device=vals.device)
+    else:
+        tv, tm = out
+    _check(lib.ss_pack_sparse(rows, Kc, dtype_code(vals.dtype), _ptr(vals), _ld(vals), _ptr(meta), _ld(meta),
+                              _ptr(tv), _ptr(tm), _stream(vals.device)))
+    return tv, tm
+
+
+def spgemm_tiled(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta: torch.Tensor, dense: torch.Tensor,
+                 sx=None, sw=None, y_dtype="bf16", out=None):
+    """Y [M, N] = tiled-sparse x dense product with the per-token x per-channel rescale."""
+    y = dtype_code(y_dtype)
+    Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
+    _check(lib.ss_spgemm_tiled(side, M, N, Kc, dtype_code(dense.dtype), _ptr(tvals), _ptr(tmeta), _ptr(dense),
+                               _ld(dense), _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _stream(dense.device)))
     return Y

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libss.so")
-SOURCES = ["ss_api.hip", "k_quant_lift.hip", "k_prune.hip", "k_slide.hip", "k_spgemm.hip"]
+SOURCES = ["ss_api.hip", "k_quant_lift.hip", "k_prune.hip", "k_slide.hip", "k_spgemm.hip", "k_spgemm_tiled.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,0 +1,342 @@
+// 2:4 sparse x dense product on a pre-tiled sparse operand (gfx950 v_smfmac),
+// with the per-token x per-channel rescale epilogue, and the pack kernel that
+// writes the tiled operand.
+// Deep reading of arXiv 2610.28947 (introduction: one operand keeps two of
+// every four along the accumulate axis; section 3.1: sparse W or sparse X);
+// SlideSparse blog section 2.2 step 3; LLM Compressor W8A8 scales.
+//
+// C[r][c] = sum_k A[r][k] B[c][k]; A = compressed operand (rows r), B = dense
+// operand (rows c). side W: r = output channel n, c = token m; side X: r =
+// token m, c = output channel n.
+//
+// Tiled sparse operand (8-bit values). A step is 128 K positions: 64
+// compressed bytes and one 32-bit index word per 32 positions of each row.
+//   values: rows in blocks of 16; per block and step one 1 KB block in
+//     instruction lane order -- bytes 16l .. 16l+15 are compressed bytes
+//     16(l/16) .. 16(l/16)+15 of row 16b + l%16 in that step. A row block's
+//     steps are consecutive; the step count is padded to a multiple of 4 with
+//     zero values (rows past the end are zero too).
+//   metadata: per row block and group of 4 steps one 1 KB block; 32-bit word
+//     4l + q is lane l's index word for step 4g + q, i.e. bytes
+//     16(4g+q) + 4(l/16) .. +3 of that row's row-major metadata. Padding words
+//     are 0x44444444 (positions 0 and 1 of each group, with zero values).
+// A lane's instruction operands are therefore one contiguous 16-byte slice of
+// a block, and a whole wave's fragment is one contiguous 1 KB read.
+//
+// Product kernel: 256 (A rows) x 128 (B rows) per workgroup of 8 waves (4 x 2),
+// each wave 64 x 64 = 4 x 4 instructions per step. A ring of four 1-step LDS
+// stages (16 KB of A values + 16 KB of B) is filled by LDS DMA
+// (global_load_lds, 1 KB per wave instruction); the index words go straight to
+// registers one 4-step group ahead. Each step waits for the next step's stage,
+// then reads that stage's fragments while the current step's smfmacs run.
+#include <type_traits>
+
+#include "ss_device.h"
+#include "ss_kernels.h"
+#include "ss_store.h"
+
+namespace ss {
+namespace tiled {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+#define SS_LDS __attribute__((address_space(3)))
+
+constexpr int BM = 256, BN = 128, WGM = 4, WGN = 2, NW = WGM * WGN, S = 4;
+constexpr int TI = BM / WGM / 16, TJ = BN / WGN / 16;          // 4 x 4 instructions per wave per step
+constexpr int PA = BM / 16 / NW, PB = BN / 8 / NW, LPW = PA + PB;  // LDS DMA loads per wave per step
+constexpr int A_BYTES = BM * 64, STAGE = A_BYTES + BN * 128;   // 32 KB
+constexpr int LDS = S * STAGE;                                 // 128 KB
+static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN, "load split");
+static_assert(S >= 3 && S <= 5, "wait counts below assume 3..5 stages");
+
+template <int AB> struct Mma;
+template <> struct Mma<0> {
+  using Acc = v4i;
+  __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
+    return __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, idx, 0, 0);
+  }
+};
+template <> struct Mma<1> {
+  using Acc = v4f;
+  __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, idx,
+                                                          0, 0);
+  }
+};
+
+// B rows in LDS: 8 rows x 128 bytes per 1 KB block; chunk c of row r sits at chunk position c ^ (r % 8).
+__device__ __forceinline__ int swz(int c, int r16) { return c ^ (r16 & 7); }
+
+// One thread per (row block, 4-step group, lane); 4 row blocks per workgroup.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ vals, int64_t ldv,
+                                                   const uint8_t* __restrict__ meta, int64_t ldm, int R, int KS,
+                                                   int KS4, int nrb, uint8_t* __restrict__ tv, uint8_t* __restrict__ tm) {
+  const int g = blockIdx.x, rb = blockIdx.y * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (rb >= nrb) return;
+  const int row = rb * 16 + (l & 15), c = l >> 4;
+  const bool live = row < R;
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int s = 4 * g + q;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    w[q] = 0x44444444u;
+    if (live && s < KS) {
+      v = *reinterpret_cast<const uint4*>(vals + row * ldv + 64 * s + 16 * c);
+      w[q] = *reinterpret_cast<const uint32_t*>(meta + row * ldm + 16 * s + 4 * c);
+    }
+    *reinterpret_cast<uint4*>(tv + ((int64_t)rb * 4 * KS4 + s) * 1024 + 16 * l) = v;
+  }
+  *reinterpret_cast<uint4*>(tm + ((int64_t)rb * KS4 + g) * 1024 + 16 * l) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int AB, int YT, bool SIDE_X>
+__global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS, const uint8_t* __restrict__ tv,
+                                                            const uint8_t* __restrict__ tm, const uint8_t* __restrict__ bd,
+                                                            int ldb, const float* __restrict__ sx,
+                                                            const float* __restrict__ sw, void* __restrict__ Y, int ldy,
+                                                            int tiles_r, int tiles_c) {
+  using Acc = typename Mma<AB>::Acc;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WGN, wn = wave % WGN;
+
+  // Tile order: workgroups are dealt to the 8 XCDs round-robin; give each XCD a
+  // contiguous run of tiles, walked in groups of 4 A-row tiles, so the tiles
+  // that share operands also share an L2.
+  const int nb = gridDim.x;
+  int bid = blockIdx.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  constexpr int GR = 4;
+  const int group = bid / (GR * tiles_c), first_r = group * GR, gsize = min(tiles_r - first_r, GR);
+  const int tr = first_r + (bid % (GR * tiles_c)) % gsize, tc = (bid % (GR * tiles_c)) / gsize;
+  const int r0 = tr * BM, c0 = tc * BN;
+  const int nrb = (R + 15) / 16, KS4 = (KS + 3) / 4, KSP = 4 * KS4;
+
+  // Per-lane sources. Rows past the end are clamped to the last row; their
+  // results are never stored.
+  const uint8_t* pa[PA];
+  uint32_t offb[PB];
+  const uint8_t* pmt[TI];
+#pragma unroll
+  for (int q = 0; q < PA; ++q) pa[q] = tv + (int64_t)min(r0 / 16 + wave + q * NW, nrb - 1) * KSP * 1024 + lane * 16;
+#pragma unroll
+  for (int q = 0; q < PB; ++q) {
+    const int b = (wave + q * NW) * 8 + (lane >> 3);
+    offb[q] = (uint32_t)min(c0 + b, C - 1) * (uint32_t)ldb + swz(lane & 7, b & 15) * 16;
+  }
+#pragma unroll
+  for (int t = 0; t < TI; ++t) pmt[t] = tm + (int64_t)min(r0 / 16 + wm * TI + t, nrb - 1) * KS4 * 1024 + lane * 16;
+
+  // Step k goes to slot k % S. Steps past the end re-read the last step (in
+  // bounds, never consumed) so that every step issues the same loads.
+  auto issue = [&](int k) {
+    SS_LDS uint8_t* base = (SS_LDS uint8_t*)smem + (k % S) * STAGE;
+    const int ka = min(k, KSP - 1), kb = min(k, KS - 1);
+#pragma unroll
+    for (int q = 0; q < PA; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(pa[q] + (int64_t)ka * 1024),
+                                       (SS_LDS void*)(base + (wave + q * NW) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < PB; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(bd + offb[q] + (uint32_t)kb * 128),
+                                       (SS_LDS void*)(base + A_BYTES + (wave + q * NW) * 1024), 16, 0, 0);
+  };
+  v4i mcur[TI], mnxt[TI];
+  auto load_meta = [&](v4i* m, int g) {
+#pragma unroll
+    for (int t = 0; t < TI; ++t) m[t] = *reinterpret_cast<const v4i*>(pmt[t] + (int64_t)g * 1024);
+  };
+
+  Acc acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) acc[i][u] = Acc{0, 0, 0, 0};
+  const int r16 = lane & 15, jj = lane >> 4;
+  struct Frag {
+    v4i a[TI];
+    v4i b[TJ][2];
+  };
+  auto read = [&](Frag& f, int k) {
+    const uint8_t* st = smem + (k % S) * STAGE;
+#pragma unroll
+    for (int t = 0; t < TI; ++t) f.a[t] = *reinterpret_cast<const v4i*>(st + (wm * TI + t) * 1024 + lane * 16);
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) {
+      const uint8_t* bb = st + A_BYTES + ((wn * TJ + u) * 2 + (r16 >> 3)) * 1024 + (r16 & 7) * 128;
+      f.b[u][0] = *reinterpret_cast<const v4i*>(bb + swz(jj, r16) * 16);
+      f.b[u][1] = *reinterpret_cast<const v4i*>(bb + swz(4 + jj, r16) * 16);
+    }
+  };
+  auto mma = [&](const Frag& f, int q) {
+#pragma unroll
+    for (int u = 0; u < TJ; ++u)
+#pragma unroll
+      for (int t = 0; t < TI; ++t) acc[t][u] = Mma<AB>::run(f.a[t], f.b[u][0], f.b[u][1], acc[t][u], mcur[t][q]);
+  };
+  // Loads complete in issue order, so "stage k+1 has landed" is a wait until at
+  // most N of this wave's loads are outstanding, N = the loads issued after
+  // stage k+1: the S-3 later stages (LPW each) plus the index groups issued
+  // since (TI each; one is issued at every step with q == 0 except in the last
+  // group, where none is).
+  auto wait_next = [&](auto qc, auto lastc) {
+    constexpr int Q = decltype(qc)::value;
+    constexpr bool LAST = decltype(lastc)::value;
+    constexpr int lo = Q + 6 - S, hi = Q + 3;
+    constexpr int nm = LAST ? 0 : (hi >= 4 && lo <= 4 ? 1 : 0) + (hi >= 8 && lo <= 8 ? 1 : 0);
+    constexpr int N = (S - 3) * LPW + nm * TI;
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  };
+  constexpr int RD = TI + 2 * TJ, NM = TI * TJ;
+  // Step j (j + 1 < KSP): make stage j+1 resident, read its fragments while
+  // multiplying step j.
+  auto step = [&](int j, auto qc, auto lastc, Frag& cur, Frag& nxt) {
+    constexpr int Q = decltype(qc)::value;
+    constexpr bool LAST = decltype(lastc)::value;
+    // the fences keep the scheduler from moving loads across the wait and the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    wait_next(qc, lastc);
+    __builtin_amdgcn_s_barrier();  // every wave's loads of stage j+1 landed; slot (j-1) % S is free
+    __builtin_amdgcn_sched_barrier(0);
+    issue(j + S - 1);
+    if (Q == 0 && !LAST) load_meta(mnxt, j / 4 + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read(nxt, j + 1);
+    mma(cur, Q);
+#pragma unroll
+    for (int p = 0; p < NM; ++p) {
+      if (p < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one smfmac
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
+  using NotLast = std::false_type;
+  using Last = std::true_type;
+
+  load_meta(mcur, 0);
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+  Frag f0, f1;
+  {
+    constexpr int N = (S - 2) * LPW;  // stage 0 landed
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  }
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read(f0, 0);
+  for (int g = 0; g + 1 < KS4; ++g) {
+    const int j = 4 * g;
+    step(j, Q0{}, NotLast{}, f0, f1);
+    step(j + 1, Q1{}, NotLast{}, f1, f0);
+    step(j + 2, Q2{}, NotLast{}, f0, f1);
+    step(j + 3, Q3{}, NotLast{}, f1, f0);
+#pragma unroll
+    for (int t = 0; t < TI; ++t) mcur[t] = mnxt[t];
+  }
+  {
+    const int j = KSP - 4;
+    step(j, Q0{}, Last{}, f0, f1);
+    step(j + 1, Q1{}, Last{}, f1, f0);
+    step(j + 2, Q2{}, Last{}, f0, f1);
+    mma(f1, 3);
+  }
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // no load may outlive the workgroup
+
+  // Epilogue: y = fl32(fl32(float(acc) * sx[m]) * sw[n]); scales loaded up front
+  // (indices clamped; out-of-range results are never stored).
+  float s_a[TI][4], s_b[TJ];
+  const float* sa = SIDE_X ? sx : sw;  // scale indexed by A row
+  const float* sb = SIDE_X ? sw : sx;  // scale indexed by B row
+#pragma unroll
+  for (int t = 0; t < TI; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_a[t][q] = sa ? sa[min(r0 + (wm * TI + t) * 16 + 4 * jj + q, R - 1)] : 1.0f;
+#pragma unroll
+  for (int u = 0; u < TJ; ++u) s_b[u] = sb ? sb[min(c0 + (wn * TJ + u) * 16 + r16, C - 1)] : 1.0f;
+#pragma unroll
+  for (int t = 0; t < TI; ++t) {
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) {
+      const int ar = r0 + (wm * TI + t) * 16 + 4 * jj;  // 4 consecutive A rows
+      const int bc = c0 + (wn * TJ + u) * 16 + r16;     // one B row
+      if (bc >= C) continue;
+      float y[4];
+      int32_t yi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (YT == 2) {
+          yi[q] = (int32_t)acc[t][u][q];
+        } else {
+          float f = (float)acc[t][u][q];
+          // the token scale first, then the channel scale
+          const float s1 = SIDE_X ? s_a[t][q] : s_b[u], s2 = SIDE_X ? s_b[u] : s_a[t][q];
+          if (sx) f = __fmul_rn(f, s1);
+          if (sw) f = __fmul_rn(f, s2);
+          y[q] = f;
+        }
+      }
+      store_out<YT, SIDE_X>(Y, ldy, ar, bc, R, y, yi);
+    }
+  }
+}
+
+template <int AB, int YT, bool SIDE_X>
+hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb,
+                  const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
+  auto kern = spgemm_kernel<AB, YT, SIDE_X>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
+  hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * NW), LDS, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, tr, tc);
+  return hipGetLastError();
+}
+
+}  // namespace tiled
+
+int64_t tiled_vals_bytes(int64_t rows, int64_t Kc) {
+  const int64_t ks4 = (Kc / 128 + 3) / 4;
+  return (rows + 15) / 16 * ks4 * 4 * 1024;
+}
+
+int64_t tiled_meta_bytes(int64_t rows, int64_t Kc) {
+  const int64_t ks4 = (Kc / 128 + 3) / 4;
+  return (rows + 15) / 16 * ks4 * 1024;
+}
+
+hipError_t launch_pack_tiled(const uint8_t* vals, int64_t ldv, const uint8_t* meta, int64_t ldm, int64_t rows,
+                             int64_t Kc, uint8_t* tv, uint8_t* tm, hipStream_t st) {
+  const int KS = (int)(Kc / 128), KS4 = (KS + 3) / 4, nrb = (int)((rows + 15) / 16);
+  hipLaunchKernelGGL(tiled::pack_kernel, dim3(KS4, (nrb + 3) / 4), dim3(256), 0, st, vals, ldv, meta, ldm, (int)rows, KS,
+                     KS4, nrb, tv, tm);
+  return hipGetLastError();
+}
+
+hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C, int64_t Kc, const uint8_t* tv,
+                               const uint8_t* tm, const void* bd, int64_t ldb_bytes, const float* sx, const float* sw,
+                               void* Y, int64_t ldy, hipStream_t st) {
+  const uint8_t* b = static_cast<const uint8_t*>(bd);
+  const int r = (int)R, c = (int)C, ks = (int)(Kc / 128), lb = (int)ldb_bytes, ly = (int)ldy;
+#define SS_TL(AB_, YT_)                                                                                   \
+  return side_x ? tiled::launch<AB_, YT_, true>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)               \
+                : tiled::launch<AB_, YT_, false>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)
+  if (ab == 0) {
+    if (yt == 0) SS_TL(0, 0);
+    if (yt == 1) SS_TL(0, 1);
+    SS_TL(0, 2);
+  }
+  if (yt == 0) SS_TL(1, 0);
+  SS_TL(1, 1);
+#undef SS_TL
+}
+
+}  // namespace ss

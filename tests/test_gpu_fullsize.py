@@ -42,9 +42,13 @@ def test_small_24_int8_exact(ss):
     ow, ox = oracle.prune24(W, "i8"), oracle.quant_lift_act(X, 2, "i8")
     _check_prep(w, ow)
     _check_prep(x, ox)
+    tv, tm = ss.pack_sparse(w[0], w[1])
     for y in ("i32", "f32"):
+        exp = oracle.spgemm("W", ow[0], ow[1], ox[0], c["K"], "i8", ox[1], ow[2], y)
         Y = host(ss.spgemm(ss.SS_SPARSE_W, c["M"], c["N"], c["K"], w[0], w[1], x[0], x[1], w[2], y))
-        assert np.array_equal(Y, oracle.spgemm("W", ow[0], ow[1], ox[0], c["K"], "i8", ox[1], ow[2], y))
+        assert np.array_equal(Y, exp)
+        Yt = host(ss.spgemm_tiled(ss.SS_SPARSE_W, c["M"], c["N"], c["K"], tv, tm, x[0], x[1], w[2], y))
+        assert np.array_equal(Yt, exp)
 
 
 def test_68_int8_full_size(ss):
@@ -64,6 +68,11 @@ def test_68_int8_full_size(ss):
     r = _rows(M)
     exp = oracle.spgemm("W", ow[0], ow[1], ox[0][r], Kc, "i8", ox[1][r], ow[2], "bf16")
     assert np.array_equal(Y[r], exp)
+    # the tiled product, as the benchmark launches it: same bytes everywhere
+    tv, tm = ss.pack_sparse(w[0], w[1])
+    Yt = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, x[0], x[1], w[2], "bf16"))
+    assert np.array_equal(Yt[r], exp)
+    assert np.array_equal(Yt, Y)
 
 
 @pytest.mark.parametrize("name", ["qkv", "down"])
@@ -81,6 +90,9 @@ def test_llama_fp8_24_sampled(ss, name):
     assert np.array_equal(host(x[0])[r].view(np.uint8), ox[0]) and np.array_equal(host(x[1])[r], ox[1])
     exp = oracle.spgemm("W", ow[0], ow[1], ox[0], K, "fp8", ox[1], ow[2], "bf16")
     assert rel_fro(bf16_to_f64(Y[r]), bf16_to_f64(exp)) <= 1e-2
+    tv, tm = ss.pack_sparse(w[0], w[1])
+    Yt = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, K, tv, tm, x[0], x[1], w[2], "bf16"))
+    assert rel_fro(bf16_to_f64(Yt[r]), bf16_to_f64(exp)) <= 1e-2
 
 
 @pytest.mark.parametrize("out", ["bf16", "fp8"])
@@ -102,6 +114,10 @@ def test_sparse_activation_full_size(ss, out):
     r = _rows(M, 24)
     exp = oracle.spgemm("X", oxs[0][r], oxs[1][r], ow, K, out, None if oxs[2] is None else oxs[2][r], osw, "bf16")
     assert rel_fro(bf16_to_f64(Y[r]), bf16_to_f64(exp)) <= 1e-2
+    if out == "fp8":
+        tv, tm = ss.pack_sparse(xs[0], xs[1])
+        Yt = host(ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, K, tv, tm, wd, xs[2], sw, "bf16"))
+        assert rel_fro(bf16_to_f64(Yt[r]), bf16_to_f64(exp)) <= 1e-2
 
 
 @pytest.mark.parametrize("n", [3, 5])
@@ -120,6 +136,9 @@ def test_qwen_qkv_slide_int8(ss, n, M):
     assert np.array_equal(host(x[0])[r], ox[0]) and np.array_equal(host(x[1])[r], ox[1])
     exp = oracle.spgemm("W", ow[0], ow[1], ox[0], Kc, "i8", ox[1], ow[2], "bf16")
     assert np.array_equal(Y[r], exp)
+    tv, tm = ss.pack_sparse(w[0], w[1])
+    Yt = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, x[0], x[1], w[2], "bf16"))
+    assert np.array_equal(Yt[r], exp)
 
 
 def test_qwen_down_810_int8_decode(ss):
@@ -135,4 +154,8 @@ def test_qwen_down_810_int8_decode(ss):
     ow, ox = oracle.slide_decompose(W, n, "i8"), oracle.quant_lift_act(X, n, "i8")
     _check_prep(w, ow)
     _check_prep(x, ox)
-    assert np.array_equal(Y, oracle.spgemm("W", ow[0], ow[1], ox[0], Kc, "i8", ox[1], ow[2], "bf16"))
+    exp = oracle.spgemm("W", ow[0], ow[1], ox[0], Kc, "i8", ox[1], ow[2], "bf16")
+    assert np.array_equal(Y, exp)
+    tv, tm = ss.pack_sparse(w[0], w[1])
+    Yt = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, x[0], x[1], w[2], "bf16"))
+    assert np.array_equal(Yt, exp)
