@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernels-only", action="store_true", help="skip the dense comparator and CPU baseline")
+    p.add_argument("--no-suite", action="store_true", help="skip the Llama/Qwen-shaped layer suite")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (the reference for HBM byte counters)")
     return p.parse_args()
@@ -249,6 +250,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    suite_res = None
+    if not (args.no_suite or args.kernels_only):
+        del bufs
+        torch.cuda.empty_cache()
+        suite_res = suite(ss, torch, dev)
+
     cpu = None
     if not (args.no_cpu or args.kernels_only):
         cpu = cpu_baseline(X_np, W_np, Kc68, Kc24)
@@ -271,8 +278,146 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "rotating_buffer_sets": NBUF,
+        "suite": suite_res,
     }
     print(json.dumps(out))
+
+
+def suite(ss, torch, dev, reps=10):
+    """Layer-shaped products on synthetic data (seeded on the GPU): Llama-3.1-8B-shaped 2:4 FP8 weight
+    GEMMs at M = 2048..16384 against dense FP8 (hipBLASLt through torch._scaled_mm, same per-token /
+    per-channel scales); Qwen2.5-7B-shaped 4:6 and 8:10 INT8 GEMMs at decode and prefill M; the
+    sparse-activation FP8 layer; quant+lift bandwidth on a large batch and a plain device copy."""
+    import synth
+    print("[bench] layer suite", file=sys.stderr, flush=True)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261203)
+
+    def randn(shape, std=1.0, dtype=torch.float32):
+        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(dtype)
+
+    def timed(fn, n=reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    res = {"data": "synthetic: W ~ N(0, 0.02^2) float32, X ~ N(0, 1) bf16, generated on the GPU (seeded)"}
+    # Llama-3.1-8B-shaped 2:4 FP8 weight GEMMs
+    llama = {}
+    for M in (2048, 4096, 8192, 16384):
+        rows, tot_sp, tot_dn = [], 0.0, 0.0
+        for name, (K, Nout) in synth.LLAMA31_8B_LINEARS.items():
+            W = randn((Nout, K), 0.02)
+            wv, wm, sw = ss.prune24(W, "fp8")
+            tv, tm = ss.pack_sparse(wv, wm)
+            wq, swd = ss.quant_lift_act(W, 2, "fp8")
+            del W, wv, wm
+            X = randn((M, K), 1.0, torch.bfloat16)
+            xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+            sx = torch.empty(M, dtype=torch.float32, device=dev)
+            Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+            t_q = timed(lambda: ss.quant_lift_act(X, 2, "fp8", out=(xq, sx)))
+            t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, K, tv, tm, xq, sx, sw, "bf16", out=Y))
+            try:
+                t_dn = timed(lambda: torch._scaled_mm(xq, wq.t(), scale_a=sx[:, None], scale_b=swd[None, :],
+                                                      out_dtype=torch.bfloat16))
+            except Exception:
+                t_dn = None
+            dense_eq = 2.0 * M * Nout * K
+            rows.append({"layer": name, "K": K, "N": Nout, "quant_us": t_q, "sparse_gemm_us": t_sp,
+                         "sparse_TOPS_dense_equiv": dense_eq / t_sp / 1e6,
+                         "sparse_frac_of_10070": dense_eq / t_sp / 1e6 / 10070.0,
+                         "dense_fp8_gemm_us": t_dn,
+                         "dense_TFLOPS": None if t_dn is None else dense_eq / t_dn / 1e6})
+            tot_sp += t_q + t_sp
+            tot_dn += t_q + (t_dn if t_dn is not None else float("nan"))
+            del tv, tm, wq, swd, X, xq, sx, Y
+        llama[str(M)] = {"layers": rows, "sparse_tokens_per_s": M / (tot_sp * 1e-6),
+                         "dense_tokens_per_s": M / (tot_dn * 1e-6), "speedup": tot_dn / tot_sp}
+        torch.cuda.empty_cache()
+    res["llama31_8b_24_fp8"] = llama
+    # Qwen2.5-7B-shaped sliding-window INT8 GEMMs, decode and prefill token counts
+    qwen = []
+    for n in (3, 5):
+        for name, (K, Nout) in synth.QWEN25_7B_LINEARS.items():
+            W = randn((Nout, K), 0.02)
+            wv, wm, sw = ss.slide_decompose(W, n, "i8")
+            tv, tm = ss.pack_sparse(wv, wm)
+            Kc = ss.lifted_k(K, n)
+            del W, wv, wm
+            for M in (1, 16, 64, 4096):
+                X = randn((M, K), 1.0, torch.bfloat16)
+                xq = torch.empty((M, Kc), dtype=torch.int8, device=dev)
+                sx = torch.empty(M, dtype=torch.float32, device=dev)
+                Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+                t_q = timed(lambda: ss.quant_lift_act(X, n, "i8", out=(xq, sx)))
+                t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y))
+                wbytes = tv.numel() + tm.numel()
+                qwen.append({"pattern": f"{2 * n - 2}:{2 * n}", "layer": name, "M": M, "K": K, "K_prime": Kc,
+                             "N": Nout, "quant_lift_us": t_q, "sparse_gemm_us": t_sp,
+                             "sparse_TOPS_dense_equiv": 2.0 * M * Nout * Kc / t_sp / 1e6,
+                             "weight_stream_GBs": wbytes / t_sp / 1e3,
+                             "tokens_per_s": M / ((t_q + t_sp) * 1e-6)})
+                del X, xq, sx, Y
+            del tv, tm
+            torch.cuda.empty_cache()
+    res["qwen25_7b_slide_int8"] = qwen
+    # sparse-activation layer: X 8192x4096 pruned 2:4 online (FP8), dense W 4096x4096 FP8
+    M, K, Nout = 8192, 4096, 4096
+    X = randn((M, K), 1.0, torch.bfloat16)
+    wq, swd = ss.quant_lift_act(randn((Nout, K), 0.02), 2, "fp8")
+    xv = torch.empty((M, K // 2), dtype=torch.float8_e4m3fn, device=dev)
+    xm = torch.empty((M, K // 8), dtype=torch.uint8, device=dev)
+    sx = torch.empty(M, dtype=torch.float32, device=dev)
+    nv, nm = ss.tiled_bytes(M, K)
+    tv = torch.empty(nv, dtype=torch.uint8, device=dev)
+    tm = torch.empty(nm, dtype=torch.uint8, device=dev)
+    Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    t_pr = timed(lambda: ss.prune24_act(X, "fp8", out=(xv, xm, sx)))
+    t_pk = timed(lambda: ss.pack_sparse(xv, xm, out=(tv, tm)))
+    t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, Nout, K, tv, tm, wq, sx, swd, "bf16", out=Y))
+    t_q = timed(lambda: ss.quant_lift_act(X, 2, "fp8", out=(xq, sx)))
+    try:
+        t_dn = timed(lambda: torch._scaled_mm(xq, wq.t(), scale_a=sx[:, None], scale_b=swd[None, :],
+                                              out_dtype=torch.bfloat16))
+    except Exception:
+        t_dn = None
+    res["sparse_activation_fp8"] = {
+        "M": M, "K": K, "N": Nout, "prune24_act_us": t_pr, "pack_us": t_pk, "sparse_gemm_us": t_sp,
+        "sparse_TOPS_dense_equiv": 2.0 * M * Nout * K / t_sp / 1e6, "dense_quant_us": t_q,
+        "dense_fp8_gemm_us": t_dn,
+        "speedup_vs_dense": None if t_dn is None else (t_q + t_dn) / (t_pr + t_pk + t_sp)}
+    del X, wq, swd, xv, xm, sx, tv, tm, Y, xq
+    torch.cuda.empty_cache()
+    # quant+lift on a large batch (launch latency amortised) and a plain device copy
+    ql = {}
+    for n in (2, 4):
+        M, K = 16384, 4096
+        X = randn((M, K), 1.0, torch.bfloat16)
+        Kc = ss.lifted_k(K, n)
+        xq = torch.empty((M, Kc), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        t = timed(lambda: ss.quant_lift_act(X, n, "i8", out=(xq, sx)))
+        byts = 2 * M * K + M * Kc + 4 * M
+        ql[f"n{n}"] = {"M": M, "K": K, "K_prime": Kc, "us": t, "GB/s": byts / t / 1e3,
+                       "frac_of_8000": byts / t / 1e3 / 8000.0}
+        del X, xq, sx
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), n=5)
+    ql["device_copy_1GiB_GBs"] = 2 * (1 << 30) / t / 1e3
+    del src, dst
+    torch.cuda.empty_cache()
+    res["quant_lift_large_int8"] = ql
+    return res
 
 
 def cpu_baseline(X_np, W_np, Kc68, Kc24):
