@@ -29,6 +29,13 @@
 // (global_load_lds, 1 KB per wave instruction); the index words go straight to
 // registers one 4-step group ahead. Each step waits for the next step's stage,
 // then reads that stage's fragments while the current step's smfmacs run.
+//
+// Decode kernel (side W, at most 64 tokens, when the tiled grid would leave
+// the chip idle): one 16-row block per workgroup of 8 waves; the waves split
+// the K steps in whole 4-step index groups, stream the sparse values straight
+// to registers (a 4-step ring) with the few token rows of the dense operand,
+// and sum their partial tiles through LDS before the same epilogue. The
+// weight stream is the HBM-bound part.
 #include <type_traits>
 
 #include "ss_device.h"
@@ -100,7 +107,9 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
                                                             int tiles_r, int tiles_c) {
   using Acc = typename Mma<AB>::Acc;
   extern __shared__ __align__(16) uint8_t smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WGN, wn = wave % WGN;
+  // the wave index is uniform: keep it (and the addresses built from it) in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
 
   // Tile order: workgroups are dealt to the 8 XCDs round-robin; give each XCD a
   // contiguous run of tiles, walked in groups of 4 A-row tiles, so the tiles
@@ -303,6 +312,108 @@ hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, co
 
 }  // namespace tiled
 
+
+namespace decode {
+
+constexpr int NW = 8;
+
+// One workgroup per 16-row block of the sparse operand; NCT = 16-token column tiles (C <= 16 * NCT).
+template <int AB, int YT, int NCT>
+__global__ __launch_bounds__(64 * NW, 1) void decode_kernel(int R, int C, int KS, const uint8_t* __restrict__ tv,
+                                                            const uint8_t* __restrict__ tm,
+                                                            const uint8_t* __restrict__ bd, int ldb,
+                                                            const float* __restrict__ sx,
+                                                            const float* __restrict__ sw, void* __restrict__ Y,
+                                                            int ldy) {
+  using Acc = typename tiled::Mma<AB>::Acc;
+  __shared__ Acc red[NW][NCT][64];
+  const int rb = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, jj = lane >> 4;
+  const int KS4 = (KS + 3) / 4, KSP = 4 * KS4;
+  const int g0 = KS4 * wave / NW, g1 = KS4 * (wave + 1) / NW;  // this wave's 4-step groups
+  Acc acc[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) acc[c] = Acc{0, 0, 0, 0};
+  if (g0 < g1) {
+    const uint8_t* pa = tv + (int64_t)rb * KSP * 1024 + lane * 16;
+    const uint8_t* pm = tm + (int64_t)rb * KS4 * 1024 + lane * 16;
+    const uint8_t* pb[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) pb[c] = bd + (int64_t)min(c * 16 + r16, C - 1) * ldb + 16 * jj;
+    tiled::v4i A[4], B[4][NCT][2], mcur, mnxt;
+    // padded steps (>= KS) hold zero values; their dense slices re-read step KS-1
+    auto load_step = [&](int slot, int k) {
+      const int kb = min(k, KS - 1);
+      A[slot] = *reinterpret_cast<const tiled::v4i*>(pa + (int64_t)k * 1024);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        B[slot][c][0] = *reinterpret_cast<const tiled::v4i*>(pb[c] + (int64_t)kb * 128);
+        B[slot][c][1] = *reinterpret_cast<const tiled::v4i*>(pb[c] + (int64_t)kb * 128 + 64);
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_step(q, 4 * g0 + q);
+    mcur = *reinterpret_cast<const tiled::v4i*>(pm + (int64_t)g0 * 1024);
+    mnxt = *reinterpret_cast<const tiled::v4i*>(pm + (int64_t)min(g0 + 1, KS4 - 1) * 1024);
+    for (int g = g0; g < g1; ++g) {
+      const int kn = min(4 * (g + 1), KSP - 4);  // next group (re-read past the end, never used)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) acc[c] = tiled::Mma<AB>::run(A[q], B[q][c][0], B[q][c][1], acc[c], mcur[q]);
+        load_step(q, kn + q);
+      }
+      mcur = mnxt;
+      mnxt = *reinterpret_cast<const tiled::v4i*>(pm + (int64_t)min(g + 2, KS4 - 1) * 1024);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) red[wave][c][lane] = acc[c];
+  __syncthreads();
+  if (wave < NCT) {
+    const int c = wave;
+    Acc s = red[0][c][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s += red[w][c][lane];
+    const int ar = rb * 16 + 4 * jj, bc = c * 16 + r16;
+    if (bc < C) {
+      float y[4];
+      int32_t yi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (YT == 2) {
+          yi[q] = (int32_t)s[q];
+        } else {
+          float f = (float)s[q];
+          if (sx) f = __fmul_rn(f, sx[bc]);
+          if (sw) f = __fmul_rn(f, sw[min(ar + q, R - 1)]);
+          y[q] = f;
+        }
+      }
+      store_out<YT, false>(Y, ldy, ar, bc, R, y, yi);
+    }
+  }
+}
+
+template <int AB, int YT>
+hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb,
+                  const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
+  const int nrb = (R + 15) / 16;
+  if (C <= 16)
+    hipLaunchKernelGGL((decode_kernel<AB, YT, 1>), dim3(nrb), dim3(64 * NW), 0, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y,
+                       ldy);
+  else if (C <= 32)
+    hipLaunchKernelGGL((decode_kernel<AB, YT, 2>), dim3(nrb), dim3(64 * NW), 0, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y,
+                       ldy);
+  else
+    hipLaunchKernelGGL((decode_kernel<AB, YT, 4>), dim3(nrb), dim3(64 * NW), 0, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y,
+                       ldy);
+  return hipGetLastError();
+}
+
+}  // namespace decode
+
 int64_t tiled_vals_bytes(int64_t rows, int64_t Kc) {
   const int64_t ks4 = (Kc / 128 + 3) / 4;
   return (rows + 15) / 16 * ks4 * 4 * 1024;
@@ -326,9 +437,13 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
                                void* Y, int64_t ldy, hipStream_t st) {
   const uint8_t* b = static_cast<const uint8_t*>(bd);
   const int r = (int)R, c = (int)C, ks = (int)(Kc / 128), lb = (int)ldb_bytes, ly = (int)ldy;
+  // few tokens and too few 256-row tiles to fill the chip: the row-block decode kernel
+  const int64_t tiles = ((R + tiled::BM - 1) / tiled::BM) * ((C + tiled::BN - 1) / tiled::BN);
+  const bool dec = !side_x && C <= 64 && (C <= 8 || tiles < 128);
 #define SS_TL(AB_, YT_)                                                                                   \
-  return side_x ? tiled::launch<AB_, YT_, true>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)               \
-                : tiled::launch<AB_, YT_, false>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)
+  return dec      ? decode::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)                   \
+         : side_x ? tiled::launch<AB_, YT_, true>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)               \
+                  : tiled::launch<AB_, YT_, false>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)
   if (ab == 0) {
     if (yt == 0) SS_TL(0, 0);
     if (yt == 1) SS_TL(0, 1);

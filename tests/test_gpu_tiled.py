@@ -162,3 +162,29 @@ def test_repeated_calls_and_streams(ss):
     st.synchronize()
     for o in outs:
         assert np.array_equal(host(o), exp)
+
+
+# Few tokens (side W): the product runs the row-block decode kernel (16 rows per workgroup, K split across
+# waves, partial sums reduced in LDS); these cases cover its column-tile counts (<= 16, 32, 64 tokens), ragged
+# row counts, K short enough that some waves get no work, and long K.
+DECODE_SHAPES = [(1, 1000, 512), (5, 1000, 600), (8, 260, 2048), (9, 300, 1000), (16, 512, 4096), (17, 130, 512),
+                 (32, 700, 3000), (33, 520, 768), (64, 1000, 6000), (64, 4608, 3584)]
+
+
+@pytest.mark.parametrize("ab", ["i8", "fp8"])
+@pytest.mark.parametrize("shape", DECODE_SHAPES)
+def test_spgemm_tiled_decode_tokens(ss, ab, shape):
+    M, N, K = shape
+    n = 3 if K % 6 == 0 else 2
+    vals, meta, dense, sx, sw, Kc = _gemm_case(101 + M + N, M, N, K, n, ab, "W")
+    tv, tm = ss.pack_sparse(dev_codes(vals, ab), dev_u8(meta))
+    d, dsx, dsw = dev_codes(dense, ab), dev_f32(sx), dev_f32(sw)
+    for y in (["i32", "bf16"] if ab == "i8" else ["f32", "bf16"]):
+        Y = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, d, dsx, dsw, y_dtype=y))
+        exp = oracle.spgemm("W", vals, meta, dense, Kc, ab, sx, sw, y)
+        if ab == "i8":
+            assert np.array_equal(Y, exp), y
+        elif y == "bf16":
+            assert rel_fro(bf16_to_f64(Y), bf16_to_f64(exp)) <= TOL
+        else:
+            assert rel_fro(Y, exp) <= TOL
