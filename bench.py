@@ -397,6 +397,26 @@ def suite(ss, torch, dev, reps=10):
         "speedup_vs_dense": None if t_dn is None else (t_q + t_dn) / (t_pr + t_pk + t_sp)}
     del X, wq, swd, xv, xm, sx, tv, tm, Y, xq
     torch.cuda.empty_cache()
+    # the same layer in bf16 (no quantisation): online prune + pack + product against dense bf16 (hipBLASLt)
+    X = randn((M, K), 1.0, torch.bfloat16)
+    Wb = randn((Nout, K), 0.02, torch.bfloat16)
+    xv = torch.empty((M, K // 2), dtype=torch.bfloat16, device=dev)
+    xm = torch.empty((M, K // 8), dtype=torch.uint8, device=dev)
+    nv, nm = ss.tiled_bytes(M, K, "bf16")
+    tv = torch.empty(nv, dtype=torch.uint8, device=dev)
+    tm = torch.empty(nm, dtype=torch.uint8, device=dev)
+    Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+    t_pr = timed(lambda: ss.prune24_act(X, "bf16", out=(xv, xm, None)))
+    t_pk = timed(lambda: ss.pack_sparse(xv, xm, out=(tv, tm)))
+    t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, Nout, K, tv, tm, Wb, None, None, "bf16", out=Y))
+    t_dn = timed(lambda: torch.matmul(X, Wb.t()))
+    res["sparse_activation_bf16"] = {
+        "M": M, "K": K, "N": Nout, "prune24_act_us": t_pr, "pack_us": t_pk, "sparse_gemm_us": t_sp,
+        "sparse_TFLOPS_dense_equiv": 2.0 * M * Nout * K / t_sp / 1e6,
+        "sparse_frac_of_5030": 2.0 * M * Nout * K / t_sp / 1e6 / 5030.0, "dense_bf16_gemm_us": t_dn,
+        "speedup_vs_dense": t_dn / (t_pr + t_pk + t_sp)}
+    del X, Wb, xv, xm, tv, tm, Y
+    torch.cuda.empty_cache()
     # quant+lift on a large batch (launch latency amortised) and a plain device copy
     ql = {}
     for n in (2, 4):

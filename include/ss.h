@@ -175,41 +175,48 @@ ss_status ss_spgemm(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_
                     ss_dtype y_dt, void* Y, int64_t ldy, void* stream);
 
 /* Tiled sparse operand -- the layout ss_spgemm_tiled streams.
- * A re-arrangement of a compressed operand with 8-bit values (I8 or
- * FP8E4M3; same bytes, same product) into the lane order of the gfx950
- * 16x16x128 structured-sparse instructions, so that each wave's share of a
- * K step is one contiguous 1 KB block. A step is 128 K positions.
- * With KS = Kc/128, G = ceil(KS/4), RB = ceil(rows/16):
+ * A re-arrangement of a compressed operand (same values, same 2:4 positions)
+ * into the lane order of the gfx950 structured-sparse instructions
+ * (16x16x128 for I8/FP8E4M3, 16x16x64 for BF16), so that each wave's share of
+ * a K step is one contiguous 1 KB block. A step is 64 compressed bytes of a
+ * row: 128 K positions for 8-bit values, 64 for BF16. With
+ * KS = Kc*es/128 (es = value bytes), G = ceil(KS/4), RB = ceil(rows/16):
  *   tvals: RB*4G blocks of 1024 bytes; block (b, s) at byte (b*4G + s)*1024;
- *     its bytes 16l..16l+15 (l = 0..63) are vals[16b + l%16][64s + 16(l/16)
- *     .. +15]; rows >= rows and steps s >= KS hold zeros.
- *   tmeta: RB*G blocks of 1024 bytes; block (b, g) at byte (b*G + g)*1024;
- *     its 32-bit word 4l + q is meta[16b + l%16][16(4g+q) + 4(l/16) .. +3]
- *     read as a little-endian word (the instruction's index operand for lane
- *     l); padding words are 0x44444444.
- * Returns the byte sizes of the two buffers (-1 for a bad argument). */
-int64_t ss_tiled_vals_bytes(int64_t rows, int64_t Kc);
-int64_t ss_tiled_meta_bytes(int64_t rows, int64_t Kc);
+ *     its bytes 16l..16l+15 (l = 0..63) are bytes 64s + 16(l/16) .. +15 of
+ *     row 16b + l%16 of vals (row-major, in bytes); rows >= rows and steps
+ *     s >= KS hold zeros.
+ *   tmeta, 8-bit values: RB*G blocks of 1024 bytes; block (b, g) at byte
+ *     (b*G + g)*1024; its 32-bit word 4l + q is meta[16b + l%16][16(4g+q) +
+ *     4(l/16) .. +3] as a little-endian word (the 16x16x128 index operand of
+ *     lane l); padding words 0x44444444.
+ *   tmeta, BF16 values: RB*G blocks of 512 bytes; block (b, g) at byte
+ *     (b*G + g)*512; its 16-bit word 4l + q is meta[16b + l%16][8(4g+q) +
+ *     2(l/16) .. +1] (the 16x16x64 index of lane l); padding 0x4444.
+ * Return the byte sizes of the two buffers for value type dt (I8, FP8E4M3 or
+ * BF16); -1 for a bad argument. */
+int64_t ss_tiled_vals_bytes(int64_t rows, int64_t Kc, ss_dtype dt);
+int64_t ss_tiled_meta_bytes(int64_t rows, int64_t Kc, ss_dtype dt);
 
 /* ss_pack_sparse -- compressed operand (row-major, as written by ss_prune24,
- * ss_slide_decompose or ss_prune24_act with 8-bit output) -> tiled operand.
- * A layout change only: the values and 2:4 positions are those of the input
- * (deep reading of arXiv 2610.28947, section 2.3: values plus 2-bit
- * positions). dt: I8 or FP8E4M3 (BF16 -> SS_ERR_UNSUPPORTED).
- * vals [rows][Kc/2] (ldv elements), meta [rows][Kc/8] (ldm bytes);
- * tvals / tmeta: ss_tiled_vals_bytes / ss_tiled_meta_bytes bytes, 16-byte
- * aligned, written completely. Kc % SS_KALIGN == 0. */
+ * ss_slide_decompose or ss_prune24_act) -> tiled operand. A layout change
+ * only (deep reading of arXiv 2610.28947, section 2.3: values plus 2-bit
+ * positions). dt: I8, FP8E4M3 or BF16. vals [rows][Kc/2] (ldv elements),
+ * meta [rows][Kc/8] (ldm bytes); tvals / tmeta: ss_tiled_vals_bytes /
+ * ss_tiled_meta_bytes bytes, 16-byte aligned, written completely.
+ * Kc % SS_KALIGN == 0. */
 ss_status ss_pack_sparse(int64_t rows, int64_t Kc, ss_dtype dt, const void* vals, int64_t ldv,
                          const uint8_t* meta, int64_t ldm, void* tvals, uint8_t* tmeta, void* stream);
 
 /* ss_spgemm_tiled -- ss_spgemm on a tiled sparse operand.
- * Same product, scales, sides and output rules as ss_spgemm (same sources),
- * for 8-bit operands: ab_dt I8 or FP8E4M3 (BF16 -> SS_ERR_UNSUPPORTED; use
- * ss_spgemm). The sparse operand is tvals/tmeta of ss_pack_sparse for its
- * rows (N for side SS_SPARSE_W, M for SS_SPARSE_X) and Kc; dense [rows][Kc]
- * with ldd elements. 0 < Kc, Kc % SS_KALIGN == 0; the dense operand must
- * span less than 4 GiB (else SS_ERR_UNSUPPORTED); Y as in ss_spgemm. Both
- * sx and sw are required unless y_dt is SS_I32. */
+ * Same product, scales, sides and output rules as ss_spgemm (same sources).
+ * The sparse operand is tvals/tmeta of ss_pack_sparse for its rows (N for
+ * side SS_SPARSE_W, M for SS_SPARSE_X), Kc and ab_dt; dense [rows][Kc] with
+ * ldd elements of ab_dt. 0 < Kc, Kc % SS_KALIGN == 0; the dense operand must
+ * span less than 4 GiB (else SS_ERR_UNSUPPORTED); Y as in ss_spgemm. I8 and
+ * FP8E4M3 products need both sx and sw unless y_dt is SS_I32; for BF16 a NULL
+ * scale skips that factor. Side SS_SPARSE_W with at most 64 tokens and too few
+ * 256-row tiles to fill the GPU runs a row-block kernel (same results; FP8 and
+ * BF16 sums in a different order). */
 ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt,
                           const void* tvals, const uint8_t* tmeta, const void* dense, int64_t ldd,
                           const float* sx, const float* sw, ss_dtype y_dt, void* Y, int64_t ldy,

@@ -14,8 +14,8 @@ Functions keep the names of the C entry points:
     quant_lift_act(X, n, q_dtype)           -> (Xq, sx)
     prune24_act(X, out_dtype)               -> (vals, meta, sx | None)
     spgemm(side, M, N, Kc, vals, meta, dense, sx, sw, y_dtype) -> Y [M, N]
-    tiled_bytes(rows, Kc)                   -> (tvals bytes, tmeta bytes)
-    pack_sparse(vals, meta)                 -> (tvals, tmeta)  8-bit tiled operand
+    tiled_bytes(rows, Kc, dtype)            -> (tvals bytes, tmeta bytes)
+    pack_sparse(vals, meta)                 -> (tvals, tmeta)  tiled operand
     spgemm_tiled(side, M, N, Kc, tvals, tmeta, dense, sx, sw, y_dtype) -> Y [M, N]
 """
 from __future__ import annotations
@@ -50,9 +50,9 @@ lib.ss_slide_decompose.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp,
 lib.ss_quant_lift_act.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp, _i64, _fp, _vp]
 lib.ss_prune24_act.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _fp, _vp]
 lib.ss_spgemm.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
-lib.ss_tiled_vals_bytes.argtypes = [_i64, _i64]
+lib.ss_tiled_vals_bytes.argtypes = [_i64, _i64, _int]
 lib.ss_tiled_vals_bytes.restype = _i64
-lib.ss_tiled_meta_bytes.argtypes = [_i64, _i64]
+lib.ss_tiled_meta_bytes.argtypes = [_i64, _i64, _int]
 lib.ss_tiled_meta_bytes.restype = _i64
 lib.ss_pack_sparse.argtypes = [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _vp, _vp]
 lib.ss_spgemm_tiled.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
@@ -180,16 +180,17 @@ def spgemm(side: int, M: int, N: int, Kc: int, vals: torch.Tensor, meta: torch.T
     return Y
 
 
-def tiled_bytes(rows: int, Kc: int):
-    return int(lib.ss_tiled_vals_bytes(rows, Kc)), int(lib.ss_tiled_meta_bytes(rows, Kc))
+def tiled_bytes(rows: int, Kc: int, dtype="i8"):
+    d = dtype_code(dtype)
+    return int(lib.ss_tiled_vals_bytes(rows, Kc, d)), int(lib.ss_tiled_meta_bytes(rows, Kc, d))
 
 
 def pack_sparse(vals: torch.Tensor, meta: torch.Tensor, out=None):
-    """Row-major compressed 8-bit operand -> tiled operand (flat uint8 tensors)."""
+    """Row-major compressed operand -> tiled operand (flat uint8 tensors)."""
     rows, half = vals.shape
     Kc = 2 * half
     if out is None:
-        nv, nm = tiled_bytes(rows, Kc)
+        nv, nm = tiled_bytes(rows, Kc, vals.dtype)
         if nv < 0:
             raise SSError(SS_ERR_SHAPE)
         tv = torch.empty(nv, dtype=torch.uint8, device=vals.device)

@@ -22,6 +22,11 @@
 //     are 0x44444444 (positions 0 and 1 of each group, with zero values).
 // A lane's instruction operands are therefore one contiguous 16-byte slice of
 // a block, and a whole wave's fragment is one contiguous 1 KB read.
+// bf16 values: the same bytes per step (a step is then 64 K positions, 32
+// compressed values per row) and 16-bit index words: a metadata block holds 4
+// steps in 512 bytes, lane l's 2-byte word for step 4g + q at byte 8l + 2q
+// (bytes 8(4g+q) + 2(l/16) of the row-major metadata); padding 0x4444. The
+// bf16 instruction (16x16x64) takes the word through its half-select.
 //
 // Product kernel: 256 (A rows) x 128 (B rows) per workgroup of 8 waves (4 x 2),
 // each wave 64 x 64 = 4 x 4 instructions per step. A ring of four 1-step LDS
@@ -58,25 +63,55 @@ constexpr int LDS = S * STAGE;                                 // 128 KB
 static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN, "load split");
 static_assert(S >= 3 && S <= 5, "wait counts below assume 3..5 stages");
 
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v16bf __attribute__((ext_vector_type(16)));
+
+// AB: 0 = int8, 1 = fp8 (16x16x128), 2 = bf16 (16x16x64; HALF selects the 16-bit index half)
 template <int AB> struct Mma;
 template <> struct Mma<0> {
   using Acc = v4i;
-  __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
+  template <int HALF> __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
     return __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, idx, 0, 0);
   }
 };
 template <> struct Mma<1> {
   using Acc = v4f;
-  __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
+  template <int HALF> __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
     return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, idx,
                                                           0, 0);
   }
 };
+template <> struct Mma<2> {
+  using Acc = v4f;
+  template <int HALF> __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+        __builtin_bit_cast(v8bf, a), __builtin_bit_cast(v16bf, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7)), c,
+        idx, 0, HALF);
+  }
+};
+
+// Per element size: index bytes per lane per step, and the block of one row block's 4-step index group.
+template <int AB> struct Meta {
+  static constexpr int ES = AB == 2 ? 2 : 1;  // value bytes
+  static constexpr int WB = 4 / ES;           // index bytes per lane per step
+  static constexpr int BLOCK = 256 * WB;      // bytes of one row block's 4-step group
+  using V = typename std::conditional<AB == 2, v2i, v4i>::type;
+  // the 32-bit word holding step q's index (bf16: two steps per word)
+  __device__ static int word(const V& m, int q) { return AB == 2 ? m[q >> 1] : m[q]; }
+};
+// one instruction with step q's index
+template <int AB, int Q, typename Acc>
+__device__ __forceinline__ Acc mma_step(v4i a, v4i b0, v4i b1, Acc c, const typename Meta<AB>::V& m) {
+  return Mma<AB>::template run<AB == 2 ? (Q & 1) : 0>(a, b0, b1, c, Meta<AB>::word(m, Q));
+}
 
 // B rows in LDS: 8 rows x 128 bytes per 1 KB block; chunk c of row r sits at chunk position c ^ (r % 8).
 __device__ __forceinline__ int swz(int c, int r16) { return c ^ (r16 & 7); }
 
-// One thread per (row block, 4-step group, lane); 4 row blocks per workgroup.
+// One thread per (row block, 4-step group, lane); 4 row blocks per workgroup. ES = value bytes; ldv in
+// bytes.
+template <int ES>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ vals, int64_t ldv,
                                                    const uint8_t* __restrict__ meta, int64_t ldm, int R, int KS,
                                                    int KS4, int nrb, uint8_t* __restrict__ tv, uint8_t* __restrict__ tm) {
@@ -89,14 +124,19 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ v
   for (int q = 0; q < 4; ++q) {
     const int s = 4 * g + q;
     uint4 v = make_uint4(0, 0, 0, 0);
-    w[q] = 0x44444444u;
+    w[q] = ES == 1 ? 0x44444444u : 0x4444u;
     if (live && s < KS) {
       v = *reinterpret_cast<const uint4*>(vals + row * ldv + 64 * s + 16 * c);
-      w[q] = *reinterpret_cast<const uint32_t*>(meta + row * ldm + 16 * s + 4 * c);
+      if constexpr (ES == 1) w[q] = *reinterpret_cast<const uint32_t*>(meta + row * ldm + 16 * s + 4 * c);
+      else w[q] = *reinterpret_cast<const uint16_t*>(meta + row * ldm + 8 * s + 2 * c);
     }
     *reinterpret_cast<uint4*>(tv + ((int64_t)rb * 4 * KS4 + s) * 1024 + 16 * l) = v;
   }
-  *reinterpret_cast<uint4*>(tm + ((int64_t)rb * KS4 + g) * 1024 + 16 * l) = make_uint4(w[0], w[1], w[2], w[3]);
+  if constexpr (ES == 1)
+    *reinterpret_cast<uint4*>(tm + ((int64_t)rb * KS4 + g) * 1024 + 16 * l) = make_uint4(w[0], w[1], w[2], w[3]);
+  else
+    *reinterpret_cast<uint2*>(tm + ((int64_t)rb * KS4 + g) * 512 + 8 * l) =
+        make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
 }
 
 template <int AB, int YT, bool SIDE_X>
@@ -106,6 +146,8 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
                                                             const float* __restrict__ sw, void* __restrict__ Y, int ldy,
                                                             int tiles_r, int tiles_c) {
   using Acc = typename Mma<AB>::Acc;
+  using MT = Meta<AB>;
+  using MV = typename MT::V;
   extern __shared__ __align__(16) uint8_t smem[];
   // the wave index is uniform: keep it (and the addresses built from it) in scalar registers
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -136,7 +178,8 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
     offb[q] = (uint32_t)min(c0 + b, C - 1) * (uint32_t)ldb + swz(lane & 7, b & 15) * 16;
   }
 #pragma unroll
-  for (int t = 0; t < TI; ++t) pmt[t] = tm + (int64_t)min(r0 / 16 + wm * TI + t, nrb - 1) * KS4 * 1024 + lane * 16;
+  for (int t = 0; t < TI; ++t)
+    pmt[t] = tm + (int64_t)min(r0 / 16 + wm * TI + t, nrb - 1) * KS4 * MT::BLOCK + lane * (4 * MT::WB);
 
   // Step k goes to slot k % S. Steps past the end re-read the last step (in
   // bounds, never consumed) so that every step issues the same loads.
@@ -152,10 +195,10 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
       __builtin_amdgcn_global_load_lds((const void*)(bd + offb[q] + (uint32_t)kb * 128),
                                        (SS_LDS void*)(base + A_BYTES + (wave + q * NW) * 1024), 16, 0, 0);
   };
-  v4i mcur[TI], mnxt[TI];
-  auto load_meta = [&](v4i* m, int g) {
+  MV mcur[TI], mnxt[TI];
+  auto load_meta = [&](MV* m, int g) {
 #pragma unroll
-    for (int t = 0; t < TI; ++t) m[t] = *reinterpret_cast<const v4i*>(pmt[t] + (int64_t)g * 1024);
+    for (int t = 0; t < TI; ++t) m[t] = *reinterpret_cast<const MV*>(pmt[t] + (int64_t)g * MT::BLOCK);
   };
 
   Acc acc[TI][TJ];
@@ -179,12 +222,14 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
       f.b[u][1] = *reinterpret_cast<const v4i*>(bb + swz(4 + jj, r16) * 16);
     }
   };
-  auto mma = [&](const Frag& f, int q) {
+  auto mma = [&](const Frag& f, auto qc) {
+    constexpr int Q = decltype(qc)::value;
 #pragma unroll
     for (int u = 0; u < TJ; ++u)
 #pragma unroll
-      for (int t = 0; t < TI; ++t) acc[t][u] = Mma<AB>::run(f.a[t], f.b[u][0], f.b[u][1], acc[t][u], mcur[t][q]);
+      for (int t = 0; t < TI; ++t) acc[t][u] = mma_step<AB, Q>(f.a[t], f.b[u][0], f.b[u][1], acc[t][u], mcur[t]);
   };
+
   // Loads complete in issue order, so "stage k+1 has landed" is a wait until at
   // most N of this wave's loads are outstanding, N = the loads issued after
   // stage k+1: the S-3 later stages (LPW each) plus the index groups issued
@@ -213,7 +258,7 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
     if (Q == 0 && !LAST) load_meta(mnxt, j / 4 + 1);
     __builtin_amdgcn_sched_barrier(0);
     read(nxt, j + 1);
-    mma(cur, Q);
+    mma(cur, qc);
 #pragma unroll
     for (int p = 0; p < NM; ++p) {
       if (p < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
@@ -253,7 +298,7 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
     step(j, Q0{}, Last{}, f0, f1);
     step(j + 1, Q1{}, Last{}, f1, f0);
     step(j + 2, Q2{}, Last{}, f0, f1);
-    mma(f1, 3);
+    mma(f1, std::integral_constant<int, 3>{});
   }
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // no load may outlive the workgroup
 
@@ -326,6 +371,8 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(int R, int C, int KS
                                                             const float* __restrict__ sw, void* __restrict__ Y,
                                                             int ldy) {
   using Acc = typename tiled::Mma<AB>::Acc;
+  using MT = tiled::Meta<AB>;
+  using MV = typename MT::V;
   __shared__ Acc red[NW][NCT][64];
   const int rb = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -337,11 +384,12 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(int R, int C, int KS
   for (int c = 0; c < NCT; ++c) acc[c] = Acc{0, 0, 0, 0};
   if (g0 < g1) {
     const uint8_t* pa = tv + (int64_t)rb * KSP * 1024 + lane * 16;
-    const uint8_t* pm = tm + (int64_t)rb * KS4 * 1024 + lane * 16;
+    const uint8_t* pm = tm + (int64_t)rb * KS4 * MT::BLOCK + lane * (4 * MT::WB);
     const uint8_t* pb[NCT];
 #pragma unroll
     for (int c = 0; c < NCT; ++c) pb[c] = bd + (int64_t)min(c * 16 + r16, C - 1) * ldb + 16 * jj;
-    tiled::v4i A[4], B[4][NCT][2], mcur, mnxt;
+    tiled::v4i A[4], B[4][NCT][2];
+    MV mcur, mnxt;
     // padded steps (>= KS) hold zero values; their dense slices re-read step KS-1
     auto load_step = [&](int slot, int k) {
       const int kb = min(k, KS - 1);
@@ -354,18 +402,22 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(int R, int C, int KS
     };
 #pragma unroll
     for (int q = 0; q < 4; ++q) load_step(q, 4 * g0 + q);
-    mcur = *reinterpret_cast<const tiled::v4i*>(pm + (int64_t)g0 * 1024);
-    mnxt = *reinterpret_cast<const tiled::v4i*>(pm + (int64_t)min(g0 + 1, KS4 - 1) * 1024);
+    mcur = *reinterpret_cast<const MV*>(pm + (int64_t)g0 * MT::BLOCK);
+    mnxt = *reinterpret_cast<const MV*>(pm + (int64_t)min(g0 + 1, KS4 - 1) * MT::BLOCK);
     for (int g = g0; g < g1; ++g) {
       const int kn = min(4 * (g + 1), KSP - 4);  // next group (re-read past the end, never used)
+      auto one = [&](auto qc) {
+        constexpr int Q = decltype(qc)::value;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) acc[c] = tiled::Mma<AB>::run(A[q], B[q][c][0], B[q][c][1], acc[c], mcur[q]);
-        load_step(q, kn + q);
-      }
+        for (int c = 0; c < NCT; ++c) acc[c] = tiled::mma_step<AB, Q>(A[Q], B[Q][c][0], B[Q][c][1], acc[c], mcur);
+        load_step(Q, kn + Q);
+      };
+      one(std::integral_constant<int, 0>{});
+      one(std::integral_constant<int, 1>{});
+      one(std::integral_constant<int, 2>{});
+      one(std::integral_constant<int, 3>{});
       mcur = mnxt;
-      mnxt = *reinterpret_cast<const tiled::v4i*>(pm + (int64_t)min(g + 2, KS4 - 1) * 1024);
+      mnxt = *reinterpret_cast<const MV*>(pm + (int64_t)min(g + 2, KS4 - 1) * MT::BLOCK);
     }
   }
 #pragma unroll
@@ -414,21 +466,25 @@ hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, co
 
 }  // namespace decode
 
-int64_t tiled_vals_bytes(int64_t rows, int64_t Kc) {
-  const int64_t ks4 = (Kc / 128 + 3) / 4;
+int64_t tiled_vals_bytes(int64_t rows, int64_t Kc, int es) {
+  const int64_t ks4 = (Kc * es / 128 + 3) / 4;
   return (rows + 15) / 16 * ks4 * 4 * 1024;
 }
 
-int64_t tiled_meta_bytes(int64_t rows, int64_t Kc) {
-  const int64_t ks4 = (Kc / 128 + 3) / 4;
-  return (rows + 15) / 16 * ks4 * 1024;
+int64_t tiled_meta_bytes(int64_t rows, int64_t Kc, int es) {
+  const int64_t ks4 = (Kc * es / 128 + 3) / 4;
+  return (rows + 15) / 16 * ks4 * 256 * (4 / es);
 }
 
-hipError_t launch_pack_tiled(const uint8_t* vals, int64_t ldv, const uint8_t* meta, int64_t ldm, int64_t rows,
-                             int64_t Kc, uint8_t* tv, uint8_t* tm, hipStream_t st) {
-  const int KS = (int)(Kc / 128), KS4 = (KS + 3) / 4, nrb = (int)((rows + 15) / 16);
-  hipLaunchKernelGGL(tiled::pack_kernel, dim3(KS4, (nrb + 3) / 4), dim3(256), 0, st, vals, ldv, meta, ldm, (int)rows, KS,
-                     KS4, nrb, tv, tm);
+hipError_t launch_pack_tiled(int es, const uint8_t* vals, int64_t ldv_bytes, const uint8_t* meta, int64_t ldm,
+                             int64_t rows, int64_t Kc, uint8_t* tv, uint8_t* tm, hipStream_t st) {
+  const int KS = (int)(Kc * es / 128), KS4 = (KS + 3) / 4, nrb = (int)((rows + 15) / 16);
+  if (es == 1)
+    hipLaunchKernelGGL(tiled::pack_kernel<1>, dim3(KS4, (nrb + 3) / 4), dim3(256), 0, st, vals, ldv_bytes, meta, ldm,
+                       (int)rows, KS, KS4, nrb, tv, tm);
+  else
+    hipLaunchKernelGGL(tiled::pack_kernel<2>, dim3(KS4, (nrb + 3) / 4), dim3(256), 0, st, vals, ldv_bytes, meta, ldm,
+                       (int)rows, KS, KS4, nrb, tv, tm);
   return hipGetLastError();
 }
 
@@ -436,7 +492,7 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
                                const uint8_t* tm, const void* bd, int64_t ldb_bytes, const float* sx, const float* sw,
                                void* Y, int64_t ldy, hipStream_t st) {
   const uint8_t* b = static_cast<const uint8_t*>(bd);
-  const int r = (int)R, c = (int)C, ks = (int)(Kc / 128), lb = (int)ldb_bytes, ly = (int)ldy;
+  const int r = (int)R, c = (int)C, ks = (int)(Kc * (ab == 2 ? 2 : 1) / 128), lb = (int)ldb_bytes, ly = (int)ldy;
   // few tokens and too few 256-row tiles to fill the chip: the row-block decode kernel
   const int64_t tiles = ((R + tiled::BM - 1) / tiled::BM) * ((C + tiled::BN - 1) / tiled::BN);
   const bool dec = !side_x && C <= 64 && (C <= 8 || tiles < 128);
@@ -449,8 +505,12 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
     if (yt == 1) SS_TL(0, 1);
     SS_TL(0, 2);
   }
-  if (yt == 0) SS_TL(1, 0);
-  SS_TL(1, 1);
+  if (ab == 1) {
+    if (yt == 0) SS_TL(1, 0);
+    SS_TL(1, 1);
+  }
+  if (yt == 0) SS_TL(2, 0);
+  SS_TL(2, 1);
 #undef SS_TL
 }
 

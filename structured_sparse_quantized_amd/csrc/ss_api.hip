@@ -194,32 +194,30 @@ ss_status ss_spgemm(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_
                     "ss_spgemm launch");
 }
 
-int64_t ss_tiled_vals_bytes(int64_t rows, int64_t Kc) {
-  if (rows < 0 || Kc < 0 || Kc % SS_KALIGN != 0) return -1;
-  return ss::tiled_vals_bytes(rows, Kc);
+int64_t ss_tiled_vals_bytes(int64_t rows, int64_t Kc, ss_dtype dt) {
+  if (rows < 0 || Kc < 0 || Kc % SS_KALIGN != 0 || (dt != SS_I8 && dt != SS_FP8E4M3 && dt != SS_BF16)) return -1;
+  return ss::tiled_vals_bytes(rows, Kc, esize(dt));
 }
 
-int64_t ss_tiled_meta_bytes(int64_t rows, int64_t Kc) {
-  if (rows < 0 || Kc < 0 || Kc % SS_KALIGN != 0) return -1;
-  return ss::tiled_meta_bytes(rows, Kc);
+int64_t ss_tiled_meta_bytes(int64_t rows, int64_t Kc, ss_dtype dt) {
+  if (rows < 0 || Kc < 0 || Kc % SS_KALIGN != 0 || (dt != SS_I8 && dt != SS_FP8E4M3 && dt != SS_BF16)) return -1;
+  return ss::tiled_meta_bytes(rows, Kc, esize(dt));
 }
 
 ss_status ss_pack_sparse(int64_t rows, int64_t Kc, ss_dtype dt, const void* vals, int64_t ldv, const uint8_t* meta,
                          int64_t ldm, void* tvals, uint8_t* tmeta, void* stream) {
-  if (dt != SS_I8 && dt != SS_FP8E4M3) {
-    if (dt == SS_BF16) return fail(SS_ERR_UNSUPPORTED, "the tiled layout holds 8-bit values only");
-    return fail(SS_ERR_DTYPE, "values must be I8 or FP8E4M3");
-  }
+  if (dt != SS_I8 && dt != SS_FP8E4M3 && dt != SS_BF16) return fail(SS_ERR_DTYPE, "values must be I8, FP8E4M3 or BF16");
   if (rows < 0 || Kc < 0) return fail(SS_ERR_SHAPE, "negative size");
   if (Kc % SS_KALIGN != 0) return fail(SS_ERR_SHAPE, "Kc=%lld is not a multiple of %d", (long long)Kc, SS_KALIGN);
-  if (rows > 0x7FFFFFF0LL || Kc / 128 > 0x7FFFFFF0LL) return fail(SS_ERR_SHAPE, "too large");
+  if (rows > 0x7FFFFFF0LL || Kc / 64 > 0x7FFFFFF0LL) return fail(SS_ERR_SHAPE, "too large");
   if (rows == 0 || Kc == 0) return ok();
+  const int es = esize(dt);
   ss_status s;
-  if ((s = check_mat("vals", vals, rows, Kc / 2, ldv, 1)) != SS_OK) return s;
+  if ((s = check_mat("vals", vals, rows, Kc / 2, ldv, es)) != SS_OK) return s;
   if ((s = check_mat("meta", meta, rows, Kc / 8, ldm, 1)) != SS_OK) return s;
   if (!tvals || !tmeta) return fail(SS_ERR_NULL, "tiled outputs are NULL");
   if (!aligned16(tvals) || !aligned16(tmeta)) return fail(SS_ERR_ALIGN, "tiled outputs are not 16-byte aligned");
-  return hip_status(ss::launch_pack_tiled(static_cast<const uint8_t*>(vals), ldv, meta, ldm, rows, Kc,
+  return hip_status(ss::launch_pack_tiled(es, static_cast<const uint8_t*>(vals), ldv * es, meta, ldm, rows, Kc,
                                           static_cast<uint8_t*>(tvals), tmeta, (hipStream_t)stream),
                     "ss_pack_sparse launch");
 }
@@ -228,10 +226,8 @@ ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dty
                           const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
                           ss_dtype y_dt, void* Y, int64_t ldy, void* stream) {
   if (side != SS_SPARSE_W && side != SS_SPARSE_X) return fail(SS_ERR_SHAPE, "bad side");
-  if (ab_dt != SS_I8 && ab_dt != SS_FP8E4M3) {
-    if (ab_dt == SS_BF16) return fail(SS_ERR_UNSUPPORTED, "the tiled product takes 8-bit operands only");
-    return fail(SS_ERR_DTYPE, "operands must be I8 or FP8E4M3");
-  }
+  if (ab_dt != SS_I8 && ab_dt != SS_FP8E4M3 && ab_dt != SS_BF16)
+    return fail(SS_ERR_DTYPE, "operands must be I8, FP8E4M3 or BF16");
   if (y_dt != SS_BF16 && y_dt != SS_F32 && y_dt != SS_I32) return fail(SS_ERR_DTYPE, "output must be BF16, F32 or I32");
   if (y_dt == SS_I32 && ab_dt != SS_I8) return fail(SS_ERR_DTYPE, "I32 output needs I8 operands");
   if (M < 0 || N < 0 || Kc < 0) return fail(SS_ERR_SHAPE, "negative size");
@@ -240,22 +236,23 @@ ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dty
   if (Kc == 0) return fail(SS_ERR_SHAPE, "Kc must be positive");
   const bool sx_side = (side == SS_SPARSE_X);
   const int64_t R = sx_side ? M : N, C = sx_side ? N : M;
-  if (R > 0x7FFFFFF0LL || C > 0x7FFFFFF0LL || ldy > 0x7FFFFFFFLL || Kc / 128 > 0x7FFFFFF0LL)
+  if (R > 0x7FFFFFF0LL || C > 0x7FFFFFF0LL || ldy > 0x7FFFFFFFLL || Kc / 64 > 0x7FFFFFF0LL)
     return fail(SS_ERR_SHAPE, "too large");
+  const int es = esize(ab_dt);
   ss_status s;
-  if ((s = check_mat("dense", dense, C, Kc, ldd, 1)) != SS_OK) return s;
+  if ((s = check_mat("dense", dense, C, Kc, ldd, es)) != SS_OK) return s;
   // the kernel addresses the dense operand with 32-bit byte offsets
-  if ((uint64_t)(C - 1) * (uint64_t)ldd + (uint64_t)Kc > 0xFFFFFFFFull)
+  if ((uint64_t)(C - 1) * (uint64_t)ldd * es + (uint64_t)Kc * es > 0xFFFFFFFFull)
     return fail(SS_ERR_UNSUPPORTED, "dense operand spans more than 4 GiB");
   if ((s = check_mat("Y", Y, 1, N, ldy, esize(y_dt))) != SS_OK) return s;
   if (!tvals || !tmeta) return fail(SS_ERR_NULL, "tiled operand is NULL");
   if (!aligned16(tvals) || !aligned16(tmeta)) return fail(SS_ERR_ALIGN, "tiled operand is not 16-byte aligned");
-  if (y_dt != SS_I32 && (!sx || !sw)) return fail(SS_ERR_NULL, "INT8/FP8 products need both scales");
-  const int ab = ab_dt == SS_I8 ? 0 : 1;
+  if (ab_dt != SS_BF16 && y_dt != SS_I32 && (!sx || !sw)) return fail(SS_ERR_NULL, "INT8/FP8 products need both scales");
+  const int ab = ab_dt == SS_I8 ? 0 : ab_dt == SS_FP8E4M3 ? 1 : 2;
   const int yt = y_dt == SS_BF16 ? 0 : y_dt == SS_F32 ? 1 : 2;
   return hip_status(ss::launch_spgemm_tiled(sx_side, ab, yt, R, C, Kc, static_cast<const uint8_t*>(tvals), tmeta, dense,
-                                            ldd, y_dt == SS_I32 ? nullptr : sx, y_dt == SS_I32 ? nullptr : sw, Y, ldy,
-                                            (hipStream_t)stream),
+                                            ldd * es, y_dt == SS_I32 ? nullptr : sx, y_dt == SS_I32 ? nullptr : sw, Y,
+                                            ldy, (hipStream_t)stream),
                     "ss_spgemm_tiled launch");
 }
 

@@ -20,12 +20,12 @@ hipError_t launch_spgemm(bool side_x, int ab, int yt, int64_t R, int64_t C, int6
                          int64_t lda_bytes, const uint8_t* am, int64_t ldm, const void* bd, int64_t ldb_bytes,
                          const float* sx, const float* sw, void* Y, int64_t ldy, hipStream_t st);
 
-// Tiled sparse operand (8-bit values) and the product that reads it.
-int64_t tiled_vals_bytes(int64_t rows, int64_t Kc);
-int64_t tiled_meta_bytes(int64_t rows, int64_t Kc);
-hipError_t launch_pack_tiled(const uint8_t* vals, int64_t ldv, const uint8_t* meta, int64_t ldm, int64_t rows,
-                             int64_t Kc, uint8_t* tv, uint8_t* tm, hipStream_t st);
-// ab: 0 = int8, 1 = fp8; yt: 0 = bf16, 1 = f32, 2 = i32
+// Tiled sparse operand and the product that reads it. es = value bytes (1: int8/fp8, 2: bf16).
+int64_t tiled_vals_bytes(int64_t rows, int64_t Kc, int es);
+int64_t tiled_meta_bytes(int64_t rows, int64_t Kc, int es);
+hipError_t launch_pack_tiled(int es, const uint8_t* vals, int64_t ldv_bytes, const uint8_t* meta, int64_t ldm,
+                             int64_t rows, int64_t Kc, uint8_t* tv, uint8_t* tm, hipStream_t st);
+// ab: 0 = int8, 1 = fp8, 2 = bf16; yt: 0 = bf16, 1 = f32, 2 = i32
 hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C, int64_t Kc, const uint8_t* tv,
                                const uint8_t* tm, const void* bd, int64_t ldb_bytes, const float* sx, const float* sw,
                                void* Y, int64_t ldy, hipStream_t st);

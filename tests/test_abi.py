@@ -84,28 +84,31 @@ def test_empty_problems_are_ok_without_launch():
     assert L.ss_last_error() == b""
 
 
-def _tiled_sizes(rows, Kc):
+def _tiled_sizes(rows, Kc, es=1):
     # the sizes the tiled layout description in include/ss.h fixes
-    ks4 = -(-(Kc // 128) // 4)
+    ks4 = -(-(Kc * es // 128) // 4)
     rb = -(-rows // 16)
-    return rb * ks4 * 4 * 1024, rb * ks4 * 1024
+    return rb * ks4 * 4 * 1024, rb * ks4 * 256 * (4 // es)
 
 
 def test_tiled_sizes():
     import structured_sparse_quantized_amd as ss
     for rows in (1, 15, 16, 17, 300, 4096, 28672):
         for Kc in (256, 512, 768, 1024, 6144, 61440):
-            assert ss.tiled_bytes(rows, Kc) == _tiled_sizes(rows, Kc)
+            assert ss.tiled_bytes(rows, Kc, "i8") == _tiled_sizes(rows, Kc)
+            assert ss.tiled_bytes(rows, Kc, "fp8") == _tiled_sizes(rows, Kc)
+            assert ss.tiled_bytes(rows, Kc, "bf16") == _tiled_sizes(rows, Kc, 2)
     assert ss.tiled_bytes(0, 256) == (0, 0)
-    assert ss.lib.ss_tiled_vals_bytes(4, 100) == -1 and ss.lib.ss_tiled_meta_bytes(-1, 256) == -1
+    assert ss.lib.ss_tiled_vals_bytes(4, 100, ss.SS_I8) == -1 and ss.lib.ss_tiled_meta_bytes(-1, 256, ss.SS_I8) == -1
+    assert ss.lib.ss_tiled_vals_bytes(4, 256, ss.SS_F32) == -1
 
 
 def test_tiled_validation_statuses():
     import structured_sparse_quantized_amd as ss
     L = ss.lib
-    # pack: BF16 values are valid but not implemented in the tiled layout; other types are errors
-    assert L.ss_pack_sparse(4, 256, ss.SS_BF16, FAKE, 128, FAKE, 32, FAKE, FAKE, None) == ss.SS_ERR_UNSUPPORTED
+    # pack: I8 / FP8 / BF16 values; other types are errors
     assert L.ss_pack_sparse(4, 256, ss.SS_F32, FAKE, 128, FAKE, 32, FAKE, FAKE, None) == ss.SS_ERR_DTYPE
+    assert L.ss_pack_sparse(4, 256, ss.SS_BF16, FAKE, 100, FAKE, 32, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
     assert L.ss_pack_sparse(4, 100, ss.SS_I8, FAKE, 128, FAKE, 32, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
     assert L.ss_pack_sparse(4, 256, ss.SS_I8, FAKE, 100, FAKE, 32, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
     assert L.ss_pack_sparse(4, 256, ss.SS_I8, FAKE, 128, FAKE, 32, None, FAKE, None) == ss.SS_ERR_NULL
@@ -116,8 +119,8 @@ def test_tiled_validation_statuses():
     def g(side=0, M=4, N=4, Kc=256, ab=ss.SS_I8, tv=FAKE, tm=FAKE, d=FAKE, ldd=256, sx=FAKE, sw=FAKE,
           y=ss.SS_BF16, Y=FAKE, ldy=8):
         return L.ss_spgemm_tiled(side, M, N, Kc, ab, tv, tm, d, ldd, sx, sw, y, Y, ldy, None)
-    assert g(ab=ss.SS_BF16) == ss.SS_ERR_UNSUPPORTED
     assert g(ab=ss.SS_F32) == ss.SS_ERR_DTYPE
+    assert g(ab=ss.SS_BF16, y=ss.SS_I32) == ss.SS_ERR_DTYPE
     assert g(Kc=100) == ss.SS_ERR_SHAPE
     assert g(Kc=0) == ss.SS_ERR_SHAPE
     assert g(side=3) == ss.SS_ERR_SHAPE

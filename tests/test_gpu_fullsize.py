@@ -114,10 +114,9 @@ def test_sparse_activation_full_size(ss, out):
     r = _rows(M, 24)
     exp = oracle.spgemm("X", oxs[0][r], oxs[1][r], ow, K, out, None if oxs[2] is None else oxs[2][r], osw, "bf16")
     assert rel_fro(bf16_to_f64(Y[r]), bf16_to_f64(exp)) <= 1e-2
-    if out == "fp8":
-        tv, tm = ss.pack_sparse(xs[0], xs[1])
-        Yt = host(ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, K, tv, tm, wd, xs[2], sw, "bf16"))
-        assert rel_fro(bf16_to_f64(Yt[r]), bf16_to_f64(exp)) <= 1e-2
+    tv, tm = ss.pack_sparse(xs[0], xs[1])
+    Yt = host(ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, K, tv, tm, wd, xs[2], sw, "bf16"))
+    assert rel_fro(bf16_to_f64(Yt[r]), bf16_to_f64(exp)) <= 1e-2
 
 
 @pytest.mark.parametrize("n", [3, 5])

@@ -27,23 +27,24 @@ def ss():
 PACK_SHAPES = [(1, 256), (15, 256), (16, 512), (17, 768), (130, 1024), (300, 6144), (33, 1280)]
 
 
-@pytest.mark.parametrize("q", ["i8", "fp8"])
+@pytest.mark.parametrize("q", ["i8", "fp8", "bf16"])
 @pytest.mark.parametrize("shape", PACK_SHAPES)
 def test_pack_sparse(ss, q, shape):
     rows, Kc = shape
+    es = 2 if q == "bf16" else 1
     rng = np.random.default_rng(rows + Kc)
-    vals = rng.integers(0, 256, (rows, Kc // 2), dtype=np.uint8)
+    vals = rng.integers(0, 256, (rows, Kc // 2 * es), dtype=np.uint8)
     meta = rng.integers(0, 256, (rows, Kc // 8), dtype=np.uint8)
     vd = dev_u8(vals).view(torch_dtype(q))
     tv, tm = ss.pack_sparse(vd, dev_u8(meta))
-    ev, em = tile_ref(vals, meta)
+    ev, em = tile_ref(vals, meta, es)
     assert np.array_equal(host(tv), ev)
     assert np.array_equal(host(tm), em)
 
 
 def torch_dtype(q):
     import torch
-    return torch.int8 if q == "i8" else torch.float8_e4m3fn
+    return {"i8": torch.int8, "fp8": torch.float8_e4m3fn, "bf16": torch.bfloat16}[q]
 
 
 def test_pack_sparse_padded_leading_dims(ss):
@@ -63,20 +64,37 @@ GEMM_SHAPES = [(1, 1, 8), (64, 256, 512), (200, 130, 768), (129, 257, 1024), (17
 
 
 def _gemm_case(seed, M, N, K, n, ab, side):
-    """Operands built by the oracle (no HIP step)."""
+    """Operands built by the oracle (no HIP step). bf16: unscaled bf16 operands (scales None)."""
     X, W, _ = synth.workload(seed, M, N, K, x_kind="bf16")
     if side == "W":
         vals, meta, sw = oracle.prune24(W, ab) if n == 2 else oracle.slide_decompose(W, n, ab)
-        dense, sx = oracle.quant_lift_act(X, n, ab)
+        if ab == "bf16":
+            Kc = oracle.lifted_k_alloc(K, n)
+            lifted = oracle.lift(X, n)
+            dense = np.zeros((M, Kc), np.uint16)
+            dense[:, : lifted.shape[1]] = lifted
+            sx, sw = None, None
+        else:
+            dense, sx = oracle.quant_lift_act(X, n, ab)
     else:
         vals, meta, sx = oracle.prune24_act(X, ab)
-        dense, sw = oracle.quant_lift_act(W, 2, ab)
+        if ab == "bf16":
+            Kc = oracle.lifted_k_alloc(K, 2)
+            dense = np.zeros((N, Kc), np.uint16)
+            dense[:, :K] = synth.f32_to_bf16_bits(W)
+            sw = None
+        else:
+            dense, sw = oracle.quant_lift_act(W, 2, ab)
     Kc = meta.shape[1] * 8
     return vals, meta, dense, sx, sw, Kc
 
 
+def _scales(sx, sw):
+    return (None if sx is None else dev_f32(sx)), (None if sw is None else dev_f32(sw))
+
+
 @pytest.mark.parametrize("side", ["W", "X"])
-@pytest.mark.parametrize("ab", ["i8", "fp8"])
+@pytest.mark.parametrize("ab", ["i8", "fp8", "bf16"])
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
 def test_spgemm_tiled_against_oracle_operands(ss, side, ab, shape):
     M, N, K = shape
@@ -84,7 +102,8 @@ def test_spgemm_tiled_against_oracle_operands(ss, side, ab, shape):
     vals, meta, dense, sx, sw, Kc = _gemm_case(77 + M + N, M, N, K, n, ab, side)
     s = ss.SS_SPARSE_W if side == "W" else ss.SS_SPARSE_X
     tv, tm = ss.pack_sparse(dev_codes(vals, ab), dev_u8(meta))
-    d, dsx, dsw = dev_codes(dense, ab), dev_f32(sx), dev_f32(sw)
+    d = dev_codes(dense, ab)
+    dsx, dsw = _scales(sx, sw)
     for y in (["i32", "f32", "bf16"] if ab == "i8" else ["f32", "bf16"]):
         Y = host(ss.spgemm_tiled(s, M, N, Kc, tv, tm, d, dsx, dsw, y_dtype=y))
         exp = oracle.spgemm(side, vals, meta, dense, Kc, ab, sx, sw, y)
@@ -171,14 +190,15 @@ DECODE_SHAPES = [(1, 1000, 512), (5, 1000, 600), (8, 260, 2048), (9, 300, 1000),
                  (32, 700, 3000), (33, 520, 768), (64, 1000, 6000), (64, 4608, 3584)]
 
 
-@pytest.mark.parametrize("ab", ["i8", "fp8"])
+@pytest.mark.parametrize("ab", ["i8", "fp8", "bf16"])
 @pytest.mark.parametrize("shape", DECODE_SHAPES)
 def test_spgemm_tiled_decode_tokens(ss, ab, shape):
     M, N, K = shape
     n = 3 if K % 6 == 0 else 2
     vals, meta, dense, sx, sw, Kc = _gemm_case(101 + M + N, M, N, K, n, ab, "W")
     tv, tm = ss.pack_sparse(dev_codes(vals, ab), dev_u8(meta))
-    d, dsx, dsw = dev_codes(dense, ab), dev_f32(sx), dev_f32(sw)
+    d = dev_codes(dense, ab)
+    dsx, dsw = _scales(sx, sw)
     for y in (["i32", "bf16"] if ab == "i8" else ["f32", "bf16"]):
         Y = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, d, dsx, dsw, y_dtype=y))
         exp = oracle.spgemm("W", vals, meta, dense, Kc, ab, sx, sw, y)
@@ -188,3 +208,16 @@ def test_spgemm_tiled_decode_tokens(ss, ab, shape):
             assert rel_fro(bf16_to_f64(Y), bf16_to_f64(exp)) <= TOL
         else:
             assert rel_fro(Y, exp) <= TOL
+
+
+def test_activation_sparse_path_tiled_bf16(ss):
+    """bf16 activations pruned 2:4 online, times bf16 weights, on the tiled product."""
+    M, N, K = 300, 200, 512
+    X, W, _ = synth.workload(73, M, N, K, x_kind="bf16")
+    xv, xm, _ = ss.prune24_act(dev_bf16(X), "bf16")
+    tv, tm = ss.pack_sparse(xv, xm)
+    wb = synth.f32_to_bf16_bits(W)
+    Y = host(ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, K, tv, tm, dev_bf16(wb), None, None, "f32"))
+    ov, om, _ = oracle.prune24_act(X, "bf16")
+    exp = oracle.spgemm("X", ov, om, wb, K, "bf16", None, None, "f32")
+    assert rel_fro(Y, exp) <= TOL

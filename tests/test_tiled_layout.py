@@ -22,3 +22,18 @@ def test_tile_ref_by_hand():
     assert tm[(0 * 2 + gg) * 1024 + 16 * l + 4 * q + byte] == meta[l % 16, 16 * (4 * gg + q) + 4 * (l // 16) + byte]
     # step 6 (padding) of row 0
     assert tm[(0 * 2 + 1) * 1024 + 16 * 0 + 4 * 2] == 0x44
+
+
+def test_tile_ref_bf16_by_hand():
+    """BF16 values: same value bytes per step (64 K positions), 2-byte index words, 512-byte index blocks."""
+    rows, Kc = 18, 512  # 2 row blocks, 8 steps of 64 K -> 2 groups
+    vals = (np.arange(rows * Kc, dtype=np.int64).reshape(rows, Kc) % 251).astype(np.uint8)  # Kc/2 bf16 = Kc bytes
+    meta = (np.arange(rows * Kc // 8, dtype=np.int64).reshape(rows, Kc // 8) * 5 % 256).astype(np.uint8)
+    tv, tm = tile_ref(vals, meta, es=2)
+    assert tv.size == 2 * 8 * 1024 and tm.size == 2 * 2 * 512
+    b, s, l, i = 0, 6, 45, 3  # row 13, chunk 2
+    assert tv[(b * 8 + s) * 1024 + 16 * l + i] == vals[16 * b + l % 16, 64 * s + 16 * (l // 16) + i]
+    gg, q, l, byte = 1, 3, 17, 1  # row 1, chunk 1, step 7
+    assert tm[(0 * 2 + gg) * 512 + 8 * l + 2 * q + byte] == meta[l % 16, 8 * (4 * gg + q) + 2 * (l // 16) + byte]
+    # row 17 is real, row 18 is padding
+    assert tm[(1 * 2 + 0) * 512 + 8 * 1] == meta[17, 0] and tm[(1 * 2 + 0) * 512 + 8 * 2] == 0x44
