@@ -6,7 +6,7 @@ A step is one pass of every kernel on the path over one batch of the
 
   slide_decompose(W, 6:8) -> pack_sparse -> quant_lift_act(X, n=4) -> spgemm_tiled(sparse W')   6:8
   prune24(W)              -> pack_sparse -> quant_lift_act(X, n=2) -> spgemm_tiled(sparse W)    2:4
-  prune24_act(X) -> pack_sparse, quant_lift_act(W, n=2) -> spgemm_tiled(sparse X)             2:4 on X
+  prune24_act_tiled(X), quant_lift_act(W, n=2) -> spgemm_tiled(sparse X)                      2:4 on X
 
 The weight-side preparation (decompose or prune, then pack) runs offline in
 a deployment; it is timed here per step all the same.
@@ -82,12 +82,12 @@ def kernel_work(name, Kc68, Kc24):
         "quant_lift_68": 2 * M * K + M * Kc68 + 4 * M,
         "prune24_w": 4 * N * K + N * Kc24 // 2 + N * Kc24 // 8 + 4 * N,
         "quant_lift_24": 2 * M * K + M * Kc24 + 4 * M,
-        "prune24_act": 2 * M * K + M * Kc24 // 2 + M * Kc24 // 8 + 4 * M,
+        # online prune of X written in the tiled layout: X read once, tiled operand + scales written
+        "prune24_act_tiled": 2 * M * K + sum(tiled_bytes(M, Kc24)) + 4 * M,
         "quant_w": 4 * N * K + N * Kc24 + 4 * N,
         # layout change: read the row-major compressed operand, write the tiled one
         "pack_68": N * Kc68 // 2 + N * Kc68 // 8 + sum(tiled_bytes(N, Kc68)),
         "pack_24": N * Kc24 // 2 + N * Kc24 // 8 + sum(tiled_bytes(N, Kc24)),
-        "pack_x": M * Kc24 // 2 + M * Kc24 // 8 + sum(tiled_bytes(M, Kc24)),
     }
     # products: multiply-adds on the kept values only (K'/2 per row), x2 ops
     ops = {
@@ -137,12 +137,12 @@ def main():
             w24=(mk((N, Kc24 // 2), torch.int8), mk((N, Kc24 // 8), torch.uint8), mk(N, torch.float32)),
             x24=(mk((M, Kc24), torch.int8), mk(M, torch.float32)),
             y24=mk((M, N), torch.bfloat16),
-            xs=(mk((M, Kc24 // 2), torch.int8), mk((M, Kc24 // 8), torch.uint8), mk(M, torch.float32)),
+            xs=(mk(M, torch.float32),),
             wq=(mk((N, Kc24), torch.int8), mk(N, torch.float32)),
             yx=mk((M, N), torch.bfloat16),
         ))
     names = ["slide_decompose_68", "pack_68", "quant_lift_68", "spgemm_68", "prune24_w", "pack_24",
-             "quant_lift_24", "spgemm_24", "prune24_act", "pack_x", "quant_w", "spgemm_x"]
+             "quant_lift_24", "spgemm_24", "prune24_act_tiled", "quant_w", "spgemm_x"]
 
     def step(b, ev=None):
         calls = [
@@ -156,10 +156,9 @@ def main():
             lambda: ss.quant_lift_act(b["X"], 2, "i8", out=b["x24"]),
             lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc24, b["t24"][0], b["t24"][1], b["x24"][0], b["x24"][1],
                                     b["w24"][2], "bf16", out=b["y24"]),
-            lambda: ss.prune24_act(b["X"], "i8", out=b["xs"]),
-            lambda: ss.pack_sparse(b["xs"][0], b["xs"][1], out=b["tx"]),
+            lambda: ss.prune24_act_tiled(b["X"], "i8", out=(b["tx"][0], b["tx"][1], b["xs"][0])),
             lambda: ss.quant_lift_act(b["W"], 2, "i8", out=b["wq"]),
-            lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, Kc24, b["tx"][0], b["tx"][1], b["wq"][0], b["xs"][2],
+            lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, Kc24, b["tx"][0], b["tx"][1], b["wq"][0], b["xs"][0],
                                     b["wq"][1], "bf16", out=b["yx"]),
         ]
         for i, c in enumerate(calls):
@@ -216,7 +215,7 @@ def main():
     online68_s = (per_kernel_ms["quant_lift_68"] + per_kernel_ms["spgemm_68"]) * 1e-3
     online24_s = (per_kernel_ms["quant_lift_24"] + per_kernel_ms["spgemm_24"]) * 1e-3
     # sparse-activation layer: online prune + pack of X, then the product (W quantised offline)
-    onlinex_s = (per_kernel_ms["prune24_act"] + per_kernel_ms["pack_x"] + per_kernel_ms["spgemm_x"]) * 1e-3
+    onlinex_s = (per_kernel_ms["prune24_act_tiled"] + per_kernel_ms["spgemm_x"]) * 1e-3
 
     # dense INT8 comparator: our per-token quantiser + hipBLASLt int8 GEMM (torch._int_mm)
     dense = None
@@ -373,16 +372,13 @@ def suite(ss, torch, dev, reps=10):
     M, K, Nout = 8192, 4096, 4096
     X = randn((M, K), 1.0, torch.bfloat16)
     wq, swd = ss.quant_lift_act(randn((Nout, K), 0.02), 2, "fp8")
-    xv = torch.empty((M, K // 2), dtype=torch.float8_e4m3fn, device=dev)
-    xm = torch.empty((M, K // 8), dtype=torch.uint8, device=dev)
     sx = torch.empty(M, dtype=torch.float32, device=dev)
     nv, nm = ss.tiled_bytes(M, K)
     tv = torch.empty(nv, dtype=torch.uint8, device=dev)
     tm = torch.empty(nm, dtype=torch.uint8, device=dev)
     Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
     xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
-    t_pr = timed(lambda: ss.prune24_act(X, "fp8", out=(xv, xm, sx)))
-    t_pk = timed(lambda: ss.pack_sparse(xv, xm, out=(tv, tm)))
+    t_pr = timed(lambda: ss.prune24_act_tiled(X, "fp8", out=(tv, tm, sx)))
     t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, Nout, K, tv, tm, wq, sx, swd, "bf16", out=Y))
     t_q = timed(lambda: ss.quant_lift_act(X, 2, "fp8", out=(xq, sx)))
     try:
@@ -391,31 +387,28 @@ def suite(ss, torch, dev, reps=10):
     except Exception:
         t_dn = None
     res["sparse_activation_fp8"] = {
-        "M": M, "K": K, "N": Nout, "prune24_act_us": t_pr, "pack_us": t_pk, "sparse_gemm_us": t_sp,
+        "M": M, "K": K, "N": Nout, "prune24_act_tiled_us": t_pr, "sparse_gemm_us": t_sp,
         "sparse_TOPS_dense_equiv": 2.0 * M * Nout * K / t_sp / 1e6, "dense_quant_us": t_q,
         "dense_fp8_gemm_us": t_dn,
-        "speedup_vs_dense": None if t_dn is None else (t_q + t_dn) / (t_pr + t_pk + t_sp)}
-    del X, wq, swd, xv, xm, sx, tv, tm, Y, xq
+        "speedup_vs_dense": None if t_dn is None else (t_q + t_dn) / (t_pr + t_sp)}
+    del X, wq, swd, sx, tv, tm, Y, xq
     torch.cuda.empty_cache()
     # the same layer in bf16 (no quantisation): online prune + pack + product against dense bf16 (hipBLASLt)
     X = randn((M, K), 1.0, torch.bfloat16)
     Wb = randn((Nout, K), 0.02, torch.bfloat16)
-    xv = torch.empty((M, K // 2), dtype=torch.bfloat16, device=dev)
-    xm = torch.empty((M, K // 8), dtype=torch.uint8, device=dev)
     nv, nm = ss.tiled_bytes(M, K, "bf16")
     tv = torch.empty(nv, dtype=torch.uint8, device=dev)
     tm = torch.empty(nm, dtype=torch.uint8, device=dev)
     Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
-    t_pr = timed(lambda: ss.prune24_act(X, "bf16", out=(xv, xm, None)))
-    t_pk = timed(lambda: ss.pack_sparse(xv, xm, out=(tv, tm)))
+    t_pr = timed(lambda: ss.prune24_act_tiled(X, "bf16", out=(tv, tm, None)))
     t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, Nout, K, tv, tm, Wb, None, None, "bf16", out=Y))
     t_dn = timed(lambda: torch.matmul(X, Wb.t()))
     res["sparse_activation_bf16"] = {
-        "M": M, "K": K, "N": Nout, "prune24_act_us": t_pr, "pack_us": t_pk, "sparse_gemm_us": t_sp,
+        "M": M, "K": K, "N": Nout, "prune24_act_tiled_us": t_pr, "sparse_gemm_us": t_sp,
         "sparse_TFLOPS_dense_equiv": 2.0 * M * Nout * K / t_sp / 1e6,
         "sparse_frac_of_5030": 2.0 * M * Nout * K / t_sp / 1e6 / 5030.0, "dense_bf16_gemm_us": t_dn,
-        "speedup_vs_dense": t_dn / (t_pr + t_pk + t_sp)}
-    del X, Wb, xv, xm, tv, tm, Y
+        "speedup_vs_dense": t_dn / (t_pr + t_sp)}
+    del X, Wb, tv, tm, Y
     torch.cuda.empty_cache()
     # quant+lift on a large batch (launch latency amortised) and a plain device copy
     ql = {}
@@ -462,7 +455,7 @@ def cpu_baseline(X_np, W_np, Kc68, Kc24):
     oracle.spgemm("X", xs[0], xs[1], wq[0], Kc24, "i8", xs[2], wq[1], "bf16")
     t = time.perf_counter() - t0
     return {"value": M / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step (the 9 arithmetic calls; the 3 layout packs have no oracle counterpart, "
+            "sample": f"one full step (the 9 arithmetic calls; the 2 weight packs have no oracle counterpart, "
                       f"M={M} tokens) in {t:.2f} s; products in float64 BLAS "
                       f"({threads} threads), element-wise steps single-threaded NumPy; host CPUs visible: "
                       f"{len(os.sched_getaffinity(0))}"}

@@ -207,6 +207,16 @@ int64_t ss_tiled_meta_bytes(int64_t rows, int64_t Kc, ss_dtype dt);
 ss_status ss_pack_sparse(int64_t rows, int64_t Kc, ss_dtype dt, const void* vals, int64_t ldv,
                          const uint8_t* meta, int64_t ldm, void* tvals, uint8_t* tmeta, void* stream);
 
+/* ss_prune24_act_tiled -- ss_prune24_act with its output written directly in
+ * the tiled layout (one pass instead of ss_prune24_act + ss_pack_sparse; the
+ * bytes are identical to that pair). Same sources as ss_prune24_act. X [M][K]
+ * BF16 (ldx elements), K % 4 == 0; out_dt I8 / FP8E4M3 (sx[M] per-token
+ * scales) or BF16 (sx NULL); tvals / tmeta sized by ss_tiled_vals_bytes /
+ * ss_tiled_meta_bytes for (M, ss_lifted_k(K, 2), out_dt), 16-byte aligned,
+ * written completely. */
+ss_status ss_prune24_act_tiled(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
+                               ss_dtype out_dt, void* tvals, uint8_t* tmeta, float* sx, void* stream);
+
 /* ss_spgemm_tiled -- ss_spgemm on a tiled sparse operand.
  * Same product, scales, sides and output rules as ss_spgemm (same sources).
  * The sparse operand is tvals/tmeta of ss_pack_sparse for its rows (N for

@@ -16,6 +16,7 @@ Functions keep the names of the C entry points:
     spgemm(side, M, N, Kc, vals, meta, dense, sx, sw, y_dtype) -> Y [M, N]
     tiled_bytes(rows, Kc, dtype)            -> (tvals bytes, tmeta bytes)
     pack_sparse(vals, meta)                 -> (tvals, tmeta)  tiled operand
+    prune24_act_tiled(X, out_dtype)         -> (tvals, tmeta, sx | None)
     spgemm_tiled(side, M, N, Kc, tvals, tmeta, dense, sx, sw, y_dtype) -> Y [M, N]
 """
 from __future__ import annotations
@@ -55,14 +56,15 @@ lib.ss_tiled_vals_bytes.restype = _i64
 lib.ss_tiled_meta_bytes.argtypes = [_i64, _i64, _int]
 lib.ss_tiled_meta_bytes.restype = _i64
 lib.ss_pack_sparse.argtypes = [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _vp, _vp]
+lib.ss_prune24_act_tiled.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _fp, _vp]
 lib.ss_spgemm_tiled.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
 for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm", "ss_pack_sparse",
-           "ss_spgemm_tiled"):
+           "ss_prune24_act_tiled", "ss_spgemm_tiled"):
     getattr(lib, _f).restype = _int
 
 EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_error", "ss_version",
            "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm",
-           "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_spgemm_tiled")
+           "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_prune24_act_tiled", "ss_spgemm_tiled")
 
 
 class SSError(RuntimeError):
@@ -210,3 +212,20 @@ def spgemm_tiled(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta:
     _check(lib.ss_spgemm_tiled(side, M, N, Kc, dtype_code(dense.dtype), _ptr(tvals), _ptr(tmeta), _ptr(dense),
                                _ld(dense), _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _stream(dense.device)))
     return Y
+
+
+def prune24_act_tiled(X: torch.Tensor, out_dtype="fp8", out=None):
+    """Online 2:4 prune + compress of bf16 activations, written in the tiled layout."""
+    o = dtype_code(out_dtype)
+    M, K = X.shape
+    Kc = lifted_k(K, 2)
+    if out is None:
+        nv, nm = tiled_bytes(M, Kc, o)
+        tv = torch.empty(nv, dtype=torch.uint8, device=X.device)
+        tm = torch.empty(nm, dtype=torch.uint8, device=X.device)
+        sx = None if o == SS_BF16 else torch.empty(M, dtype=torch.float32, device=X.device)
+    else:
+        tv, tm, sx = out
+    _check(lib.ss_prune24_act_tiled(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), o, _ptr(tv), _ptr(tm), _ptr(sx),
+                                    _stream(X.device)))
+    return tv, tm, sx

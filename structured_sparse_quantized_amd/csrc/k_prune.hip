@@ -38,10 +38,10 @@ template <> struct Unit<float> {  // 16 float = 4 x 16 bytes
   __device__ uint32_t key(int i) const { return mag_key_f32(val(i)); }
 };
 
-// OUT: 0 = int8, 1 = fp8, 2 = bf16
+// Prune one unit: 16-bit metadata (4 nibbles) and the kept values packed as 8 codes (w[0..1]) or
+// 8 bf16 (w[0..3]). OUT: 0 = int8, 1 = fp8, 2 = bf16
 template <typename TIn, int OUT>
-__device__ __forceinline__ void emit_unit(const Unit<TIn>& u, bool zero_row, float inv, uint8_t* vrow,
-                                          uint8_t* mrow, int64_t unit) {
+__device__ __forceinline__ uint32_t prune_unit(const Unit<TIn>& u, bool zero_row, float inv, uint32_t* w) {
   uint32_t meta = 0;
   float kv[8];
 #pragma unroll
@@ -56,20 +56,48 @@ __device__ __forceinline__ void emit_unit(const Unit<TIn>& u, bool zero_row, flo
     kv[2 * g] = (v0 == 0.0f) ? 0.0f : v0;  // zeros are stored as +0
     kv[2 * g + 1] = (v1 == 0.0f) ? 0.0f : v1;
   }
-  *reinterpret_cast<uint16_t*>(mrow + unit * 2) = (uint16_t)meta;
   if constexpr (OUT == 2) {
-    uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(kv[2 * i]) | ((uint32_t)f32_to_bf16(kv[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(vrow + unit * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
-    uint32_t w[2] = {0, 0};
+    w[0] = w[1] = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t c = zero_row ? 0u : (uint32_t)Quant<OUT == 1>::code(kv[i], inv);
       w[i >> 2] |= c << (8 * (i & 3));
     }
-    *reinterpret_cast<uint2*>(vrow + unit * 8) = make_uint2(w[0], w[1]);
+  }
+  return meta;
+}
+
+// Prune one unit and store it in the row-major compressed layout.
+template <typename TIn, int OUT>
+__device__ __forceinline__ void emit_unit(const Unit<TIn>& u, bool zero_row, float inv, uint8_t* vrow,
+                                          uint8_t* mrow, int64_t unit) {
+  uint32_t w[4];
+  const uint32_t meta = prune_unit<TIn, OUT>(u, zero_row, inv, w);
+  *reinterpret_cast<uint16_t*>(mrow + unit * 2) = (uint16_t)meta;
+  if constexpr (OUT == 2) *reinterpret_cast<uint4*>(vrow + unit * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  else *reinterpret_cast<uint2*>(vrow + unit * 8) = make_uint2(w[0], w[1]);
+}
+
+// Prune one unit of row `row` and store it in the tiled layout of the product (k_spgemm_tiled.hip):
+// a step is 64 value bytes per row (8 units of 8-bit codes, 4 units of bf16); lane row%16 + 16*chunk.
+template <typename TIn, int OUT>
+__device__ __forceinline__ void emit_unit_tiled(const Unit<TIn>& u, bool zero_row, float inv, uint8_t* tv, uint8_t* tm,
+                                                int row, int unit, int KSP) {
+  uint32_t w[4];
+  const uint32_t meta = prune_unit<TIn, OUT>(u, zero_row, inv, w);
+  const int rb = row >> 4, r = row & 15, KS4 = KSP >> 2;
+  if constexpr (OUT == 2) {
+    const int s = unit >> 2, lane = r + 16 * (unit & 3);
+    *reinterpret_cast<uint4*>(tv + ((int64_t)rb * KSP + s) * 1024 + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint16_t*>(tm + ((int64_t)rb * KS4 + (s >> 2)) * 512 + 8 * lane + 2 * (s & 3)) = (uint16_t)meta;
+  } else {
+    const int s = unit >> 3, lane = r + 16 * ((unit >> 1) & 3), half = unit & 1;
+    *reinterpret_cast<uint2*>(tv + ((int64_t)rb * KSP + s) * 1024 + 16 * lane + 8 * half) = make_uint2(w[0], w[1]);
+    *reinterpret_cast<uint16_t*>(tm + ((int64_t)rb * KS4 + (s >> 2)) * 1024 + 16 * lane + 4 * (s & 3) + 2 * half) =
+        (uint16_t)meta;
   }
 }
 
@@ -95,30 +123,35 @@ template <typename TIn> __device__ __forceinline__ float unit_absmax(const Unit<
 // Persistent workgroups walk rows r, r + grid, ...; UPT units per thread are
 // held in registers and the next row is loaded before the current one is
 // reduced and written, so HBM reads and writes overlap.
-template <typename TIn, int OUT, int UPT, bool PIPE>
-__global__ __launch_bounds__(kBlock, (PIPE || UPT > 2) ? 2 : (UPT > 1 ? 4 : 8)) void prune24_kernel(const TIn* __restrict__ X, int64_t ldx, int M, int K,
+// TILED: vals/meta are the tiled operand (ldv_bytes = padded step count KSP, ldm unused); rows up to the
+// next multiple of 16 are written (zero past M) and units up to the padded step count.
+template <typename TIn, int OUT, int UPT, bool PIPE, bool TILED = false>
+__global__ __launch_bounds__(kBlock, (PIPE || UPT > 2) ? 2 : ((UPT > 1 || TILED) ? 4 : 8)) void prune24_kernel(const TIn* __restrict__ X, int64_t ldx, int M, int K,
                                                          uint8_t* __restrict__ vals, int64_t ldv_bytes,
                                                          uint8_t* __restrict__ meta, int64_t ldm, int Kc,
                                                          float* __restrict__ scale) {
   __shared__ float red[kBlock / 64];
   const int tid = threadIdx.x;
-  const int units = Kc / 16;              // includes padding units (all zero)
+  const int KSP = (int)ldv_bytes;
+  // includes padding units (all zero)
+  const int units = TILED ? KSP * (OUT == 2 ? 4 : 8) : Kc / 16;
+  const int rows = TILED ? (M + 15) / 16 * 16 : M;
   const int data_units = (K + 15) / 16;
   Unit<TIn> cur[UPT], nxt[PIPE ? UPT : 1];
   auto load = [&](Unit<TIn>* u, int r) {
-    const TIn* xr = X + (int64_t)r * ldx;
+    const TIn* xr = X + (int64_t)(r < M ? r : 0) * ldx;
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int un = tid + i * kBlock;
-      if (un < data_units) load_unit(u[i], xr, un, K);
+      if (un < data_units && r < M) load_unit(u[i], xr, un, K);
       else u[i] = Unit<TIn>{};
     }
   };
   int r = blockIdx.x;
-  if (r < M) load(cur, r);
-  for (; r < M; r += gridDim.x) {
+  if (r < rows) load(cur, r);
+  for (; r < rows; r += gridDim.x) {
     const int rn = r + gridDim.x;
-    if (PIPE && rn < M) load(nxt, rn);
+    if (PIPE && rn < rows) load(nxt, rn);
     bool zero_row = false;
     float inv = 0.0f;
     if constexpr (OUT != 2) {
@@ -129,34 +162,46 @@ __global__ __launch_bounds__(kBlock, (PIPE || UPT > 2) ? 2 : (UPT > 1 ? 4 : 8)) 
       constexpr float Q = (OUT == 1) ? 448.0f : 127.0f;
       zero_row = (amax == 0.0f);
       inv = zero_row ? 0.0f : Q / amax;
-      if (tid == 0) scale[r] = zero_row ? 0.0f : amax / Q;
+      if (tid == 0 && r < M) scale[r] = zero_row ? 0.0f : amax / Q;
     }
-    uint8_t* vr = vals + (int64_t)r * ldv_bytes;
-    uint8_t* mr = meta + (int64_t)r * ldm;
+    if constexpr (TILED) {
 #pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int un = tid + i * kBlock;
-      if (un < units) emit_unit<TIn, OUT>(cur[i], zero_row, inv, vr, mr, un);
+      for (int i = 0; i < UPT; ++i) {
+        const int un = tid + i * kBlock;
+        if (un < units) emit_unit_tiled<TIn, OUT>(cur[i], zero_row, inv, vals, meta, r, un, KSP);
+      }
+    } else {
+      uint8_t* vr = vals + (int64_t)r * ldv_bytes;
+      uint8_t* mr = meta + (int64_t)r * ldm;
+#pragma unroll
+      for (int i = 0; i < UPT; ++i) {
+        const int un = tid + i * kBlock;
+        if (un < units) emit_unit<TIn, OUT>(cur[i], zero_row, inv, vr, mr, un);
+      }
     }
     if constexpr (PIPE) {
 #pragma unroll
       for (int i = 0; i < UPT; ++i) cur[i] = nxt[i];
-    } else if (rn < M) {
+    } else if (rn < rows) {
       load(cur, rn);
     }
   }
 }
 
-// Rows longer than kBlock * 4 units: absmax pass, then a second read.
-template <typename TIn, int OUT>
+// Rows longer than kBlock * 4 units: absmax pass, then a second read. TILED as in prune24_kernel (grid
+// covers the rows up to the next multiple of 16; M = the real row count).
+template <typename TIn, int OUT, bool TILED = false>
 __global__ __launch_bounds__(kBlock) void prune24_long_kernel(const TIn* __restrict__ X, int64_t ldx, int64_t K,
                                                               uint8_t* __restrict__ vals, int64_t ldv_bytes,
                                                               uint8_t* __restrict__ meta, int64_t ldm, int64_t Kc,
-                                                              float* __restrict__ scale) {
+                                                              float* __restrict__ scale, int64_t M = 0) {
   __shared__ float red[kBlock / 64];
   const int64_t row = blockIdx.x;
-  const TIn* xr = X + row * ldx;
-  const int64_t units = Kc / 16, data_units = (K + 15) / 16;
+  const bool live = !TILED || row < M;
+  const TIn* xr = X + (live ? row : 0) * ldx;
+  const int KSP = (int)ldv_bytes;
+  const int64_t units = TILED ? (int64_t)KSP * (OUT == 2 ? 4 : 8) : Kc / 16;
+  const int64_t data_units = live ? (K + 15) / 16 : 0;
   bool zero_row = false;
   float inv = 0.0f;
   if constexpr (OUT != 2) {
@@ -170,12 +215,96 @@ __global__ __launch_bounds__(kBlock) void prune24_long_kernel(const TIn* __restr
     constexpr float Q = (OUT == 1) ? 448.0f : 127.0f;
     zero_row = (amax == 0.0f);
     inv = zero_row ? 0.0f : Q / amax;
-    if (threadIdx.x == 0) scale[row] = zero_row ? 0.0f : amax / Q;
+    if (threadIdx.x == 0 && live) scale[row] = zero_row ? 0.0f : amax / Q;
   }
   for (int64_t un = threadIdx.x; un < units; un += kBlock) {
     Unit<TIn> t{};
     if (un < data_units) load_unit(t, xr, un, K);
-    emit_unit<TIn, OUT>(t, zero_row, inv, vals + row * ldv_bytes, meta + row * ldm, un);
+    if constexpr (TILED) emit_unit_tiled<TIn, OUT>(t, zero_row, inv, vals, meta, (int)row, (int)un, KSP);
+    else emit_unit<TIn, OUT>(t, zero_row, inv, vals + row * ldv_bytes, meta + row * ldm, un);
+  }
+}
+
+// bf16 output in the tiled layout (no scale, one read pass): one workgroup per 16-row block, 8 waves;
+// lane l of a wave owns row l%16 and the 16-byte lane chunk l/16 of each step of its 4-step groups, so
+// every step's values leave as one 1 KB block and every group's index words as one 512-byte block.
+__global__ __launch_bounds__(512) void prune24_act_tiled_bf16_kernel(const uint16_t* __restrict__ X, int64_t ldx, int M,
+                                                                     int K, int KS, uint8_t* __restrict__ tv,
+                                                                     uint8_t* __restrict__ tm) {
+  constexpr int NWV = 8;
+  const int rb = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, c = lane >> 4, row = rb * 16 + r;
+  const bool live = row < M;
+  const uint16_t* xr = X + (int64_t)(live ? row : 0) * ldx;
+  const int KS4 = KS / 4;  // KS is a multiple of 4 for bf16 (Kc % 256 == 0)
+  for (int g = wave; g < KS4; g += NWV) {
+    Unit<uint16_t> x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // a step is 64 K positions: 4 units, one per lane chunk
+      const int unit = (4 * g + q) * 4 + c;
+      if (live) load_unit(x[q], xr, unit, K);
+      else x[q] = Unit<uint16_t>{};
+    }
+    uint32_t mw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w[4];
+      mw[q] = prune_unit<uint16_t, 2>(x[q], false, 0.0f, w);
+      *reinterpret_cast<uint4*>(tv + ((int64_t)rb * KS + 4 * g + q) * 1024 + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    *reinterpret_cast<uint2*>(tm + ((int64_t)rb * KS4 + g) * 512 + 8 * lane) =
+        make_uint2(mw[0] | (mw[1] << 16), mw[2] | (mw[3] << 16));
+  }
+}
+
+// forward declaration (defined below)
+int num_cus_p();
+
+template <int OUT>
+static hipError_t launch_p24_tiled(const uint16_t* X, int64_t ldx, int64_t M, int64_t K, int64_t Kc, uint8_t* tv,
+                                   uint8_t* tm, float* sx, hipStream_t st) {
+  const int es = OUT == 2 ? 2 : 1;
+  const int KS = (int)(Kc * es / 128), KSP = (KS + 3) / 4 * 4;
+  const int units = KSP * (OUT == 2 ? 4 : 8);
+  const int64_t upt = (units + kBlock - 1) / kBlock;
+  const int64_t rows = (M + 15) / 16 * 16;
+  const bool pipe = rows > 16 * (int64_t)num_cus_p();
+  const unsigned grid = (unsigned)(pipe ? 8 * (int64_t)num_cus_p() : rows);
+  const int m = (int)M, k = (int)K, kc = (int)Kc;
+#define SS_PT(U_)                                                                                                      \
+  do {                                                                                                                 \
+    if (pipe)                                                                                                          \
+      hipLaunchKernelGGL((prune24_kernel<uint16_t, OUT, U_, true, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k,  \
+                         tv, (int64_t)KSP, tm, (int64_t)0, kc, sx);                                                    \
+    else                                                                                                               \
+      hipLaunchKernelGGL((prune24_kernel<uint16_t, OUT, U_, false, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k, \
+                         tv, (int64_t)KSP, tm, (int64_t)0, kc, sx);                                                    \
+  } while (0)
+  if (upt > 4) {  // long rows: absmax pass, then a second read
+    hipLaunchKernelGGL((prune24_long_kernel<uint16_t, OUT, true>), dim3((unsigned)rows), dim3(kBlock), 0, st, X, ldx, K, tv,
+                       (int64_t)KSP, tm, (int64_t)0, Kc, sx, M);
+    return hipGetLastError();
+  }
+  if (upt <= 1) SS_PT(1);
+  else if (upt <= 2) SS_PT(2);
+  else SS_PT(4);
+#undef SS_PT
+  return hipGetLastError();
+}
+
+hipError_t launch_prune24_act_tiled(int out, const void* X, int64_t ldx, int64_t M, int64_t K, int64_t Kc, void* tv,
+                                    uint8_t* tm, float* sx, hipStream_t st) {
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  uint8_t* v = static_cast<uint8_t*>(tv);
+  switch (out) {
+    case 0: return launch_p24_tiled<0>(x, ldx, M, K, Kc, v, tm, sx, st);
+    case 1: return launch_p24_tiled<1>(x, ldx, M, K, Kc, v, tm, sx, st);
+    default: {
+      const int KS = (int)(Kc * 2 / 128);
+      hipLaunchKernelGGL(prune24_act_tiled_bf16_kernel, dim3((unsigned)((M + 15) / 16)), dim3(512), 0, st, x, ldx, (int)M,
+                         (int)K, KS, v, tm);
+      return hipGetLastError();
+    }
   }
 }
 

@@ -222,6 +222,26 @@ ss_status ss_pack_sparse(int64_t rows, int64_t Kc, ss_dtype dt, const void* vals
                     "ss_pack_sparse launch");
 }
 
+ss_status ss_prune24_act_tiled(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, ss_dtype out_dt,
+                               void* tvals, uint8_t* tmeta, float* sx, void* stream) {
+  if (x_dt != SS_BF16) return fail(SS_ERR_DTYPE, "activations must be BF16");
+  if (out_dt != SS_I8 && out_dt != SS_FP8E4M3 && out_dt != SS_BF16) return fail(SS_ERR_DTYPE, "bad output type");
+  if (M < 0 || K < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (K % 4 != 0) return fail(SS_ERR_SHAPE, "K=%lld is not a multiple of 4", (long long)K);
+  if (M > 0x7FFFFFF0LL || K > 0x3FFFFFF0LL) return fail(SS_ERR_SHAPE, "too large");
+  if (M == 0 || K == 0) return ok();
+  ss_status s;
+  if ((s = check_mat("X", X, M, K, ldx, 2)) != SS_OK) return s;
+  if (!tvals || !tmeta) return fail(SS_ERR_NULL, "tiled outputs are NULL");
+  if (!aligned16(tvals) || !aligned16(tmeta)) return fail(SS_ERR_ALIGN, "tiled outputs are not 16-byte aligned");
+  if (out_dt == SS_BF16 && sx) return fail(SS_ERR_DTYPE, "BF16 output takes no scale");
+  if (out_dt != SS_BF16 && !sx) return fail(SS_ERR_NULL, "quantised output needs sx");
+  const int64_t Kc = ss_lifted_k(K, 2);
+  return hip_status(ss::launch_prune24_act_tiled(out_code(out_dt), X, ldx, M, K, Kc, tvals, tmeta, sx,
+                                                 (hipStream_t)stream),
+                    "ss_prune24_act_tiled launch");
+}
+
 ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
                           const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
                           ss_dtype y_dt, void* Y, int64_t ldy, void* stream) {

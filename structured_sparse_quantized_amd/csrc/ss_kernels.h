@@ -20,6 +20,10 @@ hipError_t launch_spgemm(bool side_x, int ab, int yt, int64_t R, int64_t C, int6
                          int64_t lda_bytes, const uint8_t* am, int64_t ldm, const void* bd, int64_t ldb_bytes,
                          const float* sx, const float* sw, void* Y, int64_t ldy, hipStream_t st);
 
+// Online 2:4 prune of bf16 activations written in the tiled layout (out: 0 = int8, 1 = fp8, 2 = bf16).
+hipError_t launch_prune24_act_tiled(int out, const void* X, int64_t ldx, int64_t M, int64_t K, int64_t Kc, void* tv,
+                                    uint8_t* tm, float* sx, hipStream_t st);
+
 // Tiled sparse operand and the product that reads it. es = value bytes (1: int8/fp8, 2: bf16).
 int64_t tiled_vals_bytes(int64_t rows, int64_t Kc, int es);
 int64_t tiled_meta_bytes(int64_t rows, int64_t Kc, int es);

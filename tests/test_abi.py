@@ -115,6 +115,14 @@ def test_tiled_validation_statuses():
     odd = ctypes.c_void_p((1 << 20) + 8)
     assert L.ss_pack_sparse(4, 256, ss.SS_I8, FAKE, 128, FAKE, 32, odd, FAKE, None) == ss.SS_ERR_ALIGN
     assert L.ss_pack_sparse(0, 256, ss.SS_I8, FAKE, 128, FAKE, 32, FAKE, FAKE, None) == ss.SS_OK
+    # one-pass prune into the tiled layout
+    P = L.ss_prune24_act_tiled
+    assert P(FAKE, ss.SS_F32, 4, 8, 8, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_DTYPE
+    assert P(FAKE, ss.SS_BF16, 4, 6, 8, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
+    assert P(FAKE, ss.SS_BF16, 4, 8, 8, ss.SS_I8, FAKE, FAKE, None, None) == ss.SS_ERR_NULL
+    assert P(FAKE, ss.SS_BF16, 4, 8, 8, ss.SS_BF16, FAKE, FAKE, FAKE, None) == ss.SS_ERR_DTYPE
+    assert P(FAKE, ss.SS_BF16, 4, 8, 8, ss.SS_I8, None, FAKE, FAKE, None) == ss.SS_ERR_NULL
+    assert P(FAKE, ss.SS_BF16, 0, 8, 8, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_OK
     # product
     def g(side=0, M=4, N=4, Kc=256, ab=ss.SS_I8, tv=FAKE, tm=FAKE, d=FAKE, ldd=256, sx=FAKE, sw=FAKE,
           y=ss.SS_BF16, Y=FAKE, ldy=8):

@@ -221,3 +221,50 @@ def test_activation_sparse_path_tiled_bf16(ss):
     ov, om, _ = oracle.prune24_act(X, "bf16")
     exp = oracle.spgemm("X", ov, om, wb, K, "bf16", None, None, "f32")
     assert rel_fro(Y, exp) <= TOL
+
+
+PRUNE_TILED_SHAPES = [(1, 8), (7, 24), (16, 512), (33, 4096), (130, 520), (2, 18944), (300, 1000)]
+
+
+@pytest.mark.parametrize("out", ["i8", "fp8", "bf16"])
+@pytest.mark.parametrize("shape", PRUNE_TILED_SHAPES)
+def test_prune24_act_tiled(ss, out, shape):
+    """One-pass prune into the tiled layout: the oracle's compressed operand re-indexed, and the same bytes as
+    ss_prune24_act followed by ss_pack_sparse."""
+    M, K = shape
+    rng = np.random.default_rng(M * 7 + K)
+    X = synth.f32_to_bf16_bits(synth.normal_f32(rng, (M, K)))
+    if M > 3:
+        X[3] = 0  # an all-zero token
+    xd = dev_bf16(X)
+    tv, tm, sx = ss.prune24_act_tiled(xd, out)
+    ov, om, osx = oracle.prune24_act(X, out)
+    es = 2 if out == "bf16" else 1
+    ev, em = tile_ref(np.ascontiguousarray(ov).view(np.uint8).reshape(M, -1), om, es)
+    assert np.array_equal(host(tv), ev)
+    assert np.array_equal(host(tm), em)
+    if out == "bf16":
+        assert sx is None
+    else:
+        assert np.array_equal(host(sx), osx)
+    pv, pm, psx = ss.prune24_act(xd, out)
+    rv, rm = ss.pack_sparse(pv, pm)
+    assert np.array_equal(host(rv), host(tv)) and np.array_equal(host(rm), host(tm))
+
+
+@pytest.mark.parametrize("out", ["fp8", "bf16"])
+def test_activation_sparse_layer_one_pass(ss, out):
+    """Online prune into the tiled layout + tiled product, against the oracle layer."""
+    M, N, K = 260, 300, 1024
+    X, W, _ = synth.workload(81, M, N, K, x_kind="bf16")
+    tv, tm, sx = ss.prune24_act_tiled(dev_bf16(X), out)
+    ov, om, osx = oracle.prune24_act(X, out)
+    if out == "bf16":
+        wb = synth.f32_to_bf16_bits(W)
+        wd, sw, ow, osw = dev_bf16(wb), None, wb, None
+    else:
+        wd, sw = ss.quant_lift_act(dev_f32(W), 2, out)
+        ow, osw = oracle.quant_lift_act(W, 2, out)
+    Y = host(ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, K, tv, tm, wd, sx, sw, "f32"))
+    exp = oracle.spgemm("X", ov, om, ow, K, out, osx, osw, "f32")
+    assert rel_fro(Y, exp) <= TOL
