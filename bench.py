@@ -4,16 +4,20 @@ A step is one pass of every kernel on the path over one batch of the
 6:8 sliding-window INT8 workload (W 4096x4096 N(0, 0.02^2) float32, X
 2048x4096 bf16 N(0,1) with 1% outlier columns x20), all INT8:
 
-  slide_decompose(W, 6:8) -> pack_sparse -> quant_lift_act(X, n=4) -> spgemm_tiled(sparse W')   6:8
-  prune24(W)              -> pack_sparse -> quant_lift_act(X, n=2) -> spgemm_tiled(sparse W)    2:4
-  prune24_act_tiled(X), quant_lift_act(W, n=2) -> spgemm_tiled(sparse X)                      2:4 on X
+  slide_decompose_tiled(W, n=4) -> quant_lift_act(X, n=4) -> spgemm_tiled(sparse W')   6:8
+  slide_decompose_tiled(W, n=2) -> quant_lift_act(X, n=2) -> spgemm_tiled(sparse W)    2:4
+  prune24_act_tiled(X), quant_lift_act(W, n=2) -> spgemm_tiled(sparse X)              2:4 on X
 
-The weight-side preparation (decompose or prune, then pack) runs offline in
-a deployment; it is timed here per step all the same.
+The weight-side preparation (decompose or prune, written straight into the
+product's tiled layout) runs offline in a deployment; it is timed here per
+step all the same.
 
-``value`` is tokens per second of the whole step (M tokens per step). The
-JSON line also carries per-kernel times with their throughput against the
-roofline, the online 6:8 prefill rate (quant_lift + spgemm only), the dense
+``value`` is tokens per second of the whole step (M tokens per step), from K
+steps launched back to back between one pair of events. Per-kernel times come
+from a second timed region in which each call runs K times back to back
+between its own pair of events (an event between every two launches would
+drain the queue and add ~3.5 us per event). The JSON line carries these
+per-kernel times with their throughput against the roofline, the online 6:8 prefill rate (quant_lift + spgemm only), the dense
 INT8 comparator, the roofline of the dominant kernel and the CPU oracle
 baseline. Inputs are seeded and synthetic; NBUF rotating buffer sets keep the
 working set above the 256 MB Infinity Cache so kernels stream from HBM.
@@ -78,16 +82,14 @@ def tiled_bytes(rows, Kc):
 def kernel_work(name, Kc68, Kc24):
     """Algorithmic bytes (HBM-bound kernels) or ops (products) per launch."""
     b = {
-        "slide_decompose_68": 4 * N * K + N * Kc68 // 2 + N * Kc68 // 8 + 4 * N,
+        # weight preparation written in the tiled layout: W read once, tiled operand + scales written
+        "slide_decompose_tiled_68": 4 * N * K + sum(tiled_bytes(N, Kc68)) + 4 * N,
         "quant_lift_68": 2 * M * K + M * Kc68 + 4 * M,
-        "prune24_w": 4 * N * K + N * Kc24 // 2 + N * Kc24 // 8 + 4 * N,
+        "prune24_w_tiled": 4 * N * K + sum(tiled_bytes(N, Kc24)) + 4 * N,
         "quant_lift_24": 2 * M * K + M * Kc24 + 4 * M,
         # online prune of X written in the tiled layout: X read once, tiled operand + scales written
         "prune24_act_tiled": 2 * M * K + sum(tiled_bytes(M, Kc24)) + 4 * M,
         "quant_w": 4 * N * K + N * Kc24 + 4 * N,
-        # layout change: read the row-major compressed operand, write the tiled one
-        "pack_68": N * Kc68 // 2 + N * Kc68 // 8 + sum(tiled_bytes(N, Kc68)),
-        "pack_24": N * Kc24 // 2 + N * Kc24 // 8 + sum(tiled_bytes(N, Kc24)),
     }
     # products: multiply-adds on the kept values only (K'/2 per row), x2 ops
     ops = {
@@ -128,67 +130,77 @@ def main():
     for i in range(NBUF):
         bufs.append(dict(
             X=X0.clone(), W=W0.clone(),
-            w68=(mk((N, Kc68 // 2), torch.int8), mk((N, Kc68 // 8), torch.uint8), mk(N, torch.float32)),
-            t68=tuple(mk(nb, torch.uint8) for nb in tiled_bytes(N, Kc68)),
-            t24=tuple(mk(nb, torch.uint8) for nb in tiled_bytes(N, Kc24)),
+            t68=tuple(mk(nb, torch.uint8) for nb in tiled_bytes(N, Kc68)) + (mk(N, torch.float32),),
+            t24=tuple(mk(nb, torch.uint8) for nb in tiled_bytes(N, Kc24)) + (mk(N, torch.float32),),
             tx=tuple(mk(nb, torch.uint8) for nb in tiled_bytes(M, Kc24)),
             x68=(mk((M, Kc68), torch.int8), mk(M, torch.float32)),
             y68=mk((M, N), torch.bfloat16),
-            w24=(mk((N, Kc24 // 2), torch.int8), mk((N, Kc24 // 8), torch.uint8), mk(N, torch.float32)),
             x24=(mk((M, Kc24), torch.int8), mk(M, torch.float32)),
             y24=mk((M, N), torch.bfloat16),
             xs=(mk(M, torch.float32),),
             wq=(mk((N, Kc24), torch.int8), mk(N, torch.float32)),
             yx=mk((M, N), torch.bfloat16),
         ))
-    names = ["slide_decompose_68", "pack_68", "quant_lift_68", "spgemm_68", "prune24_w", "pack_24",
-             "quant_lift_24", "spgemm_24", "prune24_act_tiled", "quant_w", "spgemm_x"]
+    names = ["slide_decompose_tiled_68", "quant_lift_68", "spgemm_68", "prune24_w_tiled", "quant_lift_24",
+             "spgemm_24", "prune24_act_tiled", "quant_w", "spgemm_x"]
 
-    def step(b, ev=None):
-        calls = [
-            lambda: ss.slide_decompose(b["W"], PAT, "i8", out=b["w68"]),
-            lambda: ss.pack_sparse(b["w68"][0], b["w68"][1], out=b["t68"]),
+    def calls(b):
+        return [
+            lambda: ss.slide_decompose_tiled(b["W"], PAT, "i8", out=b["t68"]),
             lambda: ss.quant_lift_act(b["X"], PAT, "i8", out=b["x68"]),
             lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc68, b["t68"][0], b["t68"][1], b["x68"][0], b["x68"][1],
-                                    b["w68"][2], "bf16", out=b["y68"]),
-            lambda: ss.prune24(b["W"], "i8", out=b["w24"]),
-            lambda: ss.pack_sparse(b["w24"][0], b["w24"][1], out=b["t24"]),
+                                    b["t68"][2], "bf16", out=b["y68"]),
+            lambda: ss.slide_decompose_tiled(b["W"], 2, "i8", out=b["t24"]),
             lambda: ss.quant_lift_act(b["X"], 2, "i8", out=b["x24"]),
             lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc24, b["t24"][0], b["t24"][1], b["x24"][0], b["x24"][1],
-                                    b["w24"][2], "bf16", out=b["y24"]),
+                                    b["t24"][2], "bf16", out=b["y24"]),
             lambda: ss.prune24_act_tiled(b["X"], "i8", out=(b["tx"][0], b["tx"][1], b["xs"][0])),
             lambda: ss.quant_lift_act(b["W"], 2, "i8", out=b["wq"]),
             lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, Kc24, b["tx"][0], b["tx"][1], b["wq"][0], b["xs"][0],
                                     b["wq"][1], "bf16", out=b["yx"]),
         ]
-        for i, c in enumerate(calls):
-            if ev is not None:
-                ev[i][0].record()
+
+    steps_calls = [calls(b) for b in bufs]
+
+    def step(s):
+        for c in steps_calls[s % NBUF]:
             c()
-            if ev is not None:
-                ev[i][1].record()
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for s in range(args.warmup):
-        step(bufs[s % NBUF])
+        step(s)
     torch.cuda.synchronize()
 
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in names]
-           for _ in range(args.steps)]
+    # Timed region 1: K whole steps back to back, no per-call events (a timing
+    # event between two launches costs the GPU ~3.5 us: it drains the queue).
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
-        step(bufs[s % NBUF], evs[s])
+        step(s)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    per_kernel_ms = {n: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
-                     for i, n in enumerate(names)}
     print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr, flush=True)
+
+    # Timed region 2: per-call durations. Each call of the step runs K times
+    # back to back (rotating buffer sets) between one pair of events on the
+    # stream the kernels are launched on; duration = elapsed / K.
+    per_kernel_ms = {}
+    for i, n in enumerate(names):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(args.steps):
+            steps_calls[s % NBUF][i]()
+        e1.record()
+        torch.cuda.synchronize()
+        per_kernel_ms[n] = e0.elapsed_time(e1) / args.steps
+    print("[bench] per-call us: " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in per_kernel_ms.items()),
+          file=sys.stderr, flush=True)
 
     kernels = {}
     for n in names:
@@ -277,6 +289,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "rotating_buffer_sets": NBUF,
+        "per_call_sum_ms": sum(per_kernel_ms.values()),
         "suite": suite_res,
     }
     print(json.dumps(out))

@@ -217,6 +217,17 @@ ss_status ss_pack_sparse(int64_t rows, int64_t Kc, ss_dtype dt, const void* vals
 ss_status ss_prune24_act_tiled(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx,
                                ss_dtype out_dt, void* tvals, uint8_t* tmeta, float* sx, void* stream);
 
+/* ss_slide_decompose_tiled -- ss_slide_decompose with its output written
+ * directly in the tiled layout (one pass instead of ss_slide_decompose +
+ * ss_pack_sparse; the bytes are identical to that pair). Same sources as
+ * ss_slide_decompose; n = 2 is the 2:4 prune of ss_prune24 (any K: the last
+ * 4-group is zero-padded). W [rows][K] F32 or BF16 (ldw elements); out_dt
+ * I8 / FP8E4M3 (scale[rows] per-channel scales) or BF16 (scale NULL);
+ * tvals / tmeta sized by ss_tiled_vals_bytes / ss_tiled_meta_bytes for
+ * (rows, ss_lifted_k(K, n), out_dt), 16-byte aligned, written completely. */
+ss_status ss_slide_decompose_tiled(const void* W, ss_dtype w_dt, int64_t rows, int64_t K, int64_t ldw, int n,
+                                   ss_dtype out_dt, void* tvals, uint8_t* tmeta, float* scale, void* stream);
+
 /* ss_spgemm_tiled -- ss_spgemm on a tiled sparse operand.
  * Same product, scales, sides and output rules as ss_spgemm (same sources).
  * The sparse operand is tvals/tmeta of ss_pack_sparse for its rows (N for

@@ -17,6 +17,7 @@ Functions keep the names of the C entry points:
     tiled_bytes(rows, Kc, dtype)            -> (tvals bytes, tmeta bytes)
     pack_sparse(vals, meta)                 -> (tvals, tmeta)  tiled operand
     prune24_act_tiled(X, out_dtype)         -> (tvals, tmeta, sx | None)
+    slide_decompose_tiled(W, n, out_dtype)  -> (tvals, tmeta, scale | None)
     spgemm_tiled(side, M, N, Kc, tvals, tmeta, dense, sx, sw, y_dtype) -> Y [M, N]
 """
 from __future__ import annotations
@@ -57,14 +58,16 @@ lib.ss_tiled_meta_bytes.argtypes = [_i64, _i64, _int]
 lib.ss_tiled_meta_bytes.restype = _i64
 lib.ss_pack_sparse.argtypes = [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _vp, _vp]
 lib.ss_prune24_act_tiled.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _fp, _vp]
+lib.ss_slide_decompose_tiled.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp, _vp, _fp, _vp]
 lib.ss_spgemm_tiled.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
 for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm", "ss_pack_sparse",
-           "ss_prune24_act_tiled", "ss_spgemm_tiled"):
+           "ss_prune24_act_tiled", "ss_slide_decompose_tiled", "ss_spgemm_tiled"):
     getattr(lib, _f).restype = _int
 
 EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_error", "ss_version",
            "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm",
-           "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_prune24_act_tiled", "ss_spgemm_tiled")
+           "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_prune24_act_tiled",
+           "ss_slide_decompose_tiled", "ss_spgemm_tiled")
 
 
 class SSError(RuntimeError):
@@ -229,3 +232,20 @@ def prune24_act_tiled(X: torch.Tensor, out_dtype="fp8", out=None):
     _check(lib.ss_prune24_act_tiled(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), o, _ptr(tv), _ptr(tm), _ptr(sx),
                                     _stream(X.device)))
     return tv, tm, sx
+
+
+def slide_decompose_tiled(W: torch.Tensor, n: int, out_dtype="i8", out=None):
+    """Offline (2n-2):2n prune + decomposition (n = 2: the 2:4 prune), written in the tiled layout."""
+    o = dtype_code(out_dtype)
+    rows, K = W.shape
+    Kc = lifted_k(K, n)
+    if out is None:
+        nv, nm = tiled_bytes(rows, Kc, o)
+        tv = torch.empty(nv, dtype=torch.uint8, device=W.device)
+        tm = torch.empty(nm, dtype=torch.uint8, device=W.device)
+        scale = None if o == SS_BF16 else torch.empty(rows, dtype=torch.float32, device=W.device)
+    else:
+        tv, tm, scale = out
+    _check(lib.ss_slide_decompose_tiled(_ptr(W), dtype_code(W.dtype), rows, K, _ld(W), n, o, _ptr(tv), _ptr(tm),
+                                        _ptr(scale), _stream(W.device)))
+    return tv, tm, scale

@@ -124,7 +124,8 @@ template <typename TIn> __device__ __forceinline__ float unit_absmax(const Unit<
 // held in registers and the next row is loaded before the current one is
 // reduced and written, so HBM reads and writes overlap.
 // TILED: vals/meta are the tiled operand (ldv_bytes = padded step count KSP, ldm unused); rows up to the
-// next multiple of 16 are written (zero past M) and units up to the padded step count.
+// next multiple of 16 are written (zero past M) and units up to the padded step count; iteration i takes
+// row xcd_row(i, rows) so a 16-row block is written through one L2.
 template <typename TIn, int OUT, int UPT, bool PIPE, bool TILED = false>
 __global__ __launch_bounds__(kBlock, (PIPE || UPT > 2) ? 2 : ((UPT > 1 || TILED) ? 4 : 8)) void prune24_kernel(const TIn* __restrict__ X, int64_t ldx, int M, int K,
                                                          uint8_t* __restrict__ vals, int64_t ldv_bytes,
@@ -147,11 +148,13 @@ __global__ __launch_bounds__(kBlock, (PIPE || UPT > 2) ? 2 : ((UPT > 1 || TILED)
       else u[i] = Unit<TIn>{};
     }
   };
-  int r = blockIdx.x;
-  if (r < rows) load(cur, r);
-  for (; r < rows; r += gridDim.x) {
-    const int rn = r + gridDim.x;
-    if (PIPE && rn < rows) load(nxt, rn);
+  auto rowof = [&](int it) { return TILED ? xcd_row(it, rows) : it; };
+  int it = blockIdx.x;
+  if (it < rows) load(cur, rowof(it));
+  for (; it < rows; it += gridDim.x) {
+    const int r = rowof(it);
+    const int itn = it + gridDim.x;
+    if (PIPE && itn < rows) load(nxt, rowof(itn));
     bool zero_row = false;
     float inv = 0.0f;
     if constexpr (OUT != 2) {
@@ -181,9 +184,9 @@ __global__ __launch_bounds__(kBlock, (PIPE || UPT > 2) ? 2 : ((UPT > 1 || TILED)
     }
     if constexpr (PIPE) {
 #pragma unroll
-      for (int i = 0; i < UPT; ++i) cur[i] = nxt[i];
-    } else if (rn < rows) {
-      load(cur, rn);
+      for (int u = 0; u < UPT; ++u) cur[u] = nxt[u];
+    } else if (itn < rows) {
+      load(cur, rowof(itn));
     }
   }
 }
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kBlock) void prune24_long_kernel(const TIn* __restr
                                                               uint8_t* __restrict__ meta, int64_t ldm, int64_t Kc,
                                                               float* __restrict__ scale, int64_t M = 0) {
   __shared__ float red[kBlock / 64];
-  const int64_t row = blockIdx.x;
+  const int64_t row = TILED ? xcd_row(blockIdx.x, gridDim.x) : blockIdx.x;
   const bool live = !TILED || row < M;
   const TIn* xr = X + (live ? row : 0) * ldx;
   const int KSP = (int)ldv_bytes;
@@ -260,8 +263,8 @@ __global__ __launch_bounds__(512) void prune24_act_tiled_bf16_kernel(const uint1
 // forward declaration (defined below)
 int num_cus_p();
 
-template <int OUT>
-static hipError_t launch_p24_tiled(const uint16_t* X, int64_t ldx, int64_t M, int64_t K, int64_t Kc, uint8_t* tv,
+template <typename TIn, int OUT>
+static hipError_t launch_p24_tiled(const TIn* X, int64_t ldx, int64_t M, int64_t K, int64_t Kc, uint8_t* tv,
                                    uint8_t* tm, float* sx, hipStream_t st) {
   const int es = OUT == 2 ? 2 : 1;
   const int KS = (int)(Kc * es / 128), KSP = (KS + 3) / 4 * 4;
@@ -274,14 +277,14 @@ static hipError_t launch_p24_tiled(const uint16_t* X, int64_t ldx, int64_t M, in
 #define SS_PT(U_)                                                                                                      \
   do {                                                                                                                 \
     if (pipe)                                                                                                          \
-      hipLaunchKernelGGL((prune24_kernel<uint16_t, OUT, U_, true, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k,  \
+      hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, true, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k,  \
                          tv, (int64_t)KSP, tm, (int64_t)0, kc, sx);                                                    \
     else                                                                                                               \
-      hipLaunchKernelGGL((prune24_kernel<uint16_t, OUT, U_, false, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k, \
+      hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, false, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k, \
                          tv, (int64_t)KSP, tm, (int64_t)0, kc, sx);                                                    \
   } while (0)
   if (upt > 4) {  // long rows: absmax pass, then a second read
-    hipLaunchKernelGGL((prune24_long_kernel<uint16_t, OUT, true>), dim3((unsigned)rows), dim3(kBlock), 0, st, X, ldx, K, tv,
+    hipLaunchKernelGGL((prune24_long_kernel<TIn, OUT, true>), dim3((unsigned)rows), dim3(kBlock), 0, st, X, ldx, K, tv,
                        (int64_t)KSP, tm, (int64_t)0, Kc, sx, M);
     return hipGetLastError();
   }
@@ -297,14 +300,31 @@ hipError_t launch_prune24_act_tiled(int out, const void* X, int64_t ldx, int64_t
   const uint16_t* x = static_cast<const uint16_t*>(X);
   uint8_t* v = static_cast<uint8_t*>(tv);
   switch (out) {
-    case 0: return launch_p24_tiled<0>(x, ldx, M, K, Kc, v, tm, sx, st);
-    case 1: return launch_p24_tiled<1>(x, ldx, M, K, Kc, v, tm, sx, st);
+    case 0: return launch_p24_tiled<uint16_t, 0>(x, ldx, M, K, Kc, v, tm, sx, st);
+    case 1: return launch_p24_tiled<uint16_t, 1>(x, ldx, M, K, Kc, v, tm, sx, st);
     default: {
       const int KS = (int)(Kc * 2 / 128);
       hipLaunchKernelGGL(prune24_act_tiled_bf16_kernel, dim3((unsigned)((M + 15) / 16)), dim3(512), 0, st, x, ldx, (int)M,
                          (int)K, KS, v, tm);
       return hipGetLastError();
     }
+  }
+}
+
+hipError_t launch_prune24_tiled(bool in_bf16, int out, const void* W, int64_t ldw, int64_t rows, int64_t K, int64_t Kc,
+                                void* tv, uint8_t* tm, float* scale, hipStream_t st) {
+  uint8_t* v = static_cast<uint8_t*>(tv);
+  if (in_bf16) {
+    const uint16_t* w = static_cast<const uint16_t*>(W);
+    if (out == 2) return launch_prune24_act_tiled(2, W, ldw, rows, K, Kc, tv, tm, scale, st);
+    return out == 0 ? launch_p24_tiled<uint16_t, 0>(w, ldw, rows, K, Kc, v, tm, scale, st)
+                    : launch_p24_tiled<uint16_t, 1>(w, ldw, rows, K, Kc, v, tm, scale, st);
+  }
+  const float* w = static_cast<const float*>(W);
+  switch (out) {
+    case 0: return launch_p24_tiled<float, 0>(w, ldw, rows, K, Kc, v, tm, scale, st);
+    case 1: return launch_p24_tiled<float, 1>(w, ldw, rows, K, Kc, v, tm, scale, st);
+    default: return launch_p24_tiled<float, 2>(w, ldw, rows, K, Kc, v, tm, scale, st);
   }
 }
 

@@ -4,19 +4,26 @@
 // nonzeros to the n-1 stride-2 width-4 windows, per-channel quantisation and
 // 2:4 compression of W' directly in K' order.
 //
-// One workgroup per weight row; thread i owns groups i, i + 256, ... A group is
-// loaded once (8-byte vectors for float32, 4-byte for bf16), pruned, split into
-// its n-1 windows, quantised and written into an LDS image of the output row,
-// which is then stored with 16-byte writes. Rows whose groups fit in the
-// register budget (G <= 256 * kGPT) are read from HBM once; longer rows are
-// read twice (the second pass mostly from cache).
+// One workgroup per weight row. The row is staged in LDS with coalesced
+// 16-byte loads (the absmax is taken on the way); thread i then owns groups
+// i, i + 256, ... read back from LDS, prunes each, splits it into its n-1
+// windows, quantises them and writes them into an LDS image of the output
+// row, which leaves with 16-byte stores: row-major, or in the tiled layout of
+// the product (16-byte lane chunks of 1 KB step blocks; index words gathered
+// four steps at a time). Rows too long to stage use the register kernel
+// (groups held in registers, or read twice when longer still).
 #include "ss_device.h"
 #include "ss_kernels.h"
 
 namespace ss {
 namespace {
 
-constexpr int kGPT = 8;  // groups per thread held in registers
+constexpr int kGPT = 8;                     // groups per thread held in registers (long-row kernel)
+constexpr size_t kLdsMax = 160 * 1024;      // LDS of one CU
+
+template <typename TIn> __device__ __forceinline__ float to_f32(TIn v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
 
 template <typename TIn> struct GroupIO;
 template <> struct GroupIO<float> {
@@ -52,22 +59,27 @@ template <> struct GroupIO<uint16_t> {
 };
 
 // Keep the 2n-2 largest magnitudes of the group (equal magnitudes keep the
-// lower index); returns the bit mask of kept nonzero positions.
+// lower index): drop the smallest twice, where among equal magnitudes the
+// higher index counts as smaller. Returns the bit mask of kept nonzeros.
 template <int N>
 __device__ __forceinline__ uint32_t keep_nonzero(const float* e) {
   constexpr int W = 2 * N;
   uint32_t key[W];
-#pragma unroll
-  for (int i = 0; i < W; ++i) key[i] = mag_key_f32(e[i]);
-  uint32_t nz = 0;
+  uint32_t nonzero = 0;
 #pragma unroll
   for (int i = 0; i < W; ++i) {
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < W; ++j) rank += (j < i) ? (key[j] >= key[i]) : (j > i ? (key[j] > key[i]) : 0);
-    if (rank < W - 2 && key[i] != 0) nz |= 1u << i;
+    key[i] = mag_key_f32(e[i]);
+    nonzero |= (uint32_t)(key[i] != 0) << i;
   }
-  return nz;
+  uint32_t k1 = 0xFFFFFFFFu, b1 = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    if (key[i] <= k1) { k1 = key[i]; b1 = i; }
+  uint32_t k2 = 0xFFFFFFFFu, b2 = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    if (i != (int)b1 && key[i] <= k2) { k2 = key[i]; b2 = i; }
+  return nonzero & ~((1u << b1) | (1u << b2));
 }
 
 // Emit the n-1 windows of one group into the LDS row image: values (ES bytes
@@ -87,7 +99,8 @@ __device__ __forceinline__ void emit_group(const float* e, int64_t g, bool zero_
     claimed |= mine;
     const uint32_t own = mine >> (2 * w);
     uint32_t fill = own;  // slots: owned positions, then the lowest free ones
-    while (__builtin_popcount(fill) < 2) fill |= (~fill) & (fill + 1);
+    if (__builtin_popcount(fill) < 2) fill |= (~fill) & (fill + 1);
+    if (__builtin_popcount(fill) < 2) fill |= (~fill) & (fill + 1);
     const uint32_t i0 = __builtin_ctz(fill), i1 = __builtin_ctz(fill & (fill - 1));
     // select with compile-time indices (a runtime index would put e[] in scratch memory)
     const float c0 = e[2 * w], c1 = e[2 * w + 1], c2 = e[2 * w + 2], c3 = e[2 * w + 3];
@@ -99,28 +112,193 @@ __device__ __forceinline__ void emit_group(const float* e, int64_t g, bool zero_
     if constexpr (OUT == 2) {
       reinterpret_cast<uint32_t*>(lv)[t] = (uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16);
     } else {
-      const uint32_t c0 = zero_row ? 0u : (uint32_t)Quant<OUT == 1>::code(v0, inv);
-      const uint32_t c1 = zero_row ? 0u : (uint32_t)Quant<OUT == 1>::code(v1, inv);
-      reinterpret_cast<uint16_t*>(lv)[t] = (uint16_t)(c0 | (c1 << 8));
+      const uint32_t q0 = zero_row ? 0u : (uint32_t)Quant<OUT == 1>::code(v0, inv);
+      const uint32_t q1 = zero_row ? 0u : (uint32_t)Quant<OUT == 1>::code(v1, inv);
+      reinterpret_cast<uint16_t*>(lv)[t] = (uint16_t)(q0 | (q1 << 8));
     }
     atomicOr(&lm[t >> 3], (i0 | (i1 << 2)) << (4 * (t & 7)));
   }
 }
 
-template <typename TIn, int N, int OUT>
-__global__ __launch_bounds__(kBlock) void slide_kernel(const TIn* __restrict__ W, int64_t ldw, int64_t K,
+// Padding windows (K' rounded up to Kc): zero values, positions (0, 1).
+template <int OUT>
+__device__ __forceinline__ void emit_padding(int64_t t0, int64_t Kc, uint8_t* lv, uint32_t* lm) {
+  for (int64_t t = t0 + threadIdx.x; t < Kc / 4; t += kBlock) {
+    if constexpr (OUT == 2) reinterpret_cast<uint32_t*>(lv)[t] = 0;
+    else reinterpret_cast<uint16_t*>(lv)[t] = 0;
+    atomicOr(&lm[t >> 3], 0x4u << (4 * (t & 7)));
+  }
+}
+
+// Store the finished LDS image of one output row (after a barrier).
+// Row-major: vals + row * ldv_bytes, meta + row * ldm.
+// Tiled (k_spgemm_tiled.hip layout; ldv_bytes = padded step count KSP): a step
+// is 64 value bytes per row; chunk q (16 bytes) of the row is lane chunk q % 4
+// of step q / 4, at 16 * (row % 16 + 16 * (q % 4)) in that step's 1 KB block of
+// row block row / 16. Index words: 8-bit values have one 32-bit word per chunk,
+// and the words of steps 4g..4g+3 of one lane chunk form 16 bytes of the 1 KB
+// block g; bf16 values have 16 bits per chunk, 8 bytes per lane chunk in a
+// 512-byte block. Steps past the data are padding (zero values, index 0x4).
+template <int OUT, bool TILED>
+__device__ __forceinline__ void store_image(const uint8_t* lv, const uint32_t* lm, int64_t row, int64_t Kc,
+                                            uint8_t* __restrict__ vals, int64_t ldv_bytes, uint8_t* __restrict__ meta,
+                                            int64_t ldm) {
+  constexpr int ES = (OUT == 2) ? 2 : 1;
+  const int64_t nchunk = Kc / 2 * ES / 16;
+  if constexpr (!TILED) {
+    uint8_t* vr = vals + row * ldv_bytes;
+    uint8_t* mr = meta + row * ldm;
+    for (int64_t c = threadIdx.x; c < nchunk; c += kBlock)
+      reinterpret_cast<uint4*>(vr)[c] = reinterpret_cast<const uint4*>(lv)[c];
+    for (int64_t c = threadIdx.x; c < Kc / 8 / 16; c += kBlock)
+      reinterpret_cast<uint4*>(mr)[c] = reinterpret_cast<const uint4*>(lm)[c];
+  } else {
+    const int64_t KSP = ldv_bytes, KS4 = KSP / 4, rb = row >> 4;
+    const int r = (int)(row & 15);
+    for (int64_t q = threadIdx.x; q < KSP * 4; q += kBlock) {
+      const int64_t s = q >> 2;
+      const int lane = r + 16 * (int)(q & 3);
+      const uint4 v = q < nchunk ? reinterpret_cast<const uint4*>(lv)[q] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(vals + (rb * KSP + s) * 1024 + 16 * lane) = v;
+    }
+    for (int64_t p = threadIdx.x; p < KS4 * 4; p += kBlock) {
+      const int64_t g = p >> 2;
+      const int c = (int)(p & 3), lane = r + 16 * c;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t q = 4 * (4 * g + j) + c;  // chunk of step 4g + j
+        if constexpr (OUT == 2) w[j] = q < nchunk ? reinterpret_cast<const uint16_t*>(lm)[q] : 0x4444u;
+        else w[j] = q < nchunk ? lm[q] : 0x44444444u;
+      }
+      if constexpr (OUT == 2)
+        *reinterpret_cast<uint2*>(meta + (rb * KS4 + g) * 512 + 8 * lane) =
+            make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+      else
+        *reinterpret_cast<uint4*>(meta + (rb * KS4 + g) * 1024 + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// Rows that fit in LDS. Dynamic LDS: [row, zero-padded to G * 2n elements, rounded
+// to 16 bytes][values Kc/2 * ES][metadata Kc/8]. TILED: the grid covers the rows
+// up to the next multiple of 16 (rows past `rows` are written as zero rows) and
+// takes them in xcd_row order.
+template <typename TIn, int N, int OUT, bool TILED>
+__global__ __launch_bounds__(kBlock) void slide_lds_kernel(const TIn* __restrict__ W, int64_t ldw, int rows, int K,
+                                                           uint8_t* __restrict__ vals, int64_t ldv_bytes,
+                                                           uint8_t* __restrict__ meta, int64_t ldm, int Kc,
+                                                           float* __restrict__ scale) {
+  constexpr int ES = (OUT == 2) ? 2 : 1;
+  constexpr int EPU = 16 / (int)sizeof(TIn);      // elements per 16-byte unit
+  constexpr int GB = 2 * N * (int)sizeof(TIn);    // bytes per group
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ float red[kBlock / 64];
+  const int G = (K + 2 * N - 1) / (2 * N);
+  const int xbytes = (G * GB + 15) & ~15;
+  TIn* lx = reinterpret_cast<TIn*>(lds);
+  uint8_t* lv = lds + xbytes;
+  uint32_t* lm = reinterpret_cast<uint32_t*>(lv + Kc / 2 * ES);
+  const int row = TILED ? xcd_row(blockIdx.x, gridDim.x) : blockIdx.x;
+  const bool live = row < rows;
+  const TIn* wr = W + (int64_t)(live ? row : 0) * ldw;
+  const int tid = threadIdx.x;
+
+  for (int i = tid; i < Kc / 32; i += kBlock) lm[i] = 0;
+  // stage the row: whole 16-byte units, four loads in flight per thread
+  const int nfull = live ? K / EPU : 0;
+  float amax = 0.0f;
+  for (int i0 = 0; i0 < nfull; i0 += 4 * kBlock) {
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * kBlock + tid;
+      if (i < nfull) v[j] = reinterpret_cast<const uint4*>(wr)[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * kBlock + tid;
+      if (i < nfull) {
+        reinterpret_cast<uint4*>(lx)[i] = v[j];
+        const TIn* t = reinterpret_cast<const TIn*>(&v[j]);
+#pragma unroll
+        for (int k = 0; k < EPU; ++k) amax = fmaxf(amax, fabsf(to_f32<TIn>(t[k])));
+      }
+    }
+  }
+  // ragged end of the row and the zero padding of the last group
+  for (int e = nfull * EPU + tid; e < G * 2 * N; e += kBlock) {
+    const TIn v = (live && e < K) ? wr[e] : (TIn)0;
+    lx[e] = v;
+    amax = fmaxf(amax, fabsf(to_f32<TIn>(v)));
+  }
+  bool zero_row = false;
+  float inv = 0.0f;
+  if constexpr (OUT != 2) {
+    amax = block_max(amax, red);  // also publishes the staged row and the metadata clear
+    constexpr float Q = (OUT == 1) ? 448.0f : 127.0f;
+    zero_row = (amax == 0.0f);
+    inv = zero_row ? 0.0f : Q / amax;
+    if (tid == 0 && live) scale[row] = zero_row ? 0.0f : amax / Q;
+  } else {
+    __syncthreads();
+  }
+  for (int g = tid; g < G; g += kBlock) {
+    float e[2 * N];
+    const uint8_t* src = lds + g * GB;
+    if constexpr (GB % 16 == 0) {
+#pragma unroll
+      for (int j = 0; j < GB / 16; ++j) {
+        const uint4 u = reinterpret_cast<const uint4*>(src)[j];
+        const TIn* t = reinterpret_cast<const TIn*>(&u);
+#pragma unroll
+        for (int k = 0; k < EPU; ++k) e[j * EPU + k] = to_f32<TIn>(t[k]);
+      }
+    } else if constexpr (GB % 8 == 0) {
+      constexpr int E8 = 8 / (int)sizeof(TIn);
+#pragma unroll
+      for (int j = 0; j < GB / 8; ++j) {
+        const uint2 u = reinterpret_cast<const uint2*>(src)[j];
+        const TIn* t = reinterpret_cast<const TIn*>(&u);
+#pragma unroll
+        for (int k = 0; k < E8; ++k) e[j * E8 + k] = to_f32<TIn>(t[k]);
+      }
+    } else {
+      constexpr int E4 = 4 / (int)sizeof(TIn);
+#pragma unroll
+      for (int j = 0; j < GB / 4; ++j) {
+        const uint32_t u = reinterpret_cast<const uint32_t*>(src)[j];
+        const TIn* t = reinterpret_cast<const TIn*>(&u);
+#pragma unroll
+        for (int k = 0; k < E4; ++k) e[j * E4 + k] = to_f32<TIn>(t[k]);
+      }
+    }
+    emit_group<N, OUT>(e, g, zero_row, inv, lv, lm);
+  }
+  emit_padding<OUT>((int64_t)G * (N - 1), Kc, lv, lm);
+  __syncthreads();
+  store_image<OUT, TILED>(lv, lm, row, Kc, vals, ldv_bytes, meta, ldm);
+}
+
+// Rows too long for LDS staging. Dynamic LDS: [values Kc/2 * ES][metadata Kc/8].
+// Rows whose groups fit in the register budget (G <= 256 * kGPT) are read once;
+// longer rows are read twice (the second pass mostly from cache). TILED as in
+// slide_lds_kernel.
+template <typename TIn, int N, int OUT, bool TILED>
+__global__ __launch_bounds__(kBlock) void slide_kernel(const TIn* __restrict__ W, int64_t ldw, int64_t rows, int64_t K,
                                                        uint8_t* __restrict__ vals, int64_t ldv_bytes,
                                                        uint8_t* __restrict__ meta, int64_t ldm, int64_t Kc,
                                                        float* __restrict__ scale) {
   constexpr int ES = (OUT == 2) ? 2 : 1;
-  extern __shared__ __align__(16) uint8_t lds[];  // [Kc/2 * ES] values, then [Kc/8] metadata
+  extern __shared__ __align__(16) uint8_t lds[];
   __shared__ float red[kBlock / 64];
   uint8_t* lv = lds;
   uint32_t* lm = reinterpret_cast<uint32_t*>(lds + Kc / 2 * ES);
-  const int64_t row = blockIdx.x;
-  const TIn* wr = W + row * ldw;
+  const int64_t row = TILED ? xcd_row(blockIdx.x, gridDim.x) : blockIdx.x;
+  const bool live = row < rows;
+  const TIn* wr = W + (live ? row : 0) * ldw;
   const int tid = threadIdx.x;
-  const int64_t G = (K + 2 * N - 1) / (2 * N);
+  const int64_t G = live ? (K + 2 * N - 1) / (2 * N) : 0;
   const bool in_regs = G <= (int64_t)kBlock * kGPT;
 
   for (int64_t i = tid; i < Kc / 32; i += kBlock) lm[i] = 0;
@@ -152,7 +330,7 @@ __global__ __launch_bounds__(kBlock) void slide_kernel(const TIn* __restrict__ W
     constexpr float Q = (OUT == 1) ? 448.0f : 127.0f;
     zero_row = (amax == 0.0f);
     inv = zero_row ? 0.0f : Q / amax;
-    if (tid == 0) scale[row] = zero_row ? 0.0f : amax / Q;
+    if (tid == 0 && live) scale[row] = zero_row ? 0.0f : amax / Q;
   } else {
     __syncthreads();
   }
@@ -169,52 +347,57 @@ __global__ __launch_bounds__(kBlock) void slide_kernel(const TIn* __restrict__ W
       emit_group<N, OUT>(t, g, zero_row, inv, lv, lm);
     }
   }
-  // padding windows (K' rounded up to Kc): zero values, positions (0, 1)
-  for (int64_t t = G * (N - 1) + tid; t < Kc / 4; t += kBlock) {
-    if constexpr (OUT == 2) reinterpret_cast<uint32_t*>(lv)[t] = 0;
-    else reinterpret_cast<uint16_t*>(lv)[t] = 0;
-    atomicOr(&lm[t >> 3], 0x4u << (4 * (t & 7)));
-  }
+  emit_padding<OUT>(G * (N - 1), Kc, lv, lm);
   __syncthreads();
-  uint8_t* vr = vals + row * ldv_bytes;
-  uint8_t* mr = meta + row * ldm;
-  for (int64_t c = tid; c < Kc / 2 * ES / 16; c += kBlock)
-    reinterpret_cast<uint4*>(vr)[c] = reinterpret_cast<const uint4*>(lv)[c];
-  for (int64_t c = tid; c < Kc / 8 / 16; c += kBlock)
-    reinterpret_cast<uint4*>(mr)[c] = reinterpret_cast<const uint4*>(lm)[c];
+  store_image<OUT, TILED>(lv, lm, row, Kc, vals, ldv_bytes, meta, ldm);
 }
 
-template <typename TIn, int N>
-hipError_t launch_n(int out, const TIn* W, int64_t ldw, int64_t rows, int64_t K, void* vals, int64_t ldv_bytes,
-                    uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
-  dim3 grid((unsigned)rows), block(kBlock);
-  uint8_t* v = static_cast<uint8_t*>(vals);
-  const size_t lds = (size_t)Kc / 2 * (out == 2 ? 2 : 1) + (size_t)Kc / 8;
-  const void* fn = out == 0 ? (const void*)slide_kernel<TIn, N, 0> : out == 1 ? (const void*)slide_kernel<TIn, N, 1>
-                                                                              : (const void*)slide_kernel<TIn, N, 2>;
+template <typename TIn, int N, int OUT, bool TILED>
+hipError_t launch_one(const TIn* W, int64_t ldw, int64_t rows, int64_t K, uint8_t* v, int64_t ldv_bytes, uint8_t* meta,
+                      int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
+  constexpr int ES = (OUT == 2) ? 2 : 1;
+  const int64_t grid = TILED ? (rows + 15) / 16 * 16 : rows;
+  const int64_t G = (K + 2 * N - 1) / (2 * N);
+  const size_t image = (size_t)Kc / 2 * ES + (size_t)Kc / 8;
+  const size_t staged = (((size_t)G * 2 * N * sizeof(TIn) + 15) & ~(size_t)15) + image;
+  const bool small = staged <= kLdsMax && K < (1 << 30) && Kc < (1 << 30) && rows < (1 << 30);
+  const void* fn = small ? (const void*)slide_lds_kernel<TIn, N, OUT, TILED> : (const void*)slide_kernel<TIn, N, OUT, TILED>;
+  const size_t lds = small ? staged : image;
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  switch (out) {
-    case 0: hipLaunchKernelGGL((slide_kernel<TIn, N, 0>), grid, block, lds, st, W, ldw, K, v, ldv_bytes, meta, ldm, Kc, scale); break;
-    case 1: hipLaunchKernelGGL((slide_kernel<TIn, N, 1>), grid, block, lds, st, W, ldw, K, v, ldv_bytes, meta, ldm, Kc, scale); break;
-    default: hipLaunchKernelGGL((slide_kernel<TIn, N, 2>), grid, block, lds, st, W, ldw, K, v, ldv_bytes, meta, ldm, Kc, scale); break;
-  }
+  if (small)
+    hipLaunchKernelGGL((slide_lds_kernel<TIn, N, OUT, TILED>), dim3((unsigned)grid), dim3(kBlock), lds, st, W, ldw,
+                       (int)rows, (int)K, v, ldv_bytes, meta, ldm, (int)Kc, scale);
+  else
+    hipLaunchKernelGGL((slide_kernel<TIn, N, OUT, TILED>), dim3((unsigned)grid), dim3(kBlock), lds, st, W, ldw, rows, K,
+                       v, ldv_bytes, meta, ldm, Kc, scale);
   return hipGetLastError();
 }
 
-template <typename TIn>
+template <typename TIn, int N, bool TILED>
+hipError_t launch_n(int out, const TIn* W, int64_t ldw, int64_t rows, int64_t K, void* vals, int64_t ldv_bytes,
+                    uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
+  uint8_t* v = static_cast<uint8_t*>(vals);
+  switch (out) {
+    case 0: return launch_one<TIn, N, 0, TILED>(W, ldw, rows, K, v, ldv_bytes, meta, ldm, Kc, scale, st);
+    case 1: return launch_one<TIn, N, 1, TILED>(W, ldw, rows, K, v, ldv_bytes, meta, ldm, Kc, scale, st);
+    default: return launch_one<TIn, N, 2, TILED>(W, ldw, rows, K, v, ldv_bytes, meta, ldm, Kc, scale, st);
+  }
+}
+
+template <typename TIn, bool TILED>
 hipError_t launch_sl(int out, const TIn* W, int64_t ldw, int64_t rows, int64_t K, int n, void* vals, int64_t ldv_bytes,
                      uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
   switch (n) {
-    case 2: return launch_n<TIn, 2>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
-    case 3: return launch_n<TIn, 3>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
-    case 4: return launch_n<TIn, 4>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
-    case 5: return launch_n<TIn, 5>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
-    case 6: return launch_n<TIn, 6>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
-    case 7: return launch_n<TIn, 7>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
-    default: return launch_n<TIn, 8>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+    case 2: return launch_n<TIn, 2, TILED>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+    case 3: return launch_n<TIn, 3, TILED>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+    case 4: return launch_n<TIn, 4, TILED>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+    case 5: return launch_n<TIn, 5, TILED>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+    case 6: return launch_n<TIn, 6, TILED>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+    case 7: return launch_n<TIn, 7, TILED>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+    default: return launch_n<TIn, 8, TILED>(out, W, ldw, rows, K, vals, ldv_bytes, meta, ldm, Kc, scale, st);
   }
 }
 
@@ -223,8 +406,22 @@ hipError_t launch_sl(int out, const TIn* W, int64_t ldw, int64_t rows, int64_t K
 hipError_t launch_slide(bool in_bf16, int out, const void* W, int64_t ldw, int64_t rows, int64_t K, int n, void* vals,
                         int64_t ldv_bytes, uint8_t* meta, int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
   if (in_bf16)
-    return launch_sl<uint16_t>(out, static_cast<const uint16_t*>(W), ldw, rows, K, n, vals, ldv_bytes, meta, ldm, Kc, scale, st);
-  return launch_sl<float>(out, static_cast<const float*>(W), ldw, rows, K, n, vals, ldv_bytes, meta, ldm, Kc, scale, st);
+    return launch_sl<uint16_t, false>(out, static_cast<const uint16_t*>(W), ldw, rows, K, n, vals, ldv_bytes, meta, ldm,
+                                      Kc, scale, st);
+  return launch_sl<float, false>(out, static_cast<const float*>(W), ldw, rows, K, n, vals, ldv_bytes, meta, ldm, Kc,
+                                 scale, st);
+}
+
+hipError_t launch_slide_tiled(bool in_bf16, int out, const void* W, int64_t ldw, int64_t rows, int64_t K, int n,
+                              int64_t Kc, void* tv, uint8_t* tm, float* scale, hipStream_t st) {
+  // n = 2 is the 2:4 prune: the unit kernel of k_prune.hip writes the same bytes without staging
+  if (n == 2 && K < (1 << 30) && rows < (1 << 30))
+    return launch_prune24_tiled(in_bf16, out, W, ldw, rows, K, Kc, tv, tm, scale, st);
+  const int64_t KS = Kc * (out == 2 ? 2 : 1) / 128, KSP = (KS + 3) / 4 * 4;
+  if (in_bf16)
+    return launch_sl<uint16_t, true>(out, static_cast<const uint16_t*>(W), ldw, rows, K, n, tv, KSP, tm, 0, Kc, scale,
+                                     st);
+  return launch_sl<float, true>(out, static_cast<const float*>(W), ldw, rows, K, n, tv, KSP, tm, 0, Kc, scale, st);
 }
 
 }  // namespace ss

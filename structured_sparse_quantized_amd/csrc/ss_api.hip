@@ -242,6 +242,27 @@ ss_status ss_prune24_act_tiled(const void* X, ss_dtype x_dt, int64_t M, int64_t 
                     "ss_prune24_act_tiled launch");
 }
 
+ss_status ss_slide_decompose_tiled(const void* W, ss_dtype w_dt, int64_t rows, int64_t K, int64_t ldw, int n,
+                                   ss_dtype out_dt, void* tvals, uint8_t* tmeta, float* scale, void* stream) {
+  if (n < 2 || n > 8) return fail(SS_ERR_PATTERN, "n=%d outside 2..8", n);
+  if (w_dt != SS_F32 && w_dt != SS_BF16) return fail(SS_ERR_DTYPE, "input must be F32 or BF16");
+  if (out_dt != SS_I8 && out_dt != SS_FP8E4M3 && out_dt != SS_BF16)
+    return fail(SS_ERR_DTYPE, "output must be I8, FP8E4M3 or BF16");
+  if (rows < 0 || K < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (rows > 0x7FFFFFF0LL || K > 0x3FFFFFF0LL) return fail(SS_ERR_SHAPE, "too large");
+  if (rows == 0 || K == 0) return ok();
+  ss_status s;
+  if ((s = check_mat("input", W, rows, K, ldw, esize(w_dt))) != SS_OK) return s;
+  if (!tvals || !tmeta) return fail(SS_ERR_NULL, "tiled outputs are NULL");
+  if (!aligned16(tvals) || !aligned16(tmeta)) return fail(SS_ERR_ALIGN, "tiled outputs are not 16-byte aligned");
+  if (out_dt == SS_BF16 && scale) return fail(SS_ERR_DTYPE, "BF16 output takes no scale (pass NULL)");
+  if (out_dt != SS_BF16 && !scale) return fail(SS_ERR_NULL, "scale is NULL");
+  const int64_t Kc = ss_lifted_k(K, n);
+  return hip_status(ss::launch_slide_tiled(w_dt == SS_BF16, out_code(out_dt), W, ldw, rows, K, n, Kc, tvals, tmeta,
+                                           scale, (hipStream_t)stream),
+                    "ss_slide_decompose_tiled launch");
+}
+
 ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
                           const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
                           ss_dtype y_dt, void* Y, int64_t ldy, void* stream) {

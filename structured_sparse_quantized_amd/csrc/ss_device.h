@@ -58,6 +58,19 @@ __device__ __forceinline__ uint32_t top2_nibble(uint32_t k0, uint32_t k1, uint32
   return i0 | (i1 << 2);
 }
 
+// ---- tiled-layout row order ---------------------------------------------------
+// Workgroups are dealt to the 8 XCDs round-robin by index. Kernels that write
+// one row of the tiled operand per workgroup (or per persistent iteration i)
+// take row xcd_row(i, n) so that the 16 rows of a 16-row block, whose 16-byte
+// pieces share 128-byte lines, are written through one XCD's L2 and leave it
+// as whole lines. A bijection on [0, n): blocks of 128 indices map within
+// themselves, the tail (n % 128) maps to itself.
+__device__ __forceinline__ int xcd_row(int i, int n) {
+  if (i >= (n & ~127)) return i;
+  const int x = i & 7, j = i >> 3;
+  return ((((j >> 4) << 3) + x) << 4) + (j & 15);
+}
+
 // ---- reductions ---------------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

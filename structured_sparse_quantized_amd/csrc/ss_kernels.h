@@ -24,6 +24,12 @@ hipError_t launch_spgemm(bool side_x, int ab, int yt, int64_t R, int64_t C, int6
 hipError_t launch_prune24_act_tiled(int out, const void* X, int64_t ldx, int64_t M, int64_t K, int64_t Kc, void* tv,
                                     uint8_t* tm, float* sx, hipStream_t st);
 
+// Weight preparation written in the tiled layout: 2:4 (F32 / BF16 input) and the (2n-2):2n decomposition.
+hipError_t launch_prune24_tiled(bool in_bf16, int out, const void* W, int64_t ldw, int64_t rows, int64_t K, int64_t Kc,
+                                void* tv, uint8_t* tm, float* scale, hipStream_t st);
+hipError_t launch_slide_tiled(bool in_bf16, int out, const void* W, int64_t ldw, int64_t rows, int64_t K, int n,
+                              int64_t Kc, void* tv, uint8_t* tm, float* scale, hipStream_t st);
+
 // Tiled sparse operand and the product that reads it. es = value bytes (1: int8/fp8, 2: bf16).
 int64_t tiled_vals_bytes(int64_t rows, int64_t Kc, int es);
 int64_t tiled_meta_bytes(int64_t rows, int64_t Kc, int es);

@@ -123,6 +123,21 @@ def test_tiled_validation_statuses():
     assert P(FAKE, ss.SS_BF16, 4, 8, 8, ss.SS_BF16, FAKE, FAKE, FAKE, None) == ss.SS_ERR_DTYPE
     assert P(FAKE, ss.SS_BF16, 4, 8, 8, ss.SS_I8, None, FAKE, FAKE, None) == ss.SS_ERR_NULL
     assert P(FAKE, ss.SS_BF16, 0, 8, 8, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_OK
+    # one-pass weight preparation into the tiled layout
+    S = L.ss_slide_decompose_tiled
+    assert S(FAKE, ss.SS_F32, 4, 8, 8, 1, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_PATTERN
+    assert S(FAKE, ss.SS_F32, 4, 8, 8, 9, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_PATTERN
+    assert S(FAKE, ss.SS_I8, 4, 8, 8, 4, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_DTYPE
+    assert S(FAKE, ss.SS_F32, 4, 8, 8, 4, ss.SS_F32, FAKE, FAKE, FAKE, None) == ss.SS_ERR_DTYPE
+    assert S(FAKE, ss.SS_F32, 4, 8, 8, 4, ss.SS_I8, FAKE, FAKE, None, None) == ss.SS_ERR_NULL
+    assert S(FAKE, ss.SS_F32, 4, 8, 8, 4, ss.SS_BF16, FAKE, FAKE, FAKE, None) == ss.SS_ERR_DTYPE
+    assert S(FAKE, ss.SS_F32, 4, 8, 8, 4, ss.SS_I8, None, FAKE, FAKE, None) == ss.SS_ERR_NULL
+    assert S(FAKE, ss.SS_F32, 4, 8, 8, 4, ss.SS_I8, odd, FAKE, FAKE, None) == ss.SS_ERR_ALIGN
+    assert S(FAKE, ss.SS_F32, 4, 8, 6, 4, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
+    assert S(None, ss.SS_F32, 4, 8, 8, 4, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_NULL
+    assert S(FAKE, ss.SS_F32, -1, 8, 8, 4, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
+    assert S(FAKE, ss.SS_F32, 0, 8, 8, 4, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_OK
+    assert S(FAKE, ss.SS_F32, 4, 0, 8, 4, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_OK
     # product
     def g(side=0, M=4, N=4, Kc=256, ab=ss.SS_I8, tv=FAKE, tm=FAKE, d=FAKE, ldd=256, sx=FAKE, sw=FAKE,
           y=ss.SS_BF16, Y=FAKE, ldy=8):

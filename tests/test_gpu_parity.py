@@ -109,7 +109,7 @@ def test_prune24(ss, kind, out, shape, ties):
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
 @pytest.mark.parametrize("out", ["i8", "fp8", "bf16"])
 @pytest.mark.parametrize("n", [2, 3, 4, 5, 8])
-@pytest.mark.parametrize("shape", [(1, 8), (5, 40), (130, 520), (64, 3584), (3, 18944)])
+@pytest.mark.parametrize("shape", [(1, 8), (5, 40), (130, 520), (64, 3584), (3, 18944), (2, 60000)])
 def test_slide_decompose(ss, kind, out, n, shape):
     rows, K = shape
     w = _w(11 + rows + K + n, rows, K, kind, ties=(n == 4))

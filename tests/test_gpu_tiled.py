@@ -268,3 +268,62 @@ def test_activation_sparse_layer_one_pass(ss, out):
     Y = host(ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, K, tv, tm, wd, sx, sw, "f32"))
     exp = oracle.spgemm("X", ov, om, ow, K, out, osx, osw, "f32")
     assert rel_fro(Y, exp) <= TOL
+
+
+SLIDE_TILED_SHAPES = [(1, 8), (5, 40), (3, 1001), (16, 512), (130, 520), (257, 1000), (3, 18944), (2, 60000)]
+
+
+def _w_ties(seed, rows, K, kind):
+    """Weights N(0, 0.02^2) with many equal magnitudes (ties), an all-zero row and a half-zero row."""
+    rng = np.random.default_rng(seed)
+    w = synth.normal_f32(rng, (rows, K), 0.02)
+    w[:, ::2] = np.round(w[:, ::2] * 100) / 100
+    K4 = K // 4 * 4
+    w[:, 1:K4:4] = -w[:, 0:K4:4]
+    if rows > 2:
+        w[2] = 0
+        w[1, : K // 2] = 0
+    return synth.f32_to_bf16_bits(w) if kind == "bf16" else w
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("out", ["i8", "fp8", "bf16"])
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("shape", SLIDE_TILED_SHAPES)
+def test_slide_decompose_tiled(ss, kind, out, n, shape):
+    """One-pass weight preparation into the tiled layout: the oracle's decomposed operand re-indexed, and the
+    same bytes as ss_slide_decompose followed by ss_pack_sparse. Rows past 128 exercise the XCD row order."""
+    rows, K = shape
+    w = _w_ties(rows * 13 + K + n, rows, K, kind)
+    # rows start 16-byte aligned: ragged K lives in a wider buffer
+    ldk = -(-K // 8) * 8
+    wp = np.zeros((rows, ldk), w.dtype)
+    wp[:, :K] = w
+    wd = (dev_bf16(wp) if kind == "bf16" else dev_f32(wp))[:, :K]
+    tv, tm, sc = ss.slide_decompose_tiled(wd, n, out)
+    ov, om, osc = oracle.slide_decompose(w, n, out)
+    es = 2 if out == "bf16" else 1
+    ev, em = tile_ref(np.ascontiguousarray(ov).view(np.uint8).reshape(rows, -1), om, es)
+    assert np.array_equal(host(tm), em)
+    assert np.array_equal(host(tv), ev)
+    if out == "bf16":
+        assert sc is None
+    else:
+        assert np.array_equal(host(sc), osc)
+    pv, pm, psc = ss.slide_decompose(wd, n, out)
+    rv, rm = ss.pack_sparse(pv, pm)
+    assert np.array_equal(host(rv), host(tv)) and np.array_equal(host(rm), host(tm))
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_weight_sparse_path_one_pass(ss, n):
+    """One-pass weight preparation + fused quant/lift + tiled product, INT8 bit-exact against the oracle."""
+    M, N, K = 150, 260, 1000
+    X, W, _ = synth.workload(91 + n, M, N, K, x_kind="bf16", outlier_frac=0.01)
+    tv, tm, sw = ss.slide_decompose_tiled(dev_f32(W), n, "i8")
+    xq, sx = ss.quant_lift_act(dev_bf16(X), n, "i8")
+    Kc = ss.lifted_k(K, n)
+    Y = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, xq, sx, sw, "bf16"))
+    ov, om, osw = oracle.slide_decompose(W, n, "i8")
+    oxq, osx = oracle.quant_lift_act(X, n, "i8")
+    assert np.array_equal(Y, oracle.spgemm("W", ov, om, oxq, Kc, "i8", osx, osw, "bf16"))
