@@ -15,6 +15,8 @@
 #include "ss_device.h"
 #include "ss_kernels.h"
 
+#include <algorithm>
+
 namespace ss {
 namespace {
 
@@ -82,11 +84,133 @@ __device__ __forceinline__ uint32_t keep_nonzero(const float* e) {
   return nonzero & ~((1u << b1) | (1u << b2));
 }
 
+// The same mask, fast when there is no tie at the boundary: take the two
+// smallest magnitudes v1 <= v2 as values (a running min and median), then the
+// elements with |w| <= v2. Exactly two such elements are the dropped pair, and
+// every other element is then larger than v2 >= 0, so nonzero. Three or more
+// (equal magnitudes at v2, which includes three or more zeros) fall back to
+// keep_nonzero.
+template <int N>
+__device__ __forceinline__ uint32_t keep_nonzero_fast(const float* e) {
+  constexpr int W = 2 * N;
+  float m1 = fminf(fabsf(e[0]), fabsf(e[1])), m2 = fmaxf(fabsf(e[0]), fabsf(e[1]));
+#pragma unroll
+  for (int i = 2; i < W; ++i) {
+    const float a = fabsf(e[i]);
+    m2 = __builtin_amdgcn_fmed3f(m1, m2, a);
+    m1 = fminf(m1, a);
+  }
+  uint32_t le = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) le |= (fabsf(e[i]) <= m2) ? (1u << i) : 0u;
+  if (__builtin_popcount(le) == 2) return ~le & ((1u << W) - 1);
+  return keep_nonzero<N>(e);
+}
+
+// Greedy window assignment as a function of the kept-nonzero mask, for n = 3
+// and n = 4 with 8-bit codes: `sel` holds the byte selectors (v_perm, over the
+// group's codes packed 4 to a word; 0x0C gives a zero byte) of the two slots of
+// windows 0 and 1, `aux` those of window 2 (bits 0-15) and the index nibbles of
+// all windows (bits 16-27). Built at compile time from the same rule as
+// emit_group.
+template <int N> struct SlideTable { uint32_t sel[1 << (2 * N)], aux[1 << (2 * N)]; };
+template <int N> constexpr SlideTable<N> make_slide_table() {
+  SlideTable<N> t{};
+  for (uint32_t nz = 0; nz < (1u << (2 * N)); ++nz) {
+    uint32_t claimed = 0, sel = 0, aux = 0, mb = 0;
+    for (int w = 0; w < N - 1; ++w) {
+      uint32_t cand = nz & ~claimed & (0xFu << (2 * w));
+      const uint32_t m1 = cand & (0u - cand);
+      cand &= ~m1;
+      const uint32_t m2 = cand & (0u - cand);
+      const uint32_t mine = m1 | m2;
+      claimed |= mine;
+      const uint32_t own = mine >> (2 * w);
+      uint32_t fill = own;
+      for (int k = 0; k < 2; ++k) {
+        int pc = 0;
+        for (int b = 0; b < 4; ++b) pc += (int)((fill >> b) & 1u);
+        if (pc < 2) fill |= (~fill) & (fill + 1);
+      }
+      int i0 = 0;
+      while (!((fill >> i0) & 1u)) ++i0;
+      int i1 = i0 + 1;
+      while (!((fill >> i1) & 1u)) ++i1;
+      const uint32_t s0 = ((own >> i0) & 1u) ? (uint32_t)(2 * w + i0) : 0x0Cu;
+      const uint32_t s1 = ((own >> i1) & 1u) ? (uint32_t)(2 * w + i1) : 0x0Cu;
+      if (w < 2) sel |= (s0 | (s1 << 8)) << (16 * w);
+      else aux |= s0 | (s1 << 8);
+      mb |= (uint32_t)(i0 | (i1 << 2)) << (4 * w);
+    }
+    if (N < 4) aux |= 0x0C0Cu;
+    t.sel[nz] = sel;
+    t.aux[nz] = aux | (mb << 16);
+  }
+  return t;
+}
+__constant__ SlideTable<3> kSlideTab3 = make_slide_table<3>();
+__constant__ SlideTable<4> kSlideTab4 = make_slide_table<4>();
+
+template <int N> constexpr bool kTablePath = (N == 3 || N == 4);
+
+// Copy the table of pattern n into LDS (uint2 entries: sel, aux).
+template <int N>
+__device__ __forceinline__ void load_slide_table(uint2* tab) {
+  if constexpr (N == 3) {
+    for (int i = threadIdx.x; i < 64; i += kBlock) tab[i] = make_uint2(kSlideTab3.sel[i], kSlideTab3.aux[i]);
+  } else if constexpr (N == 4) {
+    for (int i = threadIdx.x; i < 256; i += kBlock) tab[i] = make_uint2(kSlideTab4.sel[i], kSlideTab4.aux[i]);
+  }
+}
+
+// 8-bit code of one value with the row's inv (as Quant::code): INT8 rounds by
+// adding 1.5 * 2^23, which leaves rint(t) in the low mantissa bits (t is
+// clamped to +-127 first; both are integers, so clamping before or after the
+// rounding is the same). FP8 uses the conversion unit.
+template <int OUT>
+__device__ __forceinline__ uint32_t code_bits(float v, float inv) {
+  const float t = __fmul_rn(v, inv);
+  if constexpr (OUT == 1) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(t, -448.0f, 448.0f), 0.0f, 0, false) & 0xFFu;
+  } else {
+    return __float_as_uint(__builtin_amdgcn_fmed3f(t, -127.0f, 127.0f) + 12582912.0f) & 0xFFu;
+  }
+}
+
+// Table path (n = 3, 4; 8-bit codes): codes of all 2n elements, two v_perm for
+// the slot bytes, one or two LDS ORs for the index nibbles. Slots that do not
+// own a nonzero select a zero byte, so a zero row needs no special case.
+template <int N, int OUT>
+__device__ __forceinline__ void emit_group_tab(const float* e, int g, float inv, const uint2* tab, uint8_t* lv,
+                                               uint32_t* lm) {
+  const uint32_t nz = keep_nonzero_fast<N>(e);
+  uint32_t c[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 2 * N; ++i) c[i >> 2] |= code_bits<OUT>(e[i], inv) << (8 * (i & 3));
+  const uint2 en = tab[nz];
+  const uint32_t v01 = __builtin_amdgcn_perm(c[1], c[0], en.x);
+  constexpr int B = 2 * (N - 1);  // value bytes per group
+  if constexpr (N == 3) {
+    reinterpret_cast<uint32_t*>(lv)[g] = v01;
+  } else {
+    const uint32_t v2 = __builtin_amdgcn_perm(c[1], c[0], (en.y & 0xFFFFu) | 0x0C0C0000u);
+    uint16_t* p = reinterpret_cast<uint16_t*>(lv + B * g);
+    p[0] = (uint16_t)v01;
+    p[1] = (uint16_t)(v01 >> 16);
+    p[2] = (uint16_t)v2;
+  }
+  constexpr int MB = 4 * (N - 1);  // index bits per group
+  const uint32_t mb = en.y >> 16;
+  const int bit = MB * g, sh = bit & 31;
+  atomicOr(&lm[bit >> 5], mb << sh);
+  if (sh > 32 - MB) atomicOr(&lm[(bit >> 5) + 1], mb >> (32 - sh));
+}
+
 // Emit the n-1 windows of one group into the LDS row image: values (ES bytes
 // each) at window slot 2t, 2t+1 and the nibble of window t into metadata word t/8.
 template <int N, int OUT>
 __device__ __forceinline__ void emit_group(const float* e, int64_t g, bool zero_row, float inv, uint8_t* lv, uint32_t* lm) {
-  const uint32_t nz = keep_nonzero<N>(e);
+  const uint32_t nz = keep_nonzero_fast<N>(e);
   uint32_t claimed = 0;
 #pragma unroll
   for (int w = 0; w < N - 1; ++w) {
@@ -181,10 +305,14 @@ __device__ __forceinline__ void store_image(const uint8_t* lv, const uint32_t* l
 }
 
 // Rows that fit in LDS. Dynamic LDS: [row, zero-padded to G * 2n elements, rounded
-// to 16 bytes][values Kc/2 * ES][metadata Kc/8]. TILED: the grid covers the rows
-// up to the next multiple of 16 (rows past `rows` are written as zero rows) and
-// takes them in xcd_row order.
-template <typename TIn, int N, int OUT, bool TILED>
+// to 16 bytes][values Kc/2 * ES][metadata Kc/8]. Persistent: iteration i of a
+// workgroup takes row blockIdx.x + i * gridDim.x (TILED: in xcd_row order over the
+// rows up to the next multiple of 16, those past `rows` written as zero rows).
+// UPT > 0: the row's 16-byte units (K / EPU <= UPT * kBlock) are prefetched into
+// registers one row ahead, so the next row streams in while this one is pruned
+// and stored (the barriers inside the loop order LDS only and do not wait for it).
+// UPT = 0: each row is loaded when it is staged.
+template <typename TIn, int N, int OUT, bool TILED, int UPT>
 __global__ __launch_bounds__(kBlock) void slide_lds_kernel(const TIn* __restrict__ W, int64_t ldw, int rows, int K,
                                                            uint8_t* __restrict__ vals, int64_t ldv_bytes,
                                                            uint8_t* __restrict__ meta, int64_t ldm, int Kc,
@@ -192,92 +320,132 @@ __global__ __launch_bounds__(kBlock) void slide_lds_kernel(const TIn* __restrict
   constexpr int ES = (OUT == 2) ? 2 : 1;
   constexpr int EPU = 16 / (int)sizeof(TIn);      // elements per 16-byte unit
   constexpr int GB = 2 * N * (int)sizeof(TIn);    // bytes per group
+  constexpr bool TAB = kTablePath<N> && OUT != 2;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ float red[kBlock / 64];
+  __shared__ uint2 tab[TAB ? (1 << (2 * N)) : 1];
   const int G = (K + 2 * N - 1) / (2 * N);
   const int xbytes = (G * GB + 15) & ~15;
   TIn* lx = reinterpret_cast<TIn*>(lds);
   uint8_t* lv = lds + xbytes;
   uint32_t* lm = reinterpret_cast<uint32_t*>(lv + Kc / 2 * ES);
-  const int row = TILED ? xcd_row(blockIdx.x, gridDim.x) : blockIdx.x;
-  const bool live = row < rows;
-  const TIn* wr = W + (int64_t)(live ? row : 0) * ldw;
   const int tid = threadIdx.x;
+  const int nrows = TILED ? (rows + 15) / 16 * 16 : rows;
+  const int nfull = K / EPU;  // whole 16-byte units of a row
+  auto row_of = [&](int it) { return TILED ? xcd_row(it, nrows) : it; };
+  if constexpr (TAB) load_slide_table<N>(tab);  // published by the first barrier below
 
-  for (int i = tid; i < Kc / 32; i += kBlock) lm[i] = 0;
-  // stage the row: whole 16-byte units, four loads in flight per thread
-  const int nfull = live ? K / EPU : 0;
-  float amax = 0.0f;
-  for (int i0 = 0; i0 < nfull; i0 += 4 * kBlock) {
-    uint4 v[4];
+  uint4 pre[UPT > 0 ? UPT : 1];
+  auto fetch = [&](int r) {
+    const TIn* wr = W + (int64_t)(r < rows ? r : 0) * ldw;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = i0 + j * kBlock + tid;
-      if (i < nfull) v[j] = reinterpret_cast<const uint4*>(wr)[i];
+    for (int j = 0; j < UPT; ++j) {
+      const int i = j * kBlock + tid;
+      pre[j] = (i < nfull && r < rows) ? reinterpret_cast<const uint4*>(wr)[i] : make_uint4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = i0 + j * kBlock + tid;
-      if (i < nfull) {
-        reinterpret_cast<uint4*>(lx)[i] = v[j];
-        const TIn* t = reinterpret_cast<const TIn*>(&v[j]);
-#pragma unroll
-        for (int k = 0; k < EPU; ++k) amax = fmaxf(amax, fabsf(to_f32<TIn>(t[k])));
-      }
-    }
+  };
+  if constexpr (UPT > 0) {
+    if ((int)blockIdx.x < nrows) fetch(row_of(blockIdx.x));
   }
-  // ragged end of the row and the zero padding of the last group
-  for (int e = nfull * EPU + tid; e < G * 2 * N; e += kBlock) {
-    const TIn v = (live && e < K) ? wr[e] : (TIn)0;
-    lx[e] = v;
-    amax = fmaxf(amax, fabsf(to_f32<TIn>(v)));
-  }
-  bool zero_row = false;
-  float inv = 0.0f;
-  if constexpr (OUT != 2) {
-    amax = block_max(amax, red);  // also publishes the staged row and the metadata clear
-    constexpr float Q = (OUT == 1) ? 448.0f : 127.0f;
-    zero_row = (amax == 0.0f);
-    inv = zero_row ? 0.0f : Q / amax;
-    if (tid == 0 && live) scale[row] = zero_row ? 0.0f : amax / Q;
-  } else {
-    __syncthreads();
-  }
-  for (int g = tid; g < G; g += kBlock) {
-    float e[2 * N];
-    const uint8_t* src = lds + g * GB;
-    if constexpr (GB % 16 == 0) {
+  for (int it = blockIdx.x; it < nrows; it += gridDim.x) {
+    const int row = row_of(it);
+    const bool live = row < rows;
+    const TIn* wr = W + (int64_t)(live ? row : 0) * ldw;
+    float amax = 0.0f;
+    auto stage = [&](const uint4& v, int i) {
+      reinterpret_cast<uint4*>(lx)[i] = v;
+      const TIn* t = reinterpret_cast<const TIn*>(&v);
 #pragma unroll
-      for (int j = 0; j < GB / 16; ++j) {
-        const uint4 u = reinterpret_cast<const uint4*>(src)[j];
-        const TIn* t = reinterpret_cast<const TIn*>(&u);
+      for (int k = 0; k < EPU; ++k) amax = fmaxf(amax, fabsf(to_f32<TIn>(t[k])));
+    };
+    if constexpr (UPT > 0) {
 #pragma unroll
-        for (int k = 0; k < EPU; ++k) e[j * EPU + k] = to_f32<TIn>(t[k]);
-      }
-    } else if constexpr (GB % 8 == 0) {
-      constexpr int E8 = 8 / (int)sizeof(TIn);
-#pragma unroll
-      for (int j = 0; j < GB / 8; ++j) {
-        const uint2 u = reinterpret_cast<const uint2*>(src)[j];
-        const TIn* t = reinterpret_cast<const TIn*>(&u);
-#pragma unroll
-        for (int k = 0; k < E8; ++k) e[j * E8 + k] = to_f32<TIn>(t[k]);
-      }
+      for (int j = 0; j < UPT; ++j)
+        if (j * kBlock + tid < nfull) stage(pre[j], j * kBlock + tid);
     } else {
-      constexpr int E4 = 4 / (int)sizeof(TIn);
+      for (int i0 = 0; i0 < nfull; i0 += 4 * kBlock) {  // four loads in flight per thread (zeros past `rows`)
+        uint4 v[4];
 #pragma unroll
-      for (int j = 0; j < GB / 4; ++j) {
-        const uint32_t u = reinterpret_cast<const uint32_t*>(src)[j];
-        const TIn* t = reinterpret_cast<const TIn*>(&u);
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + j * kBlock + tid;
+          v[j] = (i < nfull && live) ? reinterpret_cast<const uint4*>(wr)[i] : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
-        for (int k = 0; k < E4; ++k) e[j * E4 + k] = to_f32<TIn>(t[k]);
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + j * kBlock + tid;
+          if (i < nfull) stage(v[j], i);
+        }
       }
     }
-    emit_group<N, OUT>(e, g, zero_row, inv, lv, lm);
+    // ragged end of the row and the zero padding of the last group
+    for (int e = nfull * EPU + tid; e < G * 2 * N; e += kBlock) {
+      const TIn v = (live && e < K) ? wr[e] : (TIn)0;
+      lx[e] = v;
+      amax = fmaxf(amax, fabsf(to_f32<TIn>(v)));
+    }
+    for (int i = tid; i < Kc / 32; i += kBlock) lm[i] = 0;
+    if constexpr (UPT > 0) {
+      if (it + (int)gridDim.x < nrows) fetch(row_of(it + gridDim.x));
+    }
+    bool zero_row = false;
+    float inv = 0.0f;
+    if constexpr (OUT != 2) {
+      amax = block_max(amax, red);  // also publishes the staged row and the metadata clear
+      constexpr float Q = (OUT == 1) ? 448.0f : 127.0f;
+      zero_row = (amax == 0.0f);
+      inv = zero_row ? 0.0f : Q / amax;
+      if (tid == 0 && live) scale[row] = zero_row ? 0.0f : amax / Q;
+    } else {
+      lds_barrier();
+    }
+    for (int g = tid; g < G; g += kBlock) {
+      float e[2 * N];
+      const uint8_t* src = lds + g * GB;
+      if constexpr (GB % 16 == 0) {
+        // whole 16-byte LDS reads (ds_read_b128): lanes 32 or 64 bytes apart conflict at most 2-way
+        typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+        const v4u* s4 = reinterpret_cast<const v4u*>(lds) + g * (GB / 16);
+#pragma unroll
+        for (int j = 0; j < GB / 16; ++j) {
+          const v4u u = __builtin_nontemporal_load(s4 + j);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int k = 0; k < EPU; ++k) {
+            if constexpr (sizeof(TIn) == 4) e[j * EPU + k] = __uint_as_float(w[k]);
+            else e[j * EPU + k] = bf16_to_f32((uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu)));
+          }
+        }
+      } else if constexpr (GB % 8 == 0) {
+        constexpr int E8 = 8 / (int)sizeof(TIn);
+        const uint2* s2 = reinterpret_cast<const uint2*>(lds) + g * (GB / 8);
+#pragma unroll
+        for (int j = 0; j < GB / 8; ++j) {
+          const uint2 u = s2[j];
+          const uint32_t w[2] = {u.x, u.y};
+#pragma unroll
+          for (int k = 0; k < E8; ++k) {
+            if constexpr (sizeof(TIn) == 4) e[j * E8 + k] = __uint_as_float(w[k]);
+            else e[j * E8 + k] = bf16_to_f32((uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFFu)));
+          }
+        }
+      } else {
+        constexpr int E4 = 4 / (int)sizeof(TIn);
+#pragma unroll
+        for (int j = 0; j < GB / 4; ++j) {
+          const uint32_t u = reinterpret_cast<const uint32_t*>(src)[j];
+          const TIn* t = reinterpret_cast<const TIn*>(&u);
+#pragma unroll
+          for (int k = 0; k < E4; ++k) e[j * E4 + k] = to_f32<TIn>(t[k]);
+        }
+      }
+      if constexpr (TAB) emit_group_tab<N, OUT>(e, g, inv, tab, lv, lm);
+      else emit_group<N, OUT>(e, g, zero_row, inv, lv, lm);
+    }
+    emit_padding<OUT>((int64_t)G * (N - 1), Kc, lv, lm);
+    lds_barrier();
+    store_image<OUT, TILED>(lv, lm, row, Kc, vals, ldv_bytes, meta, ldm);
+    lds_barrier();  // the next row overwrites the LDS image
   }
-  emit_padding<OUT>((int64_t)G * (N - 1), Kc, lv, lm);
-  __syncthreads();
-  store_image<OUT, TILED>(lv, lm, row, Kc, vals, ldv_bytes, meta, ldm);
 }
 
 // Rows too long for LDS staging. Dynamic LDS: [values Kc/2 * ES][metadata Kc/8].
@@ -332,7 +500,7 @@ __global__ __launch_bounds__(kBlock) void slide_kernel(const TIn* __restrict__ W
     inv = zero_row ? 0.0f : Q / amax;
     if (tid == 0 && live) scale[row] = zero_row ? 0.0f : amax / Q;
   } else {
-    __syncthreads();
+    lds_barrier();
   }
   if (in_regs) {
 #pragma unroll
@@ -348,7 +516,7 @@ __global__ __launch_bounds__(kBlock) void slide_kernel(const TIn* __restrict__ W
     }
   }
   emit_padding<OUT>(G * (N - 1), Kc, lv, lm);
-  __syncthreads();
+  lds_barrier();
   store_image<OUT, TILED>(lv, lm, row, Kc, vals, ldv_bytes, meta, ldm);
 }
 
@@ -356,24 +524,43 @@ template <typename TIn, int N, int OUT, bool TILED>
 hipError_t launch_one(const TIn* W, int64_t ldw, int64_t rows, int64_t K, uint8_t* v, int64_t ldv_bytes, uint8_t* meta,
                       int64_t ldm, int64_t Kc, float* scale, hipStream_t st) {
   constexpr int ES = (OUT == 2) ? 2 : 1;
-  const int64_t grid = TILED ? (rows + 15) / 16 * 16 : rows;
+  const int64_t nrows = TILED ? (rows + 15) / 16 * 16 : rows;
   const int64_t G = (K + 2 * N - 1) / (2 * N);
   const size_t image = (size_t)Kc / 2 * ES + (size_t)Kc / 8;
   const size_t staged = (((size_t)G * 2 * N * sizeof(TIn) + 15) & ~(size_t)15) + image;
-  const bool small = staged <= kLdsMax && K < (1 << 30) && Kc < (1 << 30) && rows < (1 << 30);
-  const void* fn = small ? (const void*)slide_lds_kernel<TIn, N, OUT, TILED> : (const void*)slide_kernel<TIn, N, OUT, TILED>;
-  const size_t lds = small ? staged : image;
-  if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  // the staged kernel also holds up to 2 KB of static LDS (reduction slots, window table)
+  const bool small = staged + 4096 <= kLdsMax && K < (1 << 30) && Kc < (1 << 30) && rows < (1 << 30);
+  if (!small) {
+    const void* fn = (const void*)slide_kernel<TIn, N, OUT, TILED>;
+    if (image > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)image);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((slide_kernel<TIn, N, OUT, TILED>), dim3((unsigned)nrows), dim3(kBlock), image, st, W, ldw, rows,
+                       K, v, ldv_bytes, meta, ldm, Kc, scale);
+    return hipGetLastError();
   }
-  if (small)
-    hipLaunchKernelGGL((slide_lds_kernel<TIn, N, OUT, TILED>), dim3((unsigned)grid), dim3(kBlock), lds, st, W, ldw,
-                       (int)rows, (int)K, v, ldv_bytes, meta, ldm, (int)Kc, scale);
-  else
-    hipLaunchKernelGGL((slide_kernel<TIn, N, OUT, TILED>), dim3((unsigned)grid), dim3(kBlock), lds, st, W, ldw, rows, K,
-                       v, ldv_bytes, meta, ldm, Kc, scale);
-  return hipGetLastError();
+  // persistent grid: the workgroups that are resident at once (registers and LDS), at most 8
+  // per CU; a multiple of 8 when it is smaller than the row count (xcd_row order)
+  const int64_t units = K * (int64_t)sizeof(TIn) / 16;
+  auto go = [&](auto kern) -> hipError_t {
+    if (staged > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)staged);
+      if (e != hipSuccess) return e;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, staged) != hipSuccess || per_cu < 1) per_cu = 1;
+    per_cu = std::min(per_cu, 8);
+    const unsigned grid = (unsigned)std::min<int64_t>(nrows, (int64_t)num_cus_p() * per_cu);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), staged, st, W, ldw, (int)rows, (int)K, v, ldv_bytes, meta, ldm,
+                       (int)Kc, scale);
+    return hipGetLastError();
+  };
+  if (units <= 1 * kBlock) return go(slide_lds_kernel<TIn, N, OUT, TILED, 1>);
+  if (units <= 2 * kBlock) return go(slide_lds_kernel<TIn, N, OUT, TILED, 2>);
+  if (units <= 4 * kBlock) return go(slide_lds_kernel<TIn, N, OUT, TILED, 4>);
+  if (units <= 8 * kBlock) return go(slide_lds_kernel<TIn, N, OUT, TILED, 8>);
+  return go(slide_lds_kernel<TIn, N, OUT, TILED, 0>);
 }
 
 template <typename TIn, int N, bool TILED>

@@ -78,16 +78,26 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS accesses only. A full __syncthreads() also
+// waits for every global load in flight (vmcnt(0)), which would stall a row
+// prefetched into registers before the barrier; this one waits for LDS
+// operations (lgkmcnt) alone. Use it where the barrier guards LDS data only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Block-wide max over kBlock threads; every thread gets the result.
 __device__ __forceinline__ float block_max(float v, float* red /* >= kBlock/64 floats */) {
   v = wave_max(v);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) red[wid] = v;
-  __syncthreads();
+  lds_barrier();
   float r = red[0];
 #pragma unroll
   for (int i = 1; i < kBlock / 64; ++i) r = fmaxf(r, red[i]);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 

@@ -5,6 +5,9 @@
 
 namespace ss {
 
+// Compute units of the current device (cached).
+int num_cus_p();
+
 hipError_t launch_quant_lift(bool x_bf16, bool fp8, const void* X, int64_t ldx, int64_t M, int64_t K, int n,
                              void* Xq, int64_t ldq, int64_t Kc, float* sx, hipStream_t st);
 
