@@ -48,9 +48,9 @@ __device__ __forceinline__ uint32_t prune_unit(const Unit<TIn>& u, bool zero_row
   for (int g = 0; g < 4; ++g) {
     const uint32_t nib = top2_nibble(u.key(4 * g), u.key(4 * g + 1), u.key(4 * g + 2), u.key(4 * g + 3));
     meta |= nib << (4 * g);
-    // select among compile-time indices (a runtime index would put the unit in scratch memory)
     const float c0 = u.val(4 * g), c1 = u.val(4 * g + 1), c2 = u.val(4 * g + 2), c3 = u.val(4 * g + 3);
     const uint32_t i0 = nib & 3, i1 = nib >> 2;  // i0 < i1
+    // select among compile-time indices (a runtime index would put the unit in scratch memory)
     const float v0 = i0 == 0 ? c0 : i0 == 1 ? c1 : c2;
     const float v1 = i1 == 1 ? c1 : i1 == 2 ? c2 : c3;
     kv[2 * g] = (v0 == 0.0f) ? 0.0f : v0;  // zeros are stored as +0
@@ -60,12 +60,8 @@ __device__ __forceinline__ uint32_t prune_unit(const Unit<TIn>& u, bool zero_row
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(kv[2 * i]) | ((uint32_t)f32_to_bf16(kv[2 * i + 1]) << 16);
   } else {
-    w[0] = w[1] = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c = zero_row ? 0u : (uint32_t)Quant<OUT == 1>::code(kv[i], inv);
-      w[i >> 2] |= c << (8 * (i & 3));
-    }
+    w[0] = zero_row ? 0u : Quant<OUT == 1>::pack4(kv[0], kv[1], kv[2], kv[3], inv);
+    w[1] = zero_row ? 0u : Quant<OUT == 1>::pack4(kv[4], kv[5], kv[6], kv[7], inv);
   }
   return meta;
 }

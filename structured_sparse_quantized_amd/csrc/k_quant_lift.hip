@@ -84,6 +84,10 @@ __global__ __launch_bounds__(kBlock, (PIPE || VPT > 4) ? 2 : (VPT > 2 ? 4 : 8)) 
     const float inv = zero_row ? 0.0f : Qz::Q / amax;
     if (tid == 0) sx[r] = zero_row ? 0.0f : amax / Qz::Q;
     auto code = [&](float f) -> uint32_t { return zero_row ? 0u : (uint32_t)Qz::code(f, inv); };
+    // four codes of vector i from element e0 (same bytes as code())
+    auto code4 = [&](const uint4& v, int e0) -> uint32_t {
+      return zero_row ? 0u : Qz::pack4(V::get(v, e0), V::get(v, e0 + 1), V::get(v, e0 + 2), V::get(v, e0 + 3), inv);
+    };
     uint8_t* qr = Xq + (int64_t)r * ldq;
 
     if constexpr (N == 2) {
@@ -93,12 +97,12 @@ __global__ __launch_bounds__(kBlock, (PIPE || VPT > 4) ? 2 : (VPT > 2 ? 4 : 8)) 
         if (vi < nvec) {
           if constexpr (E == 8) {
             uint2 o;
-            o.x = code(V::get(cur[i], 0)) | code(V::get(cur[i], 1)) << 8 | code(V::get(cur[i], 2)) << 16 | code(V::get(cur[i], 3)) << 24;
-            o.y = code(V::get(cur[i], 4)) | code(V::get(cur[i], 5)) << 8 | code(V::get(cur[i], 6)) << 16 | code(V::get(cur[i], 7)) << 24;
+            o.x = code4(cur[i], 0);
+            o.y = code4(cur[i], 4);
             *reinterpret_cast<uint2*>(qr + vi * 8) = o;
           } else {
             *reinterpret_cast<uint32_t*>(qr + vi * 4) =
-                code(V::get(cur[i], 0)) | code(V::get(cur[i], 1)) << 8 | code(V::get(cur[i], 2)) << 16 | code(V::get(cur[i], 3)) << 24;
+                code4(cur[i], 0);
           }
         }
       }
@@ -111,18 +115,18 @@ __global__ __launch_bounds__(kBlock, (PIPE || VPT > 4) ? 2 : (VPT > 2 ? 4 : 8)) 
         if (vi < nvec) {
           if constexpr (E == 8) {
             uint2 o;
-            o.x = code(V::get(cur[i], 0)) | code(V::get(cur[i], 1)) << 8 | code(V::get(cur[i], 2)) << 16 | code(V::get(cur[i], 3)) << 24;
-            o.y = code(V::get(cur[i], 4)) | code(V::get(cur[i], 5)) << 8 | code(V::get(cur[i], 6)) << 16 | code(V::get(cur[i], 7)) << 24;
+            o.x = code4(cur[i], 0);
+            o.y = code4(cur[i], 4);
             *reinterpret_cast<uint2*>(lds + vi * 8) = o;
           } else {
             *reinterpret_cast<uint32_t*>(lds + vi * 4) =
-                code(V::get(cur[i], 0)) | code(V::get(cur[i], 1)) << 8 | code(V::get(cur[i], 2)) << 16 | code(V::get(cur[i], 3)) << 24;
+                code4(cur[i], 0);
           }
         }
       }
       if (tail0 + tid < K) lds[tail0 + tid] = (uint8_t)code(ctail);
       for (int c = K + tid; c < Kpad + 4; c += kBlock) lds[c] = 0;
-      __syncthreads();
+      lds_barrier();
       const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds);
       for (int c = tid; c < Kc / 16; c += kBlock) {
         uint32_t w4[4];
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kBlock, (PIPE || VPT > 4) ? 2 : (VPT > 2 ? 4 : 8)) 
         }
         *reinterpret_cast<uint4*>(qr + c * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       }
-      __syncthreads();  // the LDS row is rewritten for the next row
+      lds_barrier();  // the LDS row is rewritten for the next row
     }
     if constexpr (PIPE) {
 #pragma unroll

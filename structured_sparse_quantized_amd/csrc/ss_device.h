@@ -40,6 +40,23 @@ template <bool FP8> struct Quant {
       return (uint8_t)(int8_t)(int)r;
     }
   }
+  // Four codes packed little-endian, the same bytes as code(). INT8: clamp to
+  // +-127 (integers, so clamping before rounding is the same), then add
+  // 1.5 * 2^23: the sum's low mantissa bits hold rint(t) in two's complement.
+  // FP8: two conversions of two values each. A zero row (inv = 0) gives zero
+  // INT8 codes but FP8 -0 codes (0x80) for negative zeros: the caller masks it.
+  __device__ __forceinline__ static uint32_t pack4(float a, float b, float c, float d, float inv) {
+    if constexpr (FP8) {
+      auto t = [&](float v) { return __builtin_amdgcn_fmed3f(__fmul_rn(v, inv), -448.0f, 448.0f); };
+      const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(t(a), t(b), 0, false);
+      return __builtin_amdgcn_cvt_pk_fp8_f32(t(c), t(d), lo, true);
+    } else {
+      auto t = [&](float v) {
+        return __float_as_uint(__builtin_amdgcn_fmed3f(__fmul_rn(v, inv), -127.0f, 127.0f) + 12582912.0f);
+      };
+      return __builtin_amdgcn_perm(t(b), t(a), 0x0C0C0400u) | __builtin_amdgcn_perm(t(d), t(c), 0x04000C0Cu);
+    }
+  }
 };
 
 // ---- 2:4 selection ----------------------------------------------------------
