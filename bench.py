@@ -355,6 +355,49 @@ def suite(ss, torch, dev, reps=10):
                          "dense_tokens_per_s": M / (tot_dn * 1e-6), "speedup": tot_dn / tot_sp}
         torch.cuda.empty_cache()
     res["llama31_8b_24_fp8"] = llama
+    # the same Llama-shaped layers with 6:8 (K' = 1.5 K) at M >= 4096, INT8 and FP8, against dense
+    llama68 = {}
+    for q in ("i8", "fp8"):
+        for M in (4096, 8192):
+            rows, tot_sp, tot_dn = [], 0.0, 0.0
+            for name, (K, Nout) in synth.LLAMA31_8B_LINEARS.items():
+                W = randn((Nout, K), 0.02)
+                tv, tm, sw = ss.slide_decompose_tiled(W, 4, q)
+                wq, swd = ss.quant_lift_act(W, 2, q)
+                del W
+                Kc = ss.lifted_k(K, 4)
+                X = randn((M, K), 1.0, torch.bfloat16)
+                qdt = torch.int8 if q == "i8" else torch.float8_e4m3fn
+                xl = torch.empty((M, Kc), dtype=qdt, device=dev)
+                xq = torch.empty((M, K), dtype=qdt, device=dev)
+                sx = torch.empty(M, dtype=torch.float32, device=dev)
+                sx2 = torch.empty(M, dtype=torch.float32, device=dev)
+                Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+                t_q = timed(lambda: ss.quant_lift_act(X, 4, q, out=(xl, sx)))
+                t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, tv, tm, xl, sx, sw, "bf16", out=Y))
+                t_dq = timed(lambda: ss.quant_lift_act(X, 2, q, out=(xq, sx2)))
+                try:
+                    if q == "i8":
+                        t_dn = timed(lambda: torch._int_mm(xq, wq.t()))
+                    else:
+                        t_dn = timed(lambda: torch._scaled_mm(xq, wq.t(), scale_a=sx2[:, None], scale_b=swd[None, :],
+                                                              out_dtype=torch.bfloat16))
+                except Exception:
+                    t_dn = None
+                hw = 2.0 * M * Nout * Kc
+                rows.append({"layer": name, "K": K, "K_prime": Kc, "N": Nout, "quant_lift_us": t_q,
+                             "sparse_gemm_us": t_sp, "sparse_TOPS_dense_equiv": hw / t_sp / 1e6,
+                             "sparse_frac_of_10070": hw / t_sp / 1e6 / 10070.0,
+                             "effective_TOPS": 2.0 * M * Nout * K / t_sp / 1e6,
+                             "dense_quant_us": t_dq, "dense_gemm_us": t_dn})
+                tot_sp += t_q + t_sp
+                tot_dn += t_dq + (t_dn if t_dn is not None else float("nan"))
+                del tv, tm, sw, wq, swd, X, xl, xq, sx, sx2, Y
+            llama68[f"{q}_{M}"] = {"layers": rows, "sparse_tokens_per_s": M / (tot_sp * 1e-6),
+                                   "dense_tokens_per_s": M / (tot_dn * 1e-6), "speedup": tot_dn / tot_sp,
+                                   "dense_library": "hipBLASLt (torch._int_mm int32 out / torch._scaled_mm bf16 out)"}
+            torch.cuda.empty_cache()
+    res["llama31_8b_68"] = llama68
     # Qwen2.5-7B-shaped sliding-window INT8 GEMMs, decode and prefill token counts
     qwen = []
     for n in (3, 5):
