@@ -412,15 +412,18 @@ def suite(ss, torch, dev, reps=10):
                 xq = torch.empty((M, Kc), dtype=torch.int8, device=dev)
                 sx = torch.empty(M, dtype=torch.float32, device=dev)
                 Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+                need = ss.spgemm_tiled_workspace_bytes(ss.SS_SPARSE_W, M, Nout, Kc, "i8")
+                ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else False
                 t_q = timed(lambda: ss.quant_lift_act(X, n, "i8", out=(xq, sx)))
-                t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y))
+                t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y,
+                                                     workspace=ws))
                 wbytes = tv.numel() + tm.numel()
                 qwen.append({"pattern": f"{2 * n - 2}:{2 * n}", "layer": name, "M": M, "K": K, "K_prime": Kc,
-                             "N": Nout, "quant_lift_us": t_q, "sparse_gemm_us": t_sp,
+                             "N": Nout, "quant_lift_us": t_q, "sparse_gemm_us": t_sp, "split_k_workspace_bytes": need,
                              "sparse_TOPS_dense_equiv": 2.0 * M * Nout * Kc / t_sp / 1e6,
                              "weight_stream_GBs": wbytes / t_sp / 1e3,
                              "tokens_per_s": M / ((t_q + t_sp) * 1e-6)})
-                del X, xq, sx, Y
+                del X, xq, sx, Y, ws
             del tv, tm
             torch.cuda.empty_cache()
     res["qwen25_7b_slide_int8"] = qwen

@@ -243,6 +243,28 @@ ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dty
                           const float* sx, const float* sw, ss_dtype y_dt, void* Y, int64_t ldy,
                           void* stream);
 
+/* ss_spgemm_tiled_workspace_bytes -- bytes of device workspace that
+ * ss_spgemm_tiled_ws uses for this problem on the current device; 0 when the
+ * problem takes no workspace (then ss_spgemm_tiled_ws equals
+ * ss_spgemm_tiled); -1 for invalid arguments. Today: side SS_SPARSE_W with
+ * 17..64 tokens and too few 256-row tiles to fill the GPU (the decode regime
+ * of the SlideSparse blog, section 5.1). */
+int64_t ss_spgemm_tiled_workspace_bytes(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt);
+
+/* ss_spgemm_tiled_ws -- ss_spgemm_tiled with a caller-owned workspace that
+ * lets few-token products split K across workgroups: each writes a partial
+ * tile (int32 for I8 -- exact; fp32 otherwise) and a second kernel sums the
+ * splits in a fixed order before the same epilogue (FP8/BF16 sums in a
+ * different order than ss_spgemm_tiled, within the same 1e-2 bound).
+ * workspace: device memory, 16-byte aligned, ws_bytes >= the query above
+ * (SS_ERR_NULL / SS_ERR_ALIGN / SS_ERR_SHAPE otherwise); NULL with ws_bytes 0
+ * is accepted when the query returns 0. Its contents need no initialisation
+ * and are undefined afterwards; calls that share a workspace must be
+ * stream-ordered. Other arguments and errors as ss_spgemm_tiled. */
+ss_status ss_spgemm_tiled_ws(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
+                             const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
+                             ss_dtype y_dt, void* Y, int64_t ldy, void* workspace, int64_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,8 @@ Functions keep the names of the C entry points:
     prune24_act_tiled(X, out_dtype)         -> (tvals, tmeta, sx | None)
     slide_decompose_tiled(W, n, out_dtype)  -> (tvals, tmeta, scale | None)
     spgemm_tiled(side, M, N, Kc, tvals, tmeta, dense, sx, sw, y_dtype) -> Y [M, N]
+        (takes a workspace from torch when ss_spgemm_tiled_workspace_bytes asks for one)
+    spgemm_tiled_workspace_bytes(side, M, N, Kc, dtype) -> int
 """
 from __future__ import annotations
 
@@ -60,14 +62,18 @@ lib.ss_pack_sparse.argtypes = [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _vp,
 lib.ss_prune24_act_tiled.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _fp, _vp]
 lib.ss_slide_decompose_tiled.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp, _vp, _fp, _vp]
 lib.ss_spgemm_tiled.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
+lib.ss_spgemm_tiled_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _int]
+lib.ss_spgemm_tiled_workspace_bytes.restype = _i64
+lib.ss_spgemm_tiled_ws.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp,
+                                   _i64, _vp]
 for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm", "ss_pack_sparse",
-           "ss_prune24_act_tiled", "ss_slide_decompose_tiled", "ss_spgemm_tiled"):
+           "ss_prune24_act_tiled", "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_ws"):
     getattr(lib, _f).restype = _int
 
 EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_error", "ss_version",
            "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm",
            "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_prune24_act_tiled",
-           "ss_slide_decompose_tiled", "ss_spgemm_tiled")
+           "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_workspace_bytes", "ss_spgemm_tiled_ws")
 
 
 class SSError(RuntimeError):
@@ -207,13 +213,32 @@ def pack_sparse(vals: torch.Tensor, meta: torch.Tensor, out=None):
     return tv, tm
 
 
+def spgemm_tiled_workspace_bytes(side: int, M: int, N: int, Kc: int, dtype="i8") -> int:
+    return int(lib.ss_spgemm_tiled_workspace_bytes(side, M, N, Kc, dtype_code(dtype)))
+
+
 def spgemm_tiled(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta: torch.Tensor, dense: torch.Tensor,
-                 sx=None, sw=None, y_dtype="bf16", out=None):
-    """Y [M, N] = tiled-sparse x dense product with the per-token x per-channel rescale."""
+                 sx=None, sw=None, y_dtype="bf16", out=None, workspace=None):
+    """Y [M, N] = tiled-sparse x dense product with the per-token x per-channel rescale.
+
+    Few-token weight-sparse products split K when given a workspace; with workspace=None one is taken from
+    torch's allocator when the library asks for it (pass workspace=False to run without)."""
     y = dtype_code(y_dtype)
+    ab = dtype_code(dense.dtype)
     Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
-    _check(lib.ss_spgemm_tiled(side, M, N, Kc, dtype_code(dense.dtype), _ptr(tvals), _ptr(tmeta), _ptr(dense),
-                               _ld(dense), _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _stream(dense.device)))
+    if workspace is False:
+        _check(lib.ss_spgemm_tiled(side, M, N, Kc, ab, _ptr(tvals), _ptr(tmeta), _ptr(dense), _ld(dense), _ptr(sx),
+                                   _ptr(sw), y, _ptr(Y), _ld(Y), _stream(dense.device)))
+        return Y
+    else:
+        need = int(lib.ss_spgemm_tiled_workspace_bytes(side, M, N, Kc, ab)) if workspace is None else -1
+        if workspace is None:
+            ws = torch.empty(max(need, 0), dtype=torch.uint8, device=dense.device) if need > 0 else None
+        else:
+            ws = workspace
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.ss_spgemm_tiled_ws(side, M, N, Kc, ab, _ptr(tvals), _ptr(tmeta), _ptr(dense), _ld(dense),
+                                  _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _ptr(ws), nbytes, _stream(dense.device)))
     return Y
 
 

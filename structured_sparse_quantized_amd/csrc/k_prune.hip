@@ -10,6 +10,7 @@
 #include "ss_kernels.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace ss {
 
@@ -256,8 +257,6 @@ __global__ __launch_bounds__(512) void prune24_act_tiled_bf16_kernel(const uint1
   }
 }
 
-// forward declaration (defined below)
-int num_cus_p();
 
 template <typename TIn, int OUT>
 static hipError_t launch_p24_tiled(const TIn* X, int64_t ldx, int64_t M, int64_t K, int64_t Kc, uint8_t* tv,
@@ -325,11 +324,16 @@ hipError_t launch_prune24_tiled(bool in_bf16, int out, const void* W, int64_t ld
 }
 
 int num_cus_p() {
-  static int n = 0;
-  if (!n) {
-    int dev = 0;
-    hipGetDevice(&dev);
+  // cached per device (the library may be used on several GPUs from several threads)
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>* slot = dev < kMaxDev ? &cache[dev] : nullptr;
+  int n = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (slot) slot->store(n, std::memory_order_relaxed);
   }
   return n;
 }

@@ -31,16 +31,6 @@ template <> struct InVec<float> {  // 4 float per 16-byte vector
   __device__ static float scalar(const float* p) { return *p; }
 };
 
-int num_cus() {
-  static int n = 0;
-  if (!n) {
-    int dev = 0;
-    hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  }
-  return n;
-}
-
 // VPT = 16-byte vectors per thread (the row fits when K <= kBlock*VPT*E).
 template <typename TIn, bool FP8, int N, int VPT, bool PIPE>
 __global__ __launch_bounds__(kBlock, (PIPE || VPT > 4) ? 2 : (VPT > 2 ? 4 : 8)) void quant_lift_kernel(const TIn* __restrict__ X, int64_t ldx, int M, int K,
@@ -201,8 +191,8 @@ hipError_t launch_n(const TIn* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq
   }
   // One row per workgroup keeps the most loads in flight for batches up to a few
   // thousand rows; larger batches use persistent workgroups that prefetch.
-  const bool pipe = M > 16 * (int64_t)num_cus();
-  const unsigned grid = (unsigned)(pipe ? 8 * (int64_t)num_cus() : M);
+  const bool pipe = M > 16 * (int64_t)num_cus_p();
+  const unsigned grid = (unsigned)(pipe ? 8 * (int64_t)num_cus_p() : M);
   const int m = (int)M, k = (int)K, kc = (int)Kc;
 #define SS_QL(V_) \
   do { if (pipe) hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, true>), dim3(grid), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); else hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, false>), dim3(grid), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); } while (0)

@@ -41,6 +41,7 @@
 // to registers (a 4-step ring) with the few token rows of the dense operand,
 // and sum their partial tiles through LDS before the same epilogue. The
 // weight stream is the HBM-bound part.
+#include <algorithm>
 #include <type_traits>
 
 #include "ss_device.h"
@@ -344,12 +345,9 @@ template <int AB, int YT, bool SIDE_X>
 hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb,
                   const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
   auto kern = spgemm_kernel<AB, YT, SIDE_X>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set at every launch: the attribute is per device, and the call is cheap and thread-safe
+  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  if (e != hipSuccess) return e;
   const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
   hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * NW), LDS, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, tr, tc);
   return hipGetLastError();
@@ -466,6 +464,226 @@ hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, co
 
 }  // namespace decode
 
+// Split-K product for a few tokens (side W, C <= 64). A workgroup of 8 waves
+// takes 8 row blocks (128 rows) and one range of K: every step, each wave
+// brings its own row block's 1 KB of values and one 8-row x 128-byte block of
+// the dense operand (whole lines, XOR-swizzled as in the tiled kernel) into a
+// ring of LDS stages, so the 64 token rows of a step come from L2 once per
+// workgroup instead of once per wave, and the kernel streams the sparse values
+// at HBM rate. Each workgroup writes its partial tile (int32 for INT8, float
+// otherwise) to a workspace [split][C][RP]; a second kernel sums the splits in
+// order and applies the epilogue (INT8 stays exact).
+namespace splitk {
+
+constexpr int NW = 8, S = 4, BROWS = 64;
+constexpr int A_BYTES = NW * 1024, STAGE = A_BYTES + BROWS * 128, LDS = S * STAGE;  // 16 KB stages, 64 KB
+constexpr int LPW = 2;  // LDS DMA loads per wave per step: own value block + one dense block
+
+template <int AB, int NCT>
+__global__ __launch_bounds__(64 * NW, 4) void splitk_kernel(int R, int C, int KS, int GPS, const uint8_t* __restrict__ tv,
+                                                            const uint8_t* __restrict__ tm,
+                                                            const uint8_t* __restrict__ bd, int ldb,
+                                                            void* __restrict__ ws, int RP) {
+  using Acc = typename tiled::Mma<AB>::Acc;
+  using MT = tiled::Meta<AB>;
+  using MV = typename MT::V;
+  using tiled::v4i;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, jj = lane >> 4;
+  const int nrb = (R + 15) / 16, KS4 = (KS + 3) / 4, KSP = 4 * KS4;
+  const int sp = blockIdx.y;
+  const int g0 = sp * GPS, ng = min(KS4, g0 + GPS) - g0;  // this split's 4-step groups (ng >= 1)
+  const int k0 = 4 * g0, nst = 4 * ng;
+  const int rbw = blockIdx.x * NW + wave;  // this wave's row block
+  const int rb = min(rbw, nrb - 1);        // clamped: in bounds, results not stored
+  const uint8_t* pa = tv + (int64_t)rb * KSP * 1024 + lane * 16;
+  const uint8_t* pm = tm + (int64_t)rb * KS4 * MT::BLOCK + lane * (4 * MT::WB);
+  const int brow = 8 * wave + (lane >> 3);  // dense rows past C re-read row C-1 (never stored)
+  const uint32_t offb = (uint32_t)min(brow, C - 1) * (uint32_t)ldb + tiled::swz(lane & 7, brow & 15) * 16;
+
+  // local step i -> slot i % S; past the range the last step is re-read (in bounds, never consumed)
+  auto issue = [&](int i) {
+    SS_LDS uint8_t* base = (SS_LDS uint8_t*)smem + (i % S) * STAGE;
+    const int k = k0 + min(i, nst - 1), kb = min(k, KS - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(pa + (int64_t)k * 1024), (SS_LDS void*)(base + wave * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(bd + offb + (uint32_t)kb * 128),
+                                     (SS_LDS void*)(base + A_BYTES + wave * 1024), 16, 0, 0);
+  };
+  MV mcur, mnxt;
+  auto load_meta = [&](MV& m, int g) { m = *reinterpret_cast<const MV*>(pm + (int64_t)g * MT::BLOCK); };
+  struct Frag {
+    v4i a;
+    v4i b[NCT][2];
+  };
+  auto read = [&](Frag& f, int i) {
+    const uint8_t* st = smem + (i % S) * STAGE;
+    f.a = *reinterpret_cast<const v4i*>(st + wave * 1024 + lane * 16);
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const uint8_t* bb = st + A_BYTES + (2 * c + (r16 >> 3)) * 1024 + (r16 & 7) * 128;
+      f.b[c][0] = *reinterpret_cast<const v4i*>(bb + tiled::swz(jj, r16) * 16);
+      f.b[c][1] = *reinterpret_cast<const v4i*>(bb + tiled::swz(4 + jj, r16) * 16);
+    }
+  };
+  Acc acc[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) acc[c] = Acc{0, 0, 0, 0};
+  auto mma = [&](const Frag& f, auto qc) {
+    constexpr int Q = decltype(qc)::value;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[c] = tiled::mma_step<AB, Q>(f.a, f.b[c][0], f.b[c][1], acc[c], mcur);
+  };
+  // stage i+1 landed: outstanding loads = the S-3 later stages plus an index group issued since (one per
+  // group, at its first step, except in the last group)
+  auto wait_next = [&](auto qc, auto lastc) {
+    constexpr int Q = decltype(qc)::value;
+    constexpr bool LAST = decltype(lastc)::value;
+    constexpr int lo = Q + 6 - S, hi = Q + 3;
+    constexpr int nm = LAST ? 0 : (hi >= 4 && lo <= 4 ? 1 : 0) + (hi >= 8 && lo <= 8 ? 1 : 0);
+    constexpr int N = (S - 3) * LPW + nm;
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  };
+  auto step = [&](int j, auto qc, auto lastc, Frag& cur, Frag& nxt) {
+    constexpr int Q = decltype(qc)::value;
+    constexpr bool LAST = decltype(lastc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_next(qc, lastc);
+    __builtin_amdgcn_s_barrier();  // stage j+1 landed for every wave; slot (j-1) % S is free
+    __builtin_amdgcn_sched_barrier(0);
+    issue(j + S - 1);
+    if (Q == 0 && !LAST) load_meta(mnxt, g0 + j / 4 + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    read(nxt, j + 1);
+    mma(cur, qc);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
+  load_meta(mcur, g0);
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) issue(i);
+  Frag f0, f1;
+  {
+    constexpr int N = (S - 2) * LPW;  // stage 0 landed
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  }
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read(f0, 0);
+  for (int g = 0; g + 1 < ng; ++g) {
+    const int j = 4 * g;
+    step(j, Q0{}, std::false_type{}, f0, f1);
+    step(j + 1, Q1{}, std::false_type{}, f1, f0);
+    step(j + 2, Q2{}, std::false_type{}, f0, f1);
+    step(j + 3, Q3{}, std::false_type{}, f1, f0);
+    mcur = mnxt;
+  }
+  {
+    const int j = nst - 4;
+    step(j, Q0{}, std::true_type{}, f0, f1);
+    step(j + 1, Q1{}, std::true_type{}, f1, f0);
+    step(j + 2, Q2{}, std::true_type{}, f0, f1);
+    mma(f1, Q3{});
+  }
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // no load may outlive the workgroup
+  if (rbw < nrb) {
+    const int ar = rb * 16 + 4 * jj;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int bc = c * 16 + r16;
+      if (bc < C) {
+        int32_t* o = static_cast<int32_t*>(ws) + ((int64_t)sp * C + bc) * RP + ar;
+        if constexpr (AB == 0)
+          *reinterpret_cast<int4*>(o) = make_int4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+        else
+          *reinterpret_cast<float4*>(o) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+      }
+    }
+  }
+}
+
+// Sum the splits in order (exact for int32) and apply the epilogue: one thread per 4 rows of one token.
+template <int AB, int YT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(int R, int C, int RP, int splits,
+                                                            const void* __restrict__ ws, const float* __restrict__ sx,
+                                                            const float* __restrict__ sw, void* __restrict__ Y,
+                                                            int ldy) {
+  const int quads = RP / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int bc = (int)(idx / quads), ar = (int)(idx % quads) * 4;
+  if (bc >= C || ar >= R) return;
+  float y[4];
+  int32_t yi[4];
+  if constexpr (AB == 0) {
+    int4 s = make_int4(0, 0, 0, 0);
+    for (int p = 0; p < splits; ++p) {
+      const int4 v = *reinterpret_cast<const int4*>(static_cast<const int32_t*>(ws) + ((int64_t)p * C + bc) * RP + ar);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    yi[0] = s.x; yi[1] = s.y; yi[2] = s.z; yi[3] = s.w;
+  } else {
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int p = 0; p < splits; ++p) {
+      const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(ws) + ((int64_t)p * C + bc) * RP + ar);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    y[0] = s.x; y[1] = s.y; y[2] = s.z; y[3] = s.w;
+  }
+  if constexpr (YT != 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float f = AB == 0 ? (float)yi[q] : y[q];
+      if (sx) f = __fmul_rn(f, sx[bc]);
+      if (sw) f = __fmul_rn(f, sw[min(ar + q, R - 1)]);
+      y[q] = f;
+    }
+  }
+  store_out<YT, false>(Y, ldy, ar, bc, R, y, yi);
+}
+
+struct Plan {
+  int splits = 0, gps = 0, rp = 0;
+  int64_t bytes = 0;
+};
+
+// Split count: about one workgroup per CU over (row groups x splits), whole 4-step groups per split.
+inline Plan plan(int64_t R, int64_t C, int64_t KS) {
+  Plan p;
+  const int64_t nrb = (R + 15) / 16, nrg = (nrb + NW - 1) / NW, ks4 = (KS + 3) / 4;
+  int64_t sk = ((int64_t)num_cus_p() + nrg - 1) / nrg;
+  sk = std::max<int64_t>(1, std::min<int64_t>(sk, ks4));
+  p.gps = (int)((ks4 + sk - 1) / sk);
+  p.splits = (int)((ks4 + p.gps - 1) / p.gps);
+  p.rp = (int)(nrb * 16);
+  p.bytes = (int64_t)p.splits * C * p.rp * 4;
+  return p;
+}
+
+template <int AB, int YT>
+hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb,
+                  const float* sx, const float* sw, void* Y, int ldy, void* ws, hipStream_t st) {
+  const Plan p = plan(R, C, KS);
+  const int nrg = ((R + 15) / 16 + NW - 1) / NW;
+  const dim3 grid((unsigned)nrg, (unsigned)p.splits);
+  auto go = [&](auto kern) -> hipError_t {
+    const hipError_t a = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (a != hipSuccess) return a;
+    hipLaunchKernelGGL(kern, grid, dim3(64 * NW), LDS, st, R, C, KS, p.gps, tv, tm, bd, ldb, ws, p.rp);
+    return hipGetLastError();
+  };
+  hipError_t e = C <= 16 ? go(splitk_kernel<AB, 1>) : C <= 32 ? go(splitk_kernel<AB, 2>) : go(splitk_kernel<AB, 4>);
+  if (e != hipSuccess) return e;
+  const int64_t threads = (int64_t)C * (p.rp / 4);
+  hipLaunchKernelGGL((splitk_reduce_kernel<AB, YT>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, R, C, p.rp,
+                     p.splits, (const void*)ws, sx, sw, Y, ldy);
+  return hipGetLastError();
+}
+
+}  // namespace splitk
+
 int64_t tiled_vals_bytes(int64_t rows, int64_t Kc, int es) {
   const int64_t ks4 = (Kc * es / 128 + 3) / 4;
   return (rows + 15) / 16 * ks4 * 4 * 1024;
@@ -488,16 +706,30 @@ hipError_t launch_pack_tiled(int es, const uint8_t* vals, int64_t ldv_bytes, con
   return hipGetLastError();
 }
 
+// Few tokens on the weight-sparse side and too few 256-row tiles to fill the chip.
+static bool few_tokens(bool side_x, int64_t R, int64_t C) {
+  const int64_t tiles = ((R + tiled::BM - 1) / tiled::BM) * ((C + tiled::BN - 1) / tiled::BN);
+  return !side_x && C <= 64 && (C <= 8 || tiles < 128);
+}
+// The split-K path (with a workspace) serves the few-token products with more than 16 tokens.
+static bool use_splitk(bool side_x, int64_t R, int64_t C) { return few_tokens(side_x, R, C) && C > 16; }
+
+int64_t spgemm_tiled_workspace_bytes(bool side_x, int ab, int64_t R, int64_t C, int64_t Kc) {
+  if (!use_splitk(side_x, R, C)) return 0;
+  return splitk::plan(R, C, Kc * (ab == 2 ? 2 : 1) / 128).bytes;
+}
+
 hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C, int64_t Kc, const uint8_t* tv,
                                const uint8_t* tm, const void* bd, int64_t ldb_bytes, const float* sx, const float* sw,
-                               void* Y, int64_t ldy, hipStream_t st) {
+                               void* Y, int64_t ldy, void* ws, hipStream_t st) {
   const uint8_t* b = static_cast<const uint8_t*>(bd);
   const int r = (int)R, c = (int)C, ks = (int)(Kc * (ab == 2 ? 2 : 1) / 128), lb = (int)ldb_bytes, ly = (int)ldy;
-  // few tokens and too few 256-row tiles to fill the chip: the row-block decode kernel
-  const int64_t tiles = ((R + tiled::BM - 1) / tiled::BM) * ((C + tiled::BN - 1) / tiled::BN);
-  const bool dec = !side_x && C <= 64 && (C <= 8 || tiles < 128);
+  // few tokens: split-K when a workspace is given and the problem uses one, else the row-block decode kernel
+  const bool dec = few_tokens(side_x, R, C);
+  const bool spk = ws != nullptr && use_splitk(side_x, R, C);
 #define SS_TL(AB_, YT_)                                                                                   \
-  return dec      ? decode::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)                   \
+  return spk      ? splitk::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, ws, st)               \
+         : dec    ? decode::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)                   \
          : side_x ? tiled::launch<AB_, YT_, true>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)               \
                   : tiled::launch<AB_, YT_, false>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)
   if (ab == 0) {

@@ -263,9 +263,11 @@ ss_status ss_slide_decompose_tiled(const void* W, ss_dtype w_dt, int64_t rows, i
                     "ss_slide_decompose_tiled launch");
 }
 
-ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
-                          const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
-                          ss_dtype y_dt, void* Y, int64_t ldy, void* stream) {
+// Checks shared by ss_spgemm_tiled and ss_spgemm_tiled_ws; sets *run = false for an empty problem.
+static ss_status check_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
+                                    const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx,
+                                    const float* sw, ss_dtype y_dt, void* Y, int64_t ldy, bool* run) {
+  *run = false;
   if (side != SS_SPARSE_W && side != SS_SPARSE_X) return fail(SS_ERR_SHAPE, "bad side");
   if (ab_dt != SS_I8 && ab_dt != SS_FP8E4M3 && ab_dt != SS_BF16)
     return fail(SS_ERR_DTYPE, "operands must be I8, FP8E4M3 or BF16");
@@ -273,7 +275,7 @@ ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dty
   if (y_dt == SS_I32 && ab_dt != SS_I8) return fail(SS_ERR_DTYPE, "I32 output needs I8 operands");
   if (M < 0 || N < 0 || Kc < 0) return fail(SS_ERR_SHAPE, "negative size");
   if (Kc % SS_KALIGN != 0) return fail(SS_ERR_SHAPE, "Kc=%lld is not a multiple of %d", (long long)Kc, SS_KALIGN);
-  if (M == 0 || N == 0) return ok();
+  if (M == 0 || N == 0) return SS_OK;
   if (Kc == 0) return fail(SS_ERR_SHAPE, "Kc must be positive");
   const bool sx_side = (side == SS_SPARSE_X);
   const int64_t R = sx_side ? M : N, C = sx_side ? N : M;
@@ -289,12 +291,60 @@ ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dty
   if (!tvals || !tmeta) return fail(SS_ERR_NULL, "tiled operand is NULL");
   if (!aligned16(tvals) || !aligned16(tmeta)) return fail(SS_ERR_ALIGN, "tiled operand is not 16-byte aligned");
   if (ab_dt != SS_BF16 && y_dt != SS_I32 && (!sx || !sw)) return fail(SS_ERR_NULL, "INT8/FP8 products need both scales");
+  *run = true;
+  return SS_OK;
+}
+
+static ss_status run_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
+                                  const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx,
+                                  const float* sw, ss_dtype y_dt, void* Y, int64_t ldy, void* ws, void* stream) {
+  const bool sx_side = (side == SS_SPARSE_X);
+  const int64_t R = sx_side ? M : N, C = sx_side ? N : M;
   const int ab = ab_dt == SS_I8 ? 0 : ab_dt == SS_FP8E4M3 ? 1 : 2;
   const int yt = y_dt == SS_BF16 ? 0 : y_dt == SS_F32 ? 1 : 2;
   return hip_status(ss::launch_spgemm_tiled(sx_side, ab, yt, R, C, Kc, static_cast<const uint8_t*>(tvals), tmeta, dense,
-                                            ldd * es, y_dt == SS_I32 ? nullptr : sx, y_dt == SS_I32 ? nullptr : sw, Y,
-                                            ldy, (hipStream_t)stream),
+                                            ldd * esize(ab_dt), y_dt == SS_I32 ? nullptr : sx,
+                                            y_dt == SS_I32 ? nullptr : sw, Y, ldy, ws, (hipStream_t)stream),
                     "ss_spgemm_tiled launch");
+}
+
+ss_status ss_spgemm_tiled(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
+                          const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
+                          ss_dtype y_dt, void* Y, int64_t ldy, void* stream) {
+  bool run = false;
+  const ss_status s = check_spgemm_tiled(side, M, N, Kc, ab_dt, tvals, tmeta, dense, ldd, sx, sw, y_dt, Y, ldy, &run);
+  if (s != SS_OK) return s;
+  if (!run) return ok();
+  return run_spgemm_tiled(side, M, N, Kc, ab_dt, tvals, tmeta, dense, ldd, sx, sw, y_dt, Y, ldy, nullptr, stream);
+}
+
+int64_t ss_spgemm_tiled_workspace_bytes(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt) {
+  if (side != SS_SPARSE_W && side != SS_SPARSE_X) return -1;
+  if (ab_dt != SS_I8 && ab_dt != SS_FP8E4M3 && ab_dt != SS_BF16) return -1;
+  if (M < 0 || N < 0 || Kc < 0 || Kc % SS_KALIGN != 0) return -1;
+  if (M == 0 || N == 0 || Kc == 0 || M > 0x7FFFFFF0LL || N > 0x7FFFFFF0LL) return 0;
+  const bool sx_side = (side == SS_SPARSE_X);
+  const int ab = ab_dt == SS_I8 ? 0 : ab_dt == SS_FP8E4M3 ? 1 : 2;
+  return ss::spgemm_tiled_workspace_bytes(sx_side, ab, sx_side ? M : N, sx_side ? N : M, Kc);
+}
+
+ss_status ss_spgemm_tiled_ws(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
+                             const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
+                             ss_dtype y_dt, void* Y, int64_t ldy, void* workspace, int64_t ws_bytes, void* stream) {
+  bool run = false;
+  const ss_status s = check_spgemm_tiled(side, M, N, Kc, ab_dt, tvals, tmeta, dense, ldd, sx, sw, y_dt, Y, ldy, &run);
+  if (s != SS_OK) return s;
+  if (ws_bytes < 0) return fail(SS_ERR_SHAPE, "negative workspace size");
+  if (!run) return ok();
+  const int64_t need = ss_spgemm_tiled_workspace_bytes(side, M, N, Kc, ab_dt);
+  if (need > 0) {
+    if (!workspace) return fail(SS_ERR_NULL, "workspace is NULL (%lld bytes needed)", (long long)need);
+    if (!aligned16(workspace)) return fail(SS_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (ws_bytes < need) return fail(SS_ERR_SHAPE, "workspace of %lld bytes, %lld needed", (long long)ws_bytes,
+                                     (long long)need);
+  }
+  return run_spgemm_tiled(side, M, N, Kc, ab_dt, tvals, tmeta, dense, ldd, sx, sw, y_dt, Y, ldy,
+                          need > 0 ? workspace : nullptr, stream);
 }
 
 }  // extern "C"

@@ -39,8 +39,10 @@ int64_t tiled_meta_bytes(int64_t rows, int64_t Kc, int es);
 hipError_t launch_pack_tiled(int es, const uint8_t* vals, int64_t ldv_bytes, const uint8_t* meta, int64_t ldm,
                              int64_t rows, int64_t Kc, uint8_t* tv, uint8_t* tm, hipStream_t st);
 // ab: 0 = int8, 1 = fp8, 2 = bf16; yt: 0 = bf16, 1 = f32, 2 = i32
+// ws: workspace of spgemm_tiled_workspace_bytes bytes, or NULL (no split-K path)
 hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C, int64_t Kc, const uint8_t* tv,
                                const uint8_t* tm, const void* bd, int64_t ldb_bytes, const float* sx, const float* sw,
-                               void* Y, int64_t ldy, hipStream_t st);
+                               void* Y, int64_t ldy, void* ws, hipStream_t st);
+int64_t spgemm_tiled_workspace_bytes(bool side_x, int ab, int64_t R, int64_t C, int64_t Kc);
 
 }  // namespace ss

@@ -138,6 +138,24 @@ def test_tiled_validation_statuses():
     assert S(FAKE, ss.SS_F32, -1, 8, 8, 4, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
     assert S(FAKE, ss.SS_F32, 0, 8, 8, 4, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_OK
     assert S(FAKE, ss.SS_F32, 4, 0, 8, 4, ss.SS_I8, FAKE, FAKE, FAKE, None) == ss.SS_OK
+    # workspace query and the split-K entry point
+    Q = L.ss_spgemm_tiled_workspace_bytes
+    assert Q(ss.SS_SPARSE_W, 64, 3584, 25344, ss.SS_I8) > 0          # few tokens, few row tiles
+    assert Q(ss.SS_SPARSE_W, 16, 3584, 25344, ss.SS_I8) == 0         # row-block kernel, no workspace
+    assert Q(ss.SS_SPARSE_W, 4096, 4096, 4096, ss.SS_I8) == 0        # prefill
+    assert Q(ss.SS_SPARSE_X, 64, 3584, 4096, ss.SS_I8) == 0
+    assert Q(ss.SS_SPARSE_W, 64, 3584, 100, ss.SS_I8) == -1
+    assert Q(ss.SS_SPARSE_W, 64, 3584, 4096, ss.SS_F32) == -1
+    assert Q(ss.SS_SPARSE_W, 0, 3584, 4096, ss.SS_I8) == 0
+    need = Q(ss.SS_SPARSE_W, 64, 3584, 4096, ss.SS_I8)
+    def gw(ws=FAKE, nb=need, M=64, N=3584, Kc=4096):
+        return L.ss_spgemm_tiled_ws(0, M, N, Kc, ss.SS_I8, FAKE, FAKE, FAKE, Kc, FAKE, FAKE, ss.SS_BF16, FAKE, N,
+                                    ws, nb, None)
+    assert gw(ws=None) == ss.SS_ERR_NULL
+    assert gw(nb=need - 16) == ss.SS_ERR_SHAPE
+    assert gw(nb=-1) == ss.SS_ERR_SHAPE
+    assert gw(ws=odd) == ss.SS_ERR_ALIGN
+    assert gw(M=0) == ss.SS_OK
     # product
     def g(side=0, M=4, N=4, Kc=256, ab=ss.SS_I8, tv=FAKE, tm=FAKE, d=FAKE, ldd=256, sx=FAKE, sw=FAKE,
           y=ss.SS_BF16, Y=FAKE, ldy=8):

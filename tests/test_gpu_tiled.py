@@ -187,12 +187,16 @@ def test_repeated_calls_and_streams(ss):
 # waves, partial sums reduced in LDS); these cases cover its column-tile counts (<= 16, 32, 64 tokens), ragged
 # row counts, K short enough that some waves get no work, and long K.
 DECODE_SHAPES = [(1, 1000, 512), (5, 1000, 600), (8, 260, 2048), (9, 300, 1000), (16, 512, 4096), (17, 130, 512),
-                 (32, 700, 3000), (33, 520, 768), (64, 1000, 6000), (64, 4608, 3584)]
+                 (32, 700, 3000), (33, 520, 768), (64, 1000, 6000), (64, 4608, 3584), (40, 300, 18944),
+                 (64, 3584, 18944)]
 
 
+@pytest.mark.parametrize("path", ["auto", "no_workspace"])
 @pytest.mark.parametrize("ab", ["i8", "fp8", "bf16"])
 @pytest.mark.parametrize("shape", DECODE_SHAPES)
-def test_spgemm_tiled_decode_tokens(ss, ab, shape):
+def test_spgemm_tiled_decode_tokens(ss, ab, shape, path):
+    """Few-token weight-sparse products: the split-K path (17..64 tokens, workspace from torch) and the
+    row-block kernel (no workspace), against the oracle."""
     M, N, K = shape
     n = 3 if K % 6 == 0 else 2
     vals, meta, dense, sx, sw, Kc = _gemm_case(101 + M + N, M, N, K, n, ab, "W")
@@ -200,7 +204,8 @@ def test_spgemm_tiled_decode_tokens(ss, ab, shape):
     d = dev_codes(dense, ab)
     dsx, dsw = _scales(sx, sw)
     for y in (["i32", "bf16"] if ab == "i8" else ["f32", "bf16"]):
-        Y = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, d, dsx, dsw, y_dtype=y))
+        Y = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, d, dsx, dsw, y_dtype=y,
+                                 workspace=None if path == "auto" else False))
         exp = oracle.spgemm("W", vals, meta, dense, Kc, ab, sx, sw, y)
         if ab == "i8":
             assert np.array_equal(Y, exp), y
@@ -327,3 +332,22 @@ def test_weight_sparse_path_one_pass(ss, n):
     ov, om, osw = oracle.slide_decompose(W, n, "i8")
     oxq, osx = oracle.quant_lift_act(X, n, "i8")
     assert np.array_equal(Y, oracle.spgemm("W", ov, om, oxq, Kc, "i8", osx, osw, "bf16"))
+
+
+def test_spgemm_tiled_shared_workspace(ss):
+    """One caller-owned workspace reused by two split-K products in a row, the second smaller; INT8 exact."""
+    Kc_max = 0
+    cases = []
+    for seed, (M, N, K) in ((211, (64, 2000, 4096)), (212, (24, 700, 1024))):
+        vals, meta, dense, sx, sw, Kc = _gemm_case(seed, M, N, K, 2, "i8", "W")
+        cases.append((M, N, K, vals, meta, dense, sx, sw, Kc))
+    need = max(ss.spgemm_tiled_workspace_bytes(ss.SS_SPARSE_W, M, N, Kc, "i8") for M, N, _, _, _, _, _, _, Kc in cases)
+    assert need > 0
+    import torch
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for M, N, K, vals, meta, dense, sx, sw, Kc in cases:
+        tv, tm = ss.pack_sparse(dev_codes(vals, "i8"), dev_u8(meta))
+        dsx, dsw = _scales(sx, sw)
+        Y = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, dev_codes(dense, "i8"), dsx, dsw, "bf16",
+                                 workspace=ws))
+        assert np.array_equal(Y, oracle.spgemm("W", vals, meta, dense, Kc, "i8", sx, sw, "bf16"))
