@@ -4,7 +4,7 @@
 // nonzeros to the n-1 stride-2 width-4 windows, per-channel quantisation and
 // 2:4 compression of W' directly in K' order.
 //
-// One workgroup per weight row. The row is staged in LDS with coalesced
+// Persistent workgroups, one weight row at a time. The row is staged in LDS with coalesced
 // 16-byte loads (the absmax is taken on the way); thread i then owns groups
 // i, i + 256, ... read back from LDS, prunes each, splits it into its n-1
 // windows, quantises them and writes them into an LDS image of the output
@@ -308,12 +308,12 @@ __device__ __forceinline__ void store_image(const uint8_t* lv, const uint32_t* l
 // to 16 bytes][values Kc/2 * ES][metadata Kc/8]. Persistent: iteration i of a
 // workgroup takes row blockIdx.x + i * gridDim.x (TILED: in xcd_row order over the
 // rows up to the next multiple of 16, those past `rows` written as zero rows).
-// UPT > 0: the row's 16-byte units (K / EPU <= UPT * kBlock) are prefetched into
-// registers one row ahead, so the next row streams in while this one is pruned
-// and stored (the barriers inside the loop order LDS only and do not wait for it).
-// UPT = 0: each row is loaded when it is staged.
-template <typename TIn, int N, int OUT, bool TILED, int UPT>
-__global__ __launch_bounds__(kBlock) void slide_lds_kernel(const TIn* __restrict__ W, int64_t ldw, int rows, int K,
+// Each row is loaded when it is staged (four 16-byte loads in flight per
+// thread); eight waves per SIMD (n <= 4) overlap one workgroup's loads with another's
+// pruning. (A one-row-ahead register prefetch needed 86 VGPRs, five waves per
+// SIMD, and measured 11% slower.)
+template <typename TIn, int N, int OUT, bool TILED>
+__global__ __launch_bounds__(kBlock, N <= 4 ? 8 : 4) void slide_lds_kernel(const TIn* __restrict__ W, int64_t ldw, int rows, int K,
                                                            uint8_t* __restrict__ vals, int64_t ldv_bytes,
                                                            uint8_t* __restrict__ meta, int64_t ldm, int Kc,
                                                            float* __restrict__ scale) {
@@ -335,18 +335,6 @@ __global__ __launch_bounds__(kBlock) void slide_lds_kernel(const TIn* __restrict
   auto row_of = [&](int it) { return TILED ? xcd_row(it, nrows) : it; };
   if constexpr (TAB) load_slide_table<N>(tab);  // published by the first barrier below
 
-  uint4 pre[UPT > 0 ? UPT : 1];
-  auto fetch = [&](int r) {
-    const TIn* wr = W + (int64_t)(r < rows ? r : 0) * ldw;
-#pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      const int i = j * kBlock + tid;
-      pre[j] = (i < nfull && r < rows) ? reinterpret_cast<const uint4*>(wr)[i] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  if constexpr (UPT > 0) {
-    if ((int)blockIdx.x < nrows) fetch(row_of(blockIdx.x));
-  }
   for (int it = blockIdx.x; it < nrows; it += gridDim.x) {
     const int row = row_of(it);
     const bool live = row < rows;
@@ -358,23 +346,17 @@ __global__ __launch_bounds__(kBlock) void slide_lds_kernel(const TIn* __restrict
 #pragma unroll
       for (int k = 0; k < EPU; ++k) amax = fmaxf(amax, fabsf(to_f32<TIn>(t[k])));
     };
-    if constexpr (UPT > 0) {
+    for (int i0 = 0; i0 < nfull; i0 += 4 * kBlock) {  // four loads in flight per thread (zeros past `rows`)
+      uint4 v[4];
 #pragma unroll
-      for (int j = 0; j < UPT; ++j)
-        if (j * kBlock + tid < nfull) stage(pre[j], j * kBlock + tid);
-    } else {
-      for (int i0 = 0; i0 < nfull; i0 += 4 * kBlock) {  // four loads in flight per thread (zeros past `rows`)
-        uint4 v[4];
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + j * kBlock + tid;
+        v[j] = (i < nfull && live) ? reinterpret_cast<const uint4*>(wr)[i] : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = i0 + j * kBlock + tid;
-          v[j] = (i < nfull && live) ? reinterpret_cast<const uint4*>(wr)[i] : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = i0 + j * kBlock + tid;
-          if (i < nfull) stage(v[j], i);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + j * kBlock + tid;
+        if (i < nfull) stage(v[j], i);
       }
     }
     // ragged end of the row and the zero padding of the last group
@@ -384,9 +366,6 @@ __global__ __launch_bounds__(kBlock) void slide_lds_kernel(const TIn* __restrict
       amax = fmaxf(amax, fabsf(to_f32<TIn>(v)));
     }
     for (int i = tid; i < Kc / 32; i += kBlock) lm[i] = 0;
-    if constexpr (UPT > 0) {
-      if (it + (int)gridDim.x < nrows) fetch(row_of(it + gridDim.x));
-    }
     bool zero_row = false;
     float inv = 0.0f;
     if constexpr (OUT != 2) {
@@ -542,7 +521,6 @@ hipError_t launch_one(const TIn* W, int64_t ldw, int64_t rows, int64_t K, uint8_
   }
   // persistent grid: the workgroups that are resident at once (registers and LDS), at most 8
   // per CU; a multiple of 8 when it is smaller than the row count (xcd_row order)
-  const int64_t units = K * (int64_t)sizeof(TIn) / 16;
   auto go = [&](auto kern) -> hipError_t {
     if (staged > 64 * 1024) {
       const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)staged);
@@ -556,11 +534,7 @@ hipError_t launch_one(const TIn* W, int64_t ldw, int64_t rows, int64_t K, uint8_
                        (int)Kc, scale);
     return hipGetLastError();
   };
-  if (units <= 1 * kBlock) return go(slide_lds_kernel<TIn, N, OUT, TILED, 1>);
-  if (units <= 2 * kBlock) return go(slide_lds_kernel<TIn, N, OUT, TILED, 2>);
-  if (units <= 4 * kBlock) return go(slide_lds_kernel<TIn, N, OUT, TILED, 4>);
-  if (units <= 8 * kBlock) return go(slide_lds_kernel<TIn, N, OUT, TILED, 8>);
-  return go(slide_lds_kernel<TIn, N, OUT, TILED, 0>);
+  return go(slide_lds_kernel<TIn, N, OUT, TILED>);
 }
 
 template <typename TIn, int N, bool TILED>
