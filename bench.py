@@ -254,6 +254,11 @@ def main():
         except Exception as e:  # comparator unavailable on this stack
             dense = {"error": repr(e)[:200]}
 
+    # engine clock while the product runs back to back (sysfs; None where it is not readable)
+    sclk = None
+    if not args.kernels_only:
+        sclk = sample_sclk(lambda: steps_calls[0][names.index("spgemm_68")](), torch, seconds=0.3)
+
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -289,6 +294,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "rotating_buffer_sets": NBUF,
+        "sclk_MHz_during_spgemm_68": sclk,
         "per_call_sum_ms": sum(per_kernel_ms.values()),
         "suite": suite_res,
     }
@@ -490,6 +496,54 @@ def suite(ss, torch, dev, reps=10):
     torch.cuda.empty_cache()
     res["quant_lift_large_int8"] = ql
     return res
+
+
+def read_sclk_mhz():
+    """Current engine clock from the amdgpu sysfs DPM table (the level marked '*'), or None."""
+    import glob
+    import re
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path).read().splitlines():
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    if m:
+                        return int(m.group(1))
+        except OSError:
+            continue
+    return None
+
+
+def sample_sclk(launch, torch, seconds=0.3, period=0.002):
+    """Launch `launch` back to back for `seconds` while a thread samples the engine clock."""
+    import statistics
+    import threading
+    if read_sclk_mhz() is None:
+        return {"error": "no readable pp_dpm_sclk"}
+    samples, stop = [], threading.Event()
+
+    def run():
+        while not stop.is_set():
+            v = read_sclk_mhz()
+            if v is not None:
+                samples.append(v)
+            time.sleep(period)
+
+    th = threading.Thread(target=run)
+    launch()
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            launch()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return {"error": "no samples"}
+    return {"samples": len(samples), "median": statistics.median(samples), "min": min(samples),
+            "max": max(samples), "idle_after": read_sclk_mhz()}
 
 
 def cpu_baseline(X_np, W_np, Kc68, Kc24):
