@@ -649,11 +649,12 @@ struct Plan {
   int64_t bytes = 0;
 };
 
-// Split count: about one workgroup per CU over (row groups x splits), whole 4-step groups per split.
+// Split count: at most one workgroup per CU over (row groups x splits) -- a CU holding two would
+// finish last at half speed -- with whole 4-step groups per split.
 inline Plan plan(int64_t R, int64_t C, int64_t KS) {
   Plan p;
   const int64_t nrb = (R + 15) / 16, nrg = (nrb + NW - 1) / NW, ks4 = (KS + 3) / 4;
-  int64_t sk = ((int64_t)num_cus_p() + nrg - 1) / nrg;
+  int64_t sk = (int64_t)num_cus_p() / nrg;
   sk = std::max<int64_t>(1, std::min<int64_t>(sk, ks4));
   p.gps = (int)((ks4 + sk - 1) / sk);
   p.splits = (int)((ks4 + p.gps - 1) / p.gps);
