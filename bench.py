@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernels-only", action="store_true", help="skip the dense comparator and CPU baseline")
+    p.add_argument("--no-clock", action="store_true", help="skip the engine-clock sampling loop")
     p.add_argument("--no-suite", action="store_true", help="skip the Llama/Qwen-shaped layer suite")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (the reference for HBM byte counters)")
@@ -256,7 +257,7 @@ def main():
 
     # engine clock while the product runs back to back (sysfs; None where it is not readable)
     sclk = None
-    if not args.kernels_only:
+    if not (args.kernels_only or args.no_clock):
         sclk = sample_sclk(lambda: steps_calls[0][names.index("spgemm_68")](), torch, seconds=0.3)
 
     if args.calib_copy:
