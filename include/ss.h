@@ -265,6 +265,48 @@ ss_status ss_spgemm_tiled_ws(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_
                              const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
                              ss_dtype y_dt, void* Y, int64_t ldy, void* workspace, int64_t ws_bytes, void* stream);
 
+/* ---- Block-scaled FP8 -------------------------------------------------------
+ * The W8A8-FP8_BLOCK scheme of the LLM Compressor "compression schemes" guide:
+ * FP8 weights with one scale per block of 128 output channels x 128 positions
+ * along K, FP8 activations with one dynamic scale per token and group of 128
+ * positions. Here on 2:4-sparse weights (plain pattern, K' = K): Kc =
+ * ss_lifted_k(K, 2), G = Kc / 128 scale groups (a multiple of 2). Each block
+ * or group is quantised as a row of ss_prune24 / ss_quant_lift_act is:
+ * a = max |v| over it, codes E4M3FN(clamp(fl32(v * fl32(448 / a)))), scale
+ * fl32(a / 448); an all-zero block or group (including the padding groups past
+ * K) has scale 0 and zero codes. */
+
+/* ss_prune24_block -- block-scaled weight prep, written in the tiled layout.
+ * W [rows][K] F32 or BF16 (ldw elements), K % 4 == 0: 2:4 magnitude prune along
+ * K on the raw values (as ss_prune24; the prune keeps every block maximum),
+ * then the kept values coded with the scale of their block.
+ * tvals / tmeta: ss_tiled_vals_bytes / ss_tiled_meta_bytes(rows, Kc,
+ * SS_FP8E4M3) bytes, 16-byte aligned, written completely. sw: ceil(rows / 128)
+ * x G floats, row-major: sw[b][g] scales rows 128b .. 128b + 127 and K
+ * positions 128g .. 128g + 127. */
+ss_status ss_prune24_block(const void* W, ss_dtype w_dt, int64_t rows, int64_t K, int64_t ldw, void* tvals,
+                           uint8_t* tmeta, float* sw, void* stream);
+
+/* ss_quant_group_act -- block-scaled activation prep. X [M][K] F32 or BF16
+ * (ldx elements), any K >= 0; Xq [M][Kc] FP8E4M3 codes (ldq bytes, zero past
+ * K); sx: M x G floats, row-major (sx[m][g] for positions 128g .. 128g + 127
+ * of token m). */
+ss_status ss_quant_group_act(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, void* Xq, int64_t ldq,
+                             float* sx, void* stream);
+
+/* ss_spgemm_tiled_block -- the weight-sparse block-scaled product:
+ *   Y[m][n] = sum over g of acc_g[m][n] * fl32(sx[m][g] * sw[n / 128][g]),
+ *   acc_g = sum over the 128 positions of group g of Xq[m][k] W'[n][k] (float32),
+ * accumulated in float32 in group order and rounded to y_dt (BF16 nearest-even
+ * or F32). tvals / tmeta from ss_prune24_block for N rows and Kc; dense = Xq
+ * [M][Kc] FP8E4M3 (ldd bytes); sx, sw as written by the two calls above.
+ * 0 < Kc, Kc % SS_KALIGN == 0; the dense operand must span less than 4 GiB;
+ * Y [M][N] (ldy elements) as in ss_spgemm. Any M >= 0 (the prefill kernel
+ * serves every size). */
+ss_status ss_spgemm_tiled_block(int64_t M, int64_t N, int64_t Kc, const void* tvals, const uint8_t* tmeta,
+                                const void* dense, int64_t ldd, const float* sx, const float* sw, ss_dtype y_dt,
+                                void* Y, int64_t ldy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,14 +66,19 @@ lib.ss_spgemm_tiled_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _int]
 lib.ss_spgemm_tiled_workspace_bytes.restype = _i64
 lib.ss_spgemm_tiled_ws.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp,
                                    _i64, _vp]
+lib.ss_prune24_block.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _fp, _vp]
+lib.ss_quant_group_act.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _fp, _vp]
+lib.ss_spgemm_tiled_block.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
 for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm", "ss_pack_sparse",
-           "ss_prune24_act_tiled", "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_ws"):
+           "ss_prune24_act_tiled", "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_ws",
+           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block"):
     getattr(lib, _f).restype = _int
 
 EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_error", "ss_version",
            "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm",
            "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_prune24_act_tiled",
-           "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_workspace_bytes", "ss_spgemm_tiled_ws")
+           "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_workspace_bytes", "ss_spgemm_tiled_ws",
+           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block")
 
 
 class SSError(RuntimeError):
@@ -274,3 +279,50 @@ def slide_decompose_tiled(W: torch.Tensor, n: int, out_dtype="i8", out=None):
     _check(lib.ss_slide_decompose_tiled(_ptr(W), dtype_code(W.dtype), rows, K, _ld(W), n, o, _ptr(tv), _ptr(tm),
                                         _ptr(scale), _stream(W.device)))
     return tv, tm, scale
+
+
+# ---- block-scaled FP8 (128 x 128 weight blocks, per-token groups of 128) -------------------------------------
+
+BLOCK = 128
+
+
+def prune24_block(W: torch.Tensor, out=None):
+    """Offline 2:4 prune with FP8 codes scaled per 128 x 128 block, written in the tiled layout.
+    Returns (tvals, tmeta, sw [ceil(rows / 128), Kc / 128])."""
+    rows, K = W.shape
+    Kc = lifted_k(K, 2)
+    if out is None:
+        nv, nm = tiled_bytes(rows, Kc, SS_FP8E4M3)
+        tv = torch.empty(nv, dtype=torch.uint8, device=W.device)
+        tm = torch.empty(nm, dtype=torch.uint8, device=W.device)
+        sw = torch.empty(((rows + BLOCK - 1) // BLOCK, Kc // BLOCK), dtype=torch.float32, device=W.device)
+    else:
+        tv, tm, sw = out
+    _check(lib.ss_prune24_block(_ptr(W), dtype_code(W.dtype), rows, K, _ld(W), _ptr(tv), _ptr(tm), _ptr(sw),
+                                _stream(W.device)))
+    return tv, tm, sw
+
+
+def quant_group_act(X: torch.Tensor, out=None):
+    """Online FP8 codes with one scale per token and group of 128 positions.
+    Returns (Xq [M, Kc] float8_e4m3fn, sx [M, Kc / 128])."""
+    M, K = X.shape
+    Kc = lifted_k(K, 2)
+    if out is None:
+        Xq = torch.empty((M, Kc), dtype=torch.float8_e4m3fn, device=X.device)
+        sx = torch.empty((M, Kc // BLOCK), dtype=torch.float32, device=X.device)
+    else:
+        Xq, sx = out
+    _check(lib.ss_quant_group_act(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), _ptr(Xq), _ld(Xq), _ptr(sx),
+                                  _stream(X.device)))
+    return Xq, sx
+
+
+def spgemm_tiled_block(M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta: torch.Tensor, dense: torch.Tensor,
+                       sx: torch.Tensor, sw: torch.Tensor, y_dtype="bf16", out=None):
+    """Y [M, N]: the weight-sparse block-scaled FP8 product."""
+    y = dtype_code(y_dtype)
+    Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
+    _check(lib.ss_spgemm_tiled_block(M, N, Kc, _ptr(tvals), _ptr(tmeta), _ptr(dense), _ld(dense), _ptr(sx), _ptr(sw),
+                                     y, _ptr(Y), _ld(Y), _stream(dense.device)))
+    return Y

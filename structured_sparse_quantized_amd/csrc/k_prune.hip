@@ -323,6 +323,53 @@ hipError_t launch_prune24_tiled(bool in_bf16, int out, const void* W, int64_t ld
   }
 }
 
+// Block-scaled FP8 weights (LLM Compressor guide, W8A8-FP8_BLOCK): 2:4 prune along K, then FP8 codes with
+// one scale per block of 128 rows x 128 positions, written to the tiled operand. One workgroup per block:
+// its 1024 units (128 rows x 8) are held in registers, 4 per thread, while the block absmax is reduced
+// (a magnitude prune keeps every group maximum, so the absmax of the raw block is the block's). Blocks
+// past the last scale group are the tiled layout's step padding and rows past the end up to the next
+// 16 are zero: both are written as zero units (index words of positions 0 and 1).
+template <typename TIn>
+__global__ __launch_bounds__(kBlock) void prune24_block_kernel(const TIn* __restrict__ W, int64_t ldw, int rows,
+                                                               int K, int KS, int KSP, uint8_t* __restrict__ tv,
+                                                               uint8_t* __restrict__ tm, float* __restrict__ sw) {
+  __shared__ float red[kBlock / 64];
+  const int g = blockIdx.x, b = blockIdx.y;  // scale group (= step of the tiled operand), 128-row block
+  const int rows16 = (rows + 15) & ~15;
+  Unit<TIn> u[4];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int lu = threadIdx.x + kBlock * j, row = b * 128 + (lu >> 3), unit = g * 8 + (lu & 7);
+    u[j] = Unit<TIn>{};
+    if (row < rows && g < KS) load_unit(u[j], W + (int64_t)row * ldw, unit, K);
+    amax = fmaxf(amax, unit_absmax(u[j]));
+  }
+  amax = block_max(amax, red);
+  const bool zero = amax == 0.0f;
+  const float inv = zero ? 0.0f : Quant<true>::Q / amax;
+  if (threadIdx.x == 0 && g < KS) sw[(int64_t)b * KS + g] = zero ? 0.0f : amax / Quant<true>::Q;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int lu = threadIdx.x + kBlock * j, row = b * 128 + (lu >> 3), unit = g * 8 + (lu & 7);
+    if (row < rows16) emit_unit_tiled<TIn, 1>(u[j], zero, inv, tv, tm, row, unit, KSP);
+  }
+}
+
+hipError_t launch_prune24_block(bool in_bf16, const void* W, int64_t ldw, int64_t rows, int64_t K, int64_t Kc,
+                                void* tv, uint8_t* tm, float* sw, hipStream_t st) {
+  const int KS = (int)(Kc / 128), KSP = (KS + 3) / 4 * 4;
+  const dim3 grid((unsigned)KSP, (unsigned)((rows + 127) / 128));
+  uint8_t* v = static_cast<uint8_t*>(tv);
+  if (in_bf16)
+    hipLaunchKernelGGL(prune24_block_kernel<uint16_t>, grid, dim3(kBlock), 0, st, static_cast<const uint16_t*>(W), ldw,
+                       (int)rows, (int)K, KS, KSP, v, tm, sw);
+  else
+    hipLaunchKernelGGL(prune24_block_kernel<float>, grid, dim3(kBlock), 0, st, static_cast<const float*>(W), ldw,
+                       (int)rows, (int)K, KS, KSP, v, tm, sw);
+  return hipGetLastError();
+}
+
 int num_cus_p() {
   // cached per device (the library may be used on several GPUs from several threads)
   constexpr int kMaxDev = 64;

@@ -219,7 +219,60 @@ hipError_t launch_ql(const TIn* X, int64_t ldx, int64_t M, int64_t K, int n, uin
   }
 }
 
+// Block-scaled FP8 activations (LLM Compressor guide, W8A8-FP8_BLOCK: one dynamic scale per token and
+// group of 128 positions along K): 16 lanes per group, 8 positions per lane, the group absmax reduced
+// across the 16 lanes; a workgroup covers 16 groups of one token (1-D grid: token-major). Positions past
+// K read as zero, so groups wholly past K (the padding up to Kc) get zero codes and scale 0.
+template <typename TIn>
+__global__ __launch_bounds__(kBlock) void quant_group_kernel(const TIn* __restrict__ X, int64_t ldx, int K, int G,
+                                                             int gblocks, uint8_t* __restrict__ Xq, int64_t ldq,
+                                                             float* __restrict__ sx) {
+  using V = InVec<TIn>;
+  const int64_t m = blockIdx.x / gblocks;
+  const int g = (blockIdx.x % gblocks) * (kBlock / 16) + (threadIdx.x >> 4), l = threadIdx.x & 15;
+  if (g >= G) return;  // whole 16-lane groups leave together
+  const int k0 = g * 128 + l * 8;
+  const TIn* xr = X + m * ldx;
+  float v[8];
+  if (k0 + 8 <= K) {
+#pragma unroll
+    for (int h = 0; h < 8 / V::E; ++h) {
+      const uint4 q = reinterpret_cast<const uint4*>(xr + k0)[h];
+#pragma unroll
+      for (int i = 0; i < V::E; ++i) v[h * V::E + i] = V::get(q, i);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (k0 + i < K) ? V::scalar(xr + k0 + i) : 0.0f;
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 16));
+  const bool zero = a == 0.0f;
+  const float inv = zero ? 0.0f : Quant<true>::Q / a;
+  uint2 c = make_uint2(0u, 0u);
+  if (!zero) c = make_uint2(Quant<true>::pack4(v[0], v[1], v[2], v[3], inv), Quant<true>::pack4(v[4], v[5], v[6], v[7], inv));
+  *reinterpret_cast<uint2*>(Xq + m * ldq + k0) = c;
+  if (l == 0) sx[m * G + g] = zero ? 0.0f : a / Quant<true>::Q;
+}
+
 }  // namespace
+
+hipError_t launch_quant_group(bool x_bf16, const void* X, int64_t ldx, int64_t M, int64_t K, void* Xq, int64_t ldq,
+                              int64_t Kc, float* sx, hipStream_t st) {
+  const int G = (int)(Kc / 128), gblocks = (G + kBlock / 16 - 1) / (kBlock / 16);
+  const dim3 grid((unsigned)(M * gblocks));
+  uint8_t* q = static_cast<uint8_t*>(Xq);
+  if (x_bf16)
+    hipLaunchKernelGGL(quant_group_kernel<uint16_t>, grid, dim3(kBlock), 0, st, static_cast<const uint16_t*>(X), ldx,
+                       (int)K, G, gblocks, q, ldq, sx);
+  else
+    hipLaunchKernelGGL(quant_group_kernel<float>, grid, dim3(kBlock), 0, st, static_cast<const float*>(X), ldx, (int)K,
+                       G, gblocks, q, ldq, sx);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_lift(bool x_bf16, bool fp8, const void* X, int64_t ldx, int64_t M, int64_t K, int n,
                              void* Xq, int64_t ldq, int64_t Kc, float* sx, hipStream_t st) {

@@ -35,6 +35,14 @@
 // registers one 4-step group ahead. Each step waits for the next step's stage,
 // then reads that stage's fragments while the current step's smfmacs run.
 //
+// Block-scaled FP8 (LLM Compressor guide, W8A8-FP8_BLOCK: one weight scale per
+// 128 x 128 block, one activation scale per token and group of 128 positions;
+// side W): a step is exactly one scale group, so the same kernel runs each
+// step's smfmacs from zero and adds the partial tile times s_x[m][step] *
+// s_w[n / 128][step] into float32 accumulators. The token scales of each
+// 4-step group reach LDS by DMA with the index words (one 256-byte load per
+// wave); the weight scale is one scalar load per wave and step.
+//
 // Decode kernel (side W, at most 64 tokens, when the tiled grid would leave
 // the chip idle): one 16-row block per workgroup of 8 waves; the waves split
 // the K steps in whole 4-step index groups, stream the sparse values straight
@@ -61,6 +69,8 @@ constexpr int TI = BM / WGM / 16, TJ = BN / WGN / 16;          // 4 x 4 instruct
 constexpr int PA = BM / 16 / NW, PB = BN / 8 / NW, LPW = PA + PB;  // LDS DMA loads per wave per step
 constexpr int A_BYTES = BM * 64, STAGE = A_BYTES + BN * 128;   // 32 KB
 constexpr int LDS = S * STAGE;                                 // 128 KB
+constexpr int SX_BYTES = 128 * 4 * 4;                          // block-scaled: token scales of one 4-step group
+constexpr int LDS_BS = LDS + 2 * SX_BYTES;
 static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN, "load split");
 static_assert(S >= 3 && S <= 5, "wait counts below assume 3..5 stages");
 
@@ -140,7 +150,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ v
         make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
 }
 
-template <int AB, int YT, bool SIDE_X>
+// BS: block-scaled FP8 (AB == 1, side W); sx is [C][KS] and sw [ceil(R / 128)][KS].
+template <int AB, int YT, bool SIDE_X, bool BS = false>
 __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS, const uint8_t* __restrict__ tv,
                                                             const uint8_t* __restrict__ tm, const uint8_t* __restrict__ bd,
                                                             int ldb, const float* __restrict__ sx,
@@ -201,6 +212,20 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
 #pragma unroll
     for (int t = 0; t < TI; ++t) m[t] = *reinterpret_cast<const MV*>(pmt[t] + (int64_t)g * MT::BLOCK);
   };
+  // Block-scaled: token scales of 4-step group g into LDS buffer g % 2 -- wave w brings tokens 16w ..
+  // 16w + 15, lane l token 16w + l / 4 and step 4g + l % 4 (clamped in bounds; never used past the end),
+  // so the buffer holds 16 bytes per token.
+  const float* sxrow = nullptr;
+  if constexpr (BS) sxrow = sx + (int64_t)min(c0 + wave * 16 + (lane >> 2), C - 1) * KS;
+  auto load_sx = [&](int g) {
+    if constexpr (BS)
+      __builtin_amdgcn_global_load_lds((const void*)(sxrow + min(4 * g + (lane & 3), KS - 1)),
+                                       (SS_LDS void*)((SS_LDS uint8_t*)smem + LDS + (g & 1) * SX_BYTES + wave * 256),
+                                       4, 0, 0);
+  };
+  // Block-scaled: this wave's weight-scale row (its 64 A rows lie in one 128-row block).
+  const float* swrow = nullptr;
+  if constexpr (BS) swrow = sw + (int64_t)min((r0 + wm * TI * 16) / 128, (R - 1) / 128) * KS;
 
   Acc acc[TI][TJ];
 #pragma unroll
@@ -230,6 +255,43 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
 #pragma unroll
       for (int t = 0; t < TI; ++t) acc[t][u] = mma_step<AB, Q>(f.a[t], f.b[u][0], f.b[u][1], acc[t][u], mcur[t]);
   };
+  // Block-scaled step, one column u of B at a time: its TI partial tiles from zero, then (READ) its B
+  // fragments and A fragment u are refilled from step knext's stage -- B in place, it is single-buffered
+  // to leave registers for the partials -- and the column is scaled into the accumulators.
+  static_assert(TI == TJ, "one A fragment refilled per B column");
+  v4i bq[TJ][2];
+  auto read_b = [&](int u, int k) {
+    const uint8_t* bb = smem + (k % S) * STAGE + A_BYTES + ((wn * TJ + u) * 2 + (r16 >> 3)) * 1024 + (r16 & 7) * 128;
+    bq[u][0] = *reinterpret_cast<const v4i*>(bb + swz(jj, r16) * 16);
+    bq[u][1] = *reinterpret_cast<const v4i*>(bb + swz(4 + jj, r16) * 16);
+  };
+  auto step_bs = [&](const v4i* acur, v4i* anxt, auto qc, auto readc, const float* sc, int knext) {
+    constexpr int Q = decltype(qc)::value;
+    constexpr bool READ = decltype(readc)::value;
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) {
+      Acc p[TI];
+#pragma unroll
+      for (int t = 0; t < TI; ++t) p[t] = mma_step<AB, Q>(acur[t], bq[u][0], bq[u][1], Acc{0, 0, 0, 0}, mcur[t]);
+      if constexpr (READ) {
+        read_b(u, knext);
+        anxt[u] = *reinterpret_cast<const v4i*>(smem + (knext % S) * STAGE + (wm * TI + u) * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int t = 0; t < TI; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[t][u][q] = __builtin_fmaf(p[t][q], sc[u], acc[t][u][q]);
+    }
+  };
+  // Block-scaled: the scales of step k for this lane's TJ B rows: s_x[token][k] * s_w[block][k].
+  auto read_scales = [&](float* sc, int k) {
+    if constexpr (BS) {
+      const float swk = swrow[min(k, KS - 1)];
+      const float* buf = reinterpret_cast<const float*>(smem + LDS + ((k >> 2) & 1) * SX_BYTES) + (k & 3);
+#pragma unroll
+      for (int u = 0; u < TJ; ++u) sc[u] = __fmul_rn(buf[((wn * TJ + u) * 16 + r16) * 4], swk);
+    }
+  };
 
   // Loads complete in issue order, so "stage k+1 has landed" is a wait until at
   // most N of this wave's loads are outstanding, N = the loads issued after
@@ -241,13 +303,14 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
     constexpr bool LAST = decltype(lastc)::value;
     constexpr int lo = Q + 6 - S, hi = Q + 3;
     constexpr int nm = LAST ? 0 : (hi >= 4 && lo <= 4 ? 1 : 0) + (hi >= 8 && lo <= 8 ? 1 : 0);
-    constexpr int N = (S - 3) * LPW + nm * TI;
+    constexpr int N = (S - 3) * LPW + nm * (TI + (BS ? 1 : 0));
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   };
   constexpr int RD = TI + 2 * TJ, NM = TI * TJ;
   // Step j (j + 1 < KSP): make stage j+1 resident, read its fragments while
   // multiplying step j.
-  auto step = [&](int j, auto qc, auto lastc, Frag& cur, Frag& nxt) {
+  float sc0[TJ], sc1[TJ];  // block-scaled: scales of the current and the next step
+  auto step = [&](int j, auto qc, auto lastc, Frag& cur, Frag& nxt, float* scur, float* snxt) {
     constexpr int Q = decltype(qc)::value;
     constexpr bool LAST = decltype(lastc)::value;
     // the fences keep the scheduler from moving loads across the wait and the barrier
@@ -256,14 +319,31 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
     __builtin_amdgcn_s_barrier();  // every wave's loads of stage j+1 landed; slot (j-1) % S is free
     __builtin_amdgcn_sched_barrier(0);
     issue(j + S - 1);
-    if (Q == 0 && !LAST) load_meta(mnxt, j / 4 + 1);
+    if (Q == 0 && !LAST) {
+      // block-scaled runs the last group in the loop too: its "next" group is a re-read, never used
+      const int gn = BS ? min(j / 4 + 1, KS4 - 1) : j / 4 + 1;
+      load_meta(mnxt, gn);
+      load_sx(gn);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    read(nxt, j + 1);
-    mma(cur, qc);
+    if constexpr (BS) {
+      read_scales(snxt, j + 1);
+      step_bs(cur.a, nxt.a, qc, std::true_type{}, scur, j + 1);
+      // per column: its smfmacs, its fragment reads, its FMAs
 #pragma unroll
-    for (int p = 0; p < NM; ++p) {
-      if (p < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one smfmac
+      for (int u = 0; u < TJ; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, TI, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4 * TI, 0);
+      }
+    } else {
+      read(nxt, j + 1);
+      mma(cur, qc);
+#pragma unroll
+      for (int p = 0; p < NM; ++p) {
+        if (p < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one smfmac
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -275,6 +355,7 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
   using Last = std::true_type;
 
   load_meta(mcur, 0);
+  load_sx(0);
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(s);
   Frag f0, f1;
@@ -284,21 +365,32 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
   }
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read(f0, 0);
-  for (int g = 0; g + 1 < KS4; ++g) {
+  if constexpr (BS) {
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) {
+      read_b(u, 0);
+      f0.a[u] = *reinterpret_cast<const v4i*>(smem + (wm * TI + u) * 1024 + lane * 16);
+    }
+  } else {
+    read(f0, 0);
+  }
+  read_scales(sc0, 0);
+  // Block-scaled: every group, the last included, runs this loop (its loads past the end re-read the last
+  // step in bounds and are never used), which keeps the register allocation of the loop for the whole K.
+  for (int g = 0; g + (BS ? 0 : 1) < KS4; ++g) {
     const int j = 4 * g;
-    step(j, Q0{}, NotLast{}, f0, f1);
-    step(j + 1, Q1{}, NotLast{}, f1, f0);
-    step(j + 2, Q2{}, NotLast{}, f0, f1);
-    step(j + 3, Q3{}, NotLast{}, f1, f0);
+    step(j, Q0{}, NotLast{}, f0, f1, sc0, sc1);
+    step(j + 1, Q1{}, NotLast{}, f1, f0, sc1, sc0);
+    step(j + 2, Q2{}, NotLast{}, f0, f1, sc0, sc1);
+    step(j + 3, Q3{}, NotLast{}, f1, f0, sc1, sc0);
 #pragma unroll
     for (int t = 0; t < TI; ++t) mcur[t] = mnxt[t];
   }
-  {
+  if constexpr (!BS) {
     const int j = KSP - 4;
-    step(j, Q0{}, Last{}, f0, f1);
-    step(j + 1, Q1{}, Last{}, f1, f0);
-    step(j + 2, Q2{}, Last{}, f0, f1);
+    step(j, Q0{}, Last{}, f0, f1, sc0, sc1);
+    step(j + 1, Q1{}, Last{}, f1, f0, sc1, sc0);
+    step(j + 2, Q2{}, Last{}, f0, f1, sc0, sc1);
     mma(f1, std::integral_constant<int, 3>{});
   }
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // no load may outlive the workgroup
@@ -311,9 +403,9 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
 #pragma unroll
   for (int t = 0; t < TI; ++t)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_a[t][q] = sa ? sa[min(r0 + (wm * TI + t) * 16 + 4 * jj + q, R - 1)] : 1.0f;
+    for (int q = 0; q < 4; ++q) s_a[t][q] = (sa && !BS) ? sa[min(r0 + (wm * TI + t) * 16 + 4 * jj + q, R - 1)] : 1.0f;
 #pragma unroll
-  for (int u = 0; u < TJ; ++u) s_b[u] = sb ? sb[min(c0 + (wn * TJ + u) * 16 + r16, C - 1)] : 1.0f;
+  for (int u = 0; u < TJ; ++u) s_b[u] = (sb && !BS) ? sb[min(c0 + (wn * TJ + u) * 16 + r16, C - 1)] : 1.0f;
 #pragma unroll
   for (int t = 0; t < TI; ++t) {
 #pragma unroll
@@ -325,7 +417,9 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
       int32_t yi[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if constexpr (YT == 2) {
+        if constexpr (BS) {
+          y[q] = acc[t][u][q];  // scaled step by step
+        } else if constexpr (YT == 2) {
           yi[q] = (int32_t)acc[t][u][q];
         } else {
           float f = (float)acc[t][u][q];
@@ -341,15 +435,16 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
   }
 }
 
-template <int AB, int YT, bool SIDE_X>
+template <int AB, int YT, bool SIDE_X, bool BS = false>
 hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb,
                   const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
-  auto kern = spgemm_kernel<AB, YT, SIDE_X>;
+  auto kern = spgemm_kernel<AB, YT, SIDE_X, BS>;
+  constexpr int lds = BS ? LDS_BS : LDS;
   // set at every launch: the attribute is per device, and the call is cheap and thread-safe
-  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
-  hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * NW), LDS, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, tr, tc);
+  hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * NW), lds, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, tr, tc);
   return hipGetLastError();
 }
 
@@ -714,6 +809,15 @@ static bool few_tokens(bool side_x, int64_t R, int64_t C) {
 }
 // The split-K path (with a workspace) serves the few-token products with more than 16 tokens.
 static bool use_splitk(bool side_x, int64_t R, int64_t C) { return few_tokens(side_x, R, C) && C > 16; }
+
+hipError_t launch_spgemm_tiled_block(int yt, int64_t R, int64_t C, int64_t Kc, const uint8_t* tv, const uint8_t* tm,
+                                     const void* bd, int64_t ldb_bytes, const float* sx, const float* sw, void* Y,
+                                     int64_t ldy, hipStream_t st) {
+  const uint8_t* b = static_cast<const uint8_t*>(bd);
+  const int r = (int)R, c = (int)C, ks = (int)(Kc / 128), lb = (int)ldb_bytes, ly = (int)ldy;
+  if (yt == 0) return tiled::launch<1, 0, false, true>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st);
+  return tiled::launch<1, 1, false, true>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st);
+}
 
 int64_t spgemm_tiled_workspace_bytes(bool side_x, int ab, int64_t R, int64_t C, int64_t Kc) {
   if (!use_splitk(side_x, R, C)) return 0;

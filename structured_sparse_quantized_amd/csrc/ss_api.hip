@@ -347,4 +347,61 @@ ss_status ss_spgemm_tiled_ws(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_
                           need > 0 ? workspace : nullptr, stream);
 }
 
+ss_status ss_prune24_block(const void* W, ss_dtype w_dt, int64_t rows, int64_t K, int64_t ldw, void* tvals,
+                           uint8_t* tmeta, float* sw, void* stream) {
+  if (w_dt != SS_F32 && w_dt != SS_BF16) return fail(SS_ERR_DTYPE, "input must be F32 or BF16");
+  if (rows < 0 || K < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (K % 4 != 0) return fail(SS_ERR_SHAPE, "K=%lld is not a multiple of 4", (long long)K);
+  if (rows > 0x7FFFFFF0LL || K > 0x3FFFFFF0LL) return fail(SS_ERR_SHAPE, "too large");
+  if (rows == 0 || K == 0) return ok();
+  ss_status s;
+  if ((s = check_mat("input", W, rows, K, ldw, esize(w_dt))) != SS_OK) return s;
+  if (!tvals || !tmeta) return fail(SS_ERR_NULL, "tiled outputs are NULL");
+  if (!aligned16(tvals) || !aligned16(tmeta)) return fail(SS_ERR_ALIGN, "tiled outputs are not 16-byte aligned");
+  if (!sw) return fail(SS_ERR_NULL, "sw is NULL");
+  const int64_t Kc = ss_lifted_k(K, 2);
+  return hip_status(ss::launch_prune24_block(w_dt == SS_BF16, W, ldw, rows, K, Kc, tvals, tmeta, sw,
+                                             (hipStream_t)stream),
+                    "ss_prune24_block launch");
+}
+
+ss_status ss_quant_group_act(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, void* Xq, int64_t ldq,
+                             float* sx, void* stream) {
+  if (x_dt != SS_F32 && x_dt != SS_BF16) return fail(SS_ERR_DTYPE, "input must be F32 or BF16");
+  if (M < 0 || K < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (M > 0x7FFFFFF0LL || K > 0x3FFFFFF0LL) return fail(SS_ERR_SHAPE, "too large");
+  if (M == 0 || K == 0) return ok();
+  const int64_t Kc = ss_lifted_k(K, 2);
+  if (M * ((Kc / 128 + 15) / 16) > 0x7FFFFFFFLL) return fail(SS_ERR_SHAPE, "too large");
+  ss_status s;
+  if ((s = check_mat("X", X, M, K, ldx, esize(x_dt))) != SS_OK) return s;
+  if ((s = check_mat("Xq", Xq, M, Kc, ldq, 1)) != SS_OK) return s;
+  if (!sx) return fail(SS_ERR_NULL, "sx is NULL");
+  return hip_status(ss::launch_quant_group(x_dt == SS_BF16, X, ldx, M, K, Xq, ldq, Kc, sx, (hipStream_t)stream),
+                    "ss_quant_group_act launch");
+}
+
+ss_status ss_spgemm_tiled_block(int64_t M, int64_t N, int64_t Kc, const void* tvals, const uint8_t* tmeta,
+                                const void* dense, int64_t ldd, const float* sx, const float* sw, ss_dtype y_dt,
+                                void* Y, int64_t ldy, void* stream) {
+  if (y_dt != SS_BF16 && y_dt != SS_F32) return fail(SS_ERR_DTYPE, "output must be BF16 or F32");
+  if (M < 0 || N < 0 || Kc < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (Kc % SS_KALIGN != 0) return fail(SS_ERR_SHAPE, "Kc=%lld is not a multiple of %d", (long long)Kc, SS_KALIGN);
+  if (M == 0 || N == 0) return ok();
+  if (Kc == 0) return fail(SS_ERR_SHAPE, "Kc must be positive");
+  if (M > 0x7FFFFFF0LL || N > 0x7FFFFFF0LL || ldy > 0x7FFFFFFFLL || Kc / 64 > 0x7FFFFFF0LL)
+    return fail(SS_ERR_SHAPE, "too large");
+  ss_status s;
+  if ((s = check_mat("dense", dense, M, Kc, ldd, 1)) != SS_OK) return s;
+  if ((uint64_t)(M - 1) * (uint64_t)ldd + (uint64_t)Kc > 0xFFFFFFFFull)
+    return fail(SS_ERR_UNSUPPORTED, "dense operand spans more than 4 GiB");
+  if ((s = check_mat("Y", Y, 1, N, ldy, esize(y_dt))) != SS_OK) return s;
+  if (!tvals || !tmeta) return fail(SS_ERR_NULL, "tiled operand is NULL");
+  if (!aligned16(tvals) || !aligned16(tmeta)) return fail(SS_ERR_ALIGN, "tiled operand is not 16-byte aligned");
+  if (!sx || !sw) return fail(SS_ERR_NULL, "block-scaled products need both scale arrays");
+  return hip_status(ss::launch_spgemm_tiled_block(y_dt == SS_BF16 ? 0 : 1, N, M, Kc, static_cast<const uint8_t*>(tvals),
+                                                  tmeta, dense, ldd, sx, sw, Y, ldy, (hipStream_t)stream),
+                    "ss_spgemm_tiled_block launch");
+}
+
 }  // extern "C"

@@ -45,4 +45,15 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
                                void* Y, int64_t ldy, void* ws, hipStream_t st);
 int64_t spgemm_tiled_workspace_bytes(bool side_x, int ab, int64_t R, int64_t C, int64_t Kc);
 
+// Block-scaled FP8 (128 x 128 weight blocks, per-token groups of 128; 2:4 weights, K' = K = Kc):
+// weight prep into the tiled operand with scales [ceil(rows / 128)][Kc / 128], activation codes [M][Kc] with
+// scales [M][Kc / 128], and the weight-sparse product (yt: 0 = bf16, 1 = f32).
+hipError_t launch_prune24_block(bool in_bf16, const void* W, int64_t ldw, int64_t rows, int64_t K, int64_t Kc,
+                                void* tv, uint8_t* tm, float* sw, hipStream_t st);
+hipError_t launch_quant_group(bool x_bf16, const void* X, int64_t ldx, int64_t M, int64_t K, void* Xq, int64_t ldq,
+                              int64_t Kc, float* sx, hipStream_t st);
+hipError_t launch_spgemm_tiled_block(int yt, int64_t R, int64_t C, int64_t Kc, const uint8_t* tv, const uint8_t* tm,
+                                     const void* bd, int64_t ldb_bytes, const float* sx, const float* sw, void* Y,
+                                     int64_t ldy, hipStream_t st);
+
 }  // namespace ss

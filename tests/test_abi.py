@@ -173,3 +173,34 @@ def test_tiled_validation_statuses():
     # dense operand beyond 32-bit byte offsets
     assert g(M=70000, ldd=65536, Kc=65536) == ss.SS_ERR_UNSUPPORTED
     assert g(M=0) == ss.SS_OK and g(N=0) == ss.SS_OK
+
+
+def test_block_scaled_validation_statuses():
+    import structured_sparse_quantized_amd as ss
+    L = ss.lib
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    P = L.ss_prune24_block
+    assert P(FAKE, ss.SS_I8, 4, 8, 8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_DTYPE
+    assert P(FAKE, ss.SS_F32, 4, 6, 8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
+    assert P(FAKE, ss.SS_F32, 4, 8, 6, FAKE, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
+    assert P(FAKE, ss.SS_F32, 4, 8, 8, FAKE, FAKE, None, None) == ss.SS_ERR_NULL
+    assert P(FAKE, ss.SS_F32, 4, 8, 8, None, FAKE, FAKE, None) == ss.SS_ERR_NULL
+    assert P(FAKE, ss.SS_F32, 4, 8, 8, odd, FAKE, FAKE, None) == ss.SS_ERR_ALIGN
+    assert P(None, ss.SS_F32, 4, 8, 8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_NULL
+    assert P(FAKE, ss.SS_F32, -1, 8, 8, FAKE, FAKE, FAKE, None) == ss.SS_ERR_SHAPE
+    assert P(FAKE, ss.SS_F32, 0, 8, 8, FAKE, FAKE, FAKE, None) == ss.SS_OK
+    Q = L.ss_quant_group_act
+    assert Q(FAKE, ss.SS_I8, 4, 100, 104, FAKE, 256, FAKE, None) == ss.SS_ERR_DTYPE
+    assert Q(FAKE, ss.SS_BF16, 4, 100, 104, FAKE, 100, FAKE, None) == ss.SS_ERR_SHAPE   # ldq < Kc = 256
+    assert Q(FAKE, ss.SS_BF16, 4, 100, 100, FAKE, 256, FAKE, None) == ss.SS_ERR_ALIGN   # 200-byte rows
+    assert Q(FAKE, ss.SS_BF16, 4, 100, 104, FAKE, 256, None, None) == ss.SS_ERR_NULL
+    assert Q(FAKE, ss.SS_BF16, 4, 100, 104, None, 256, FAKE, None) == ss.SS_ERR_NULL
+    assert Q(FAKE, ss.SS_BF16, 0, 100, 104, FAKE, 256, FAKE, None) == ss.SS_OK
+    def g(M=4, N=4, Kc=256, tv=FAKE, tm=FAKE, d=FAKE, ldd=256, sx=FAKE, sw=FAKE, y=ss.SS_BF16, Y=FAKE, ldy=8):
+        return L.ss_spgemm_tiled_block(M, N, Kc, tv, tm, d, ldd, sx, sw, y, Y, ldy, None)
+    assert g(y=ss.SS_I32) == ss.SS_ERR_DTYPE and g(y=ss.SS_FP8E4M3) == ss.SS_ERR_DTYPE
+    assert g(Kc=100) == ss.SS_ERR_SHAPE and g(Kc=0) == ss.SS_ERR_SHAPE and g(M=-1) == ss.SS_ERR_SHAPE
+    assert g(sx=None) == ss.SS_ERR_NULL and g(sw=None) == ss.SS_ERR_NULL and g(tm=None) == ss.SS_ERR_NULL
+    assert g(ldd=100) == ss.SS_ERR_SHAPE and g(tv=odd) == ss.SS_ERR_ALIGN and g(d=odd) == ss.SS_ERR_ALIGN
+    assert g(M=70000, ldd=65536, Kc=65536) == ss.SS_ERR_UNSUPPORTED
+    assert g(M=0) == ss.SS_OK and g(N=0) == ss.SS_OK
