@@ -305,7 +305,7 @@ def main():
 def suite(ss, torch, dev, reps=10):
     """Layer-shaped products on synthetic data (seeded on the GPU): Llama-3.1-8B-shaped 2:4 FP8 weight
     GEMMs at M = 2048..16384 against dense FP8 (hipBLASLt through torch._scaled_mm, same per-token /
-    per-channel scales); Qwen2.5-7B-shaped 4:6 and 8:10 INT8 GEMMs at decode and prefill M; the
+    per-channel scales) and in block-scaled FP8; Qwen2.5-7B-shaped 4:6 and 8:10 INT8 GEMMs at decode and prefill M; the
     sparse-activation FP8 layer; quant+lift bandwidth on a large batch and a plain device copy."""
     import synth
     print("[bench] layer suite", file=sys.stderr, flush=True)
@@ -362,6 +362,38 @@ def suite(ss, torch, dev, reps=10):
                          "dense_tokens_per_s": M / (tot_dn * 1e-6), "speedup": tot_dn / tot_sp}
         torch.cuda.empty_cache()
     res["llama31_8b_24_fp8"] = llama
+    # the same Llama-shaped 2:4 layers with block-scaled FP8 (LLM Compressor W8A8-FP8_BLOCK: 128 x 128 weight
+    # blocks, per-token groups of 128): weight prep, group quant and the product with per-step promotion
+    blk = {}
+    for M in (4096, 8192):
+        rows, tot = [], 0.0
+        for name, (K, Nout) in synth.LLAMA31_8B_LINEARS.items():
+            W = randn((Nout, K), 0.02)
+            tv, tm, sw = ss.prune24_block(W)
+            t_w = timed(lambda: ss.prune24_block(W, out=(tv, tm, sw)), n=3) if M == 4096 else None
+            del W
+            Kc = ss.lifted_k(K, 2)
+            X = randn((M, K), 1.0, torch.bfloat16)
+            xq = torch.empty((M, Kc), dtype=torch.float8_e4m3fn, device=dev)
+            sx = torch.empty((M, Kc // 128), dtype=torch.float32, device=dev)
+            Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+            t_q = timed(lambda: ss.quant_group_act(X, out=(xq, sx)))
+            t_sp = timed(lambda: ss.spgemm_tiled_block(M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y))
+            hw = 2.0 * M * Nout * Kc
+            qbytes = 2 * M * K + M * Kc + 4 * M * (Kc // 128)
+            row = {"layer": name, "K": K, "N": Nout, "quant_group_us": t_q, "quant_group_GBs": qbytes / t_q / 1e3,
+                   "sparse_gemm_us": t_sp, "sparse_TOPS_dense_equiv": hw / t_sp / 1e6,
+                   "sparse_frac_of_10070": hw / t_sp / 1e6 / 10070.0}
+            if t_w is not None:
+                wbytes = 4 * Nout * K + Nout * Kc // 2 + Nout * Kc // 8 + 4 * ((Nout + 127) // 128) * (Kc // 128)
+                row.update({"prune24_block_us": t_w, "prune24_block_GBs": wbytes / t_w / 1e3})
+            rows.append(row)
+            tot += t_q + t_sp
+            del tv, tm, sw, X, xq, sx, Y
+        blk[str(M)] = {"layers": rows, "sparse_tokens_per_s": M / (tot * 1e-6),
+                       "time_vs_per_channel_24_fp8": llama[str(M)]["sparse_tokens_per_s"] / (M / (tot * 1e-6))}
+        torch.cuda.empty_cache()
+    res["llama31_8b_24_fp8_block"] = blk
     # the same Llama-shaped layers with 6:8 (K' = 1.5 K) at M >= 4096, INT8 and FP8, against dense
     llama68 = {}
     for q in ("i8", "fp8"):
