@@ -98,6 +98,22 @@ __global__ __launch_bounds__(kBlock, (PIPE || VPT > 4) ? 2 : (VPT > 2 ? 4 : 8)) 
       }
       if (tail0 + tid < K) qr[tail0 + tid] = (uint8_t)code(ctail);
       for (int c = K + tid; c < Kc; c += kBlock) qr[c] = 0;
+    } else if (N == 4 && E == 8 && (K & 7) == 0) {
+      // 6:8 from bf16 with whole 8-groups: a thread's vector is one group g, and its three windows
+      // (positions 2w .. 2w+3) are bytes 0-3, 2-5 and 4-7 of its eight codes -- written straight to
+      // X'[12g .. 12g+11] without the LDS gather
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int vi = tid + i * kBlock;
+        if (vi < nvec) {
+          const uint32_t lo = code4(cur[i], 0), hi = code4(cur[i], 4);
+          uint32_t* o = reinterpret_cast<uint32_t*>(qr + vi * 12);
+          o[0] = lo;
+          o[1] = (lo >> 16) | (hi << 16);
+          o[2] = hi;
+        }
+      }
+      for (int c = kl + tid; c < Kc; c += kBlock) qr[c] = 0;
     } else {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
@@ -183,7 +199,9 @@ hipError_t launch_n(const TIn* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq
   constexpr int E = InVec<TIn>::E;
   const int64_t vpt = (K / E + kBlock - 1) / kBlock;
   const int64_t kpad = (K + 2 * N - 1) / (2 * N) * (2 * N);
-  const size_t lds = (N == 2) ? 0 : (size_t)((kpad + 4 + 15) / 16 * 16);
+  // codes staged in LDS for the gather, except without a lift and for 6:8 from bf16 with whole 8-groups
+  const bool reg_lift = N == 4 && E == 8 && K % 8 == 0;
+  const size_t lds = (N == 2 || reg_lift) ? 0 : (size_t)((kpad + 4 + 15) / 16 * 16);
   const bool fits = K < (1 << 30) && Kc < (1 << 30) && M < (1 << 30) && lds <= 64 * 1024 && vpt <= 12;
   if (!fits) {
     hipLaunchKernelGGL((quant_lift_long_kernel<TIn, FP8>), dim3((unsigned)M), dim3(kBlock), 0, st, X, ldx, K, N, Xq, ldq, Kc, sx);

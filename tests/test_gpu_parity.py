@@ -69,6 +69,22 @@ def test_quant_lift_padded_leading_dim(ss):
     assert np.array_equal(host(xq), exp_q) and np.array_equal(host(sx), exp_s)
 
 
+@pytest.mark.parametrize("q", ["i8", "fp8"])
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+@pytest.mark.parametrize("K", [203, 1002, 4094])
+def test_quant_lift_ragged_k_padded_rows(ss, K, n, q):
+    """bf16 rows whose length is not a multiple of 8 (so the last 2n-group is partial and, at 6:8, the
+    groups do not line up with 16-byte vectors): rows padded to a 16-byte stride."""
+    x = _x(K + n, 11, K, "bf16")
+    ld = -(-K // 8) * 8 + 8
+    big = np.zeros((11, ld), np.uint16)
+    big[:, :K] = x
+    xq, sx = ss.quant_lift_act(dev_bf16(big)[:, :K], n, q)
+    exp_q, exp_s = oracle.quant_lift_act(x, n, q)
+    assert np.array_equal(host(sx), exp_s)
+    assert np.array_equal(host(xq).view(np.uint8), exp_q.view(np.uint8))
+
+
 # ---------------------------------------------------------------- weight prep
 W_SHAPES = [(1, 8), (5, 24), (130, 520), (256, 512), (64, 4096), (3, 14336)]
 
