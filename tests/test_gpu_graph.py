@@ -1,0 +1,70 @@
+"""The online half of the path (quant+lift, then the sparse product) captured in a HIP graph: the calls
+are stateless, allocate nothing and record no memset, so a graph replays them. Each replay runs on new
+input contents written between replays, with eager work and synchronisations in between, and must equal
+eager calls on the same inputs bit for bit (INT8). Covers the prefill kernel, the few-token row-block
+kernel and the split-K kernel with a caller-owned workspace."""
+import numpy as np
+import pytest
+
+from helpers import have_gpu
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import structured_sparse_quantized_amd as m
+    return m
+
+
+# (tokens, channels, K, n): prefill 6:8; decode 4:6 at 1 token (row-block kernel) and 48 tokens (split-K)
+CASES = [(2048, 4096, 4096, 4), (1, 3584, 18944, 3), (48, 3584, 18944, 3), (40, 4608, 3584, 5)]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_graph_replays_match_eager(ss, case):
+    import torch
+    M, N, K, n = case
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(M + N + K + n)
+    W = torch.randn((N, K), generator=gen, device=dev) * 0.02
+    tv, tm, sw = ss.slide_decompose_tiled(W, n, "i8")
+    Kc = ss.lifted_k(K, n)
+    X = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((M, Kc), dtype=torch.int8, device=dev)
+    sx = torch.empty(M, dtype=torch.float32, device=dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    need = ss.spgemm_tiled_workspace_bytes(ss.SS_SPARSE_W, M, N, Kc, "i8")
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else False
+    if M == 48:
+        assert need > 0, "this case is meant to take the split-K path"
+
+    def path():
+        ss.quant_lift_act(X, n, "i8", out=(xq, sx))
+        ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, xq, sx, sw, "bf16", out=Y, workspace=ws)
+
+    X.copy_(torch.randn((M, K), generator=gen, device=dev))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        path()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        X.copy_(torch.randn((M, K), generator=gen, device=dev) * (1.0 + rep))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = Y.clone()
+        got_q, got_s = xq.clone(), sx.clone()
+        # eager on the same input, into fresh buffers
+        eq, es = ss.quant_lift_act(X, n, "i8")
+        ey = ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, eq, es, sw, "bf16")
+        torch.cuda.synchronize()
+        assert torch.equal(got_q, eq) and torch.equal(got_s, es), rep
+        assert torch.equal(got.view(torch.int16), ey.view(torch.int16)), rep
+    assert np.isfinite(Y.float().cpu().numpy()).all()
