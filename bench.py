@@ -457,11 +457,20 @@ def suite(ss, torch, dev, reps=10):
                 t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y,
                                                      workspace=ws))
                 wbytes = tv.numel() + tm.numel()
-                qwen.append({"pattern": f"{2 * n - 2}:{2 * n}", "layer": name, "M": M, "K": K, "K_prime": Kc,
-                             "N": Nout, "quant_lift_us": t_q, "sparse_gemm_us": t_sp, "split_k_workspace_bytes": need,
-                             "sparse_TOPS_dense_equiv": 2.0 * M * Nout * Kc / t_sp / 1e6,
-                             "weight_stream_GBs": wbytes / t_sp / 1e3,
-                             "tokens_per_s": M / ((t_q + t_sp) * 1e-6)})
+                row = {"pattern": f"{2 * n - 2}:{2 * n}", "layer": name, "M": M, "K": K, "K_prime": Kc,
+                       "N": Nout, "quant_lift_us": t_q, "sparse_gemm_us": t_sp, "split_k_workspace_bytes": need,
+                       "sparse_TOPS_dense_equiv": 2.0 * M * Nout * Kc / t_sp / 1e6,
+                       "weight_stream_GBs": wbytes / t_sp / 1e3,
+                       "tokens_per_s": M / ((t_q + t_sp) * 1e-6)}
+                if M <= 64:  # decode: the quant+lift / product pair replayed from a HIP graph (no launch gaps)
+                    graph = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(graph):
+                        ss.quant_lift_act(X, n, "i8", out=(xq, sx))
+                        ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y, workspace=ws)
+                    t_g = timed(graph.replay)
+                    row.update({"graph_pair_us": t_g, "graph_tokens_per_s": M / (t_g * 1e-6)})
+                    del graph
+                qwen.append(row)
                 del X, xq, sx, Y, ws
             del tv, tm
             torch.cuda.empty_cache()
