@@ -265,6 +265,27 @@ ss_status ss_spgemm_tiled_ws(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_
                              const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
                              ss_dtype y_dt, void* Y, int64_t ldy, void* workspace, int64_t ws_bytes, void* stream);
 
+/* ss_quant_lift_spgemm_decode -- few-token layer in one launch: ss_quant_lift_act
+ * (per-token codes, lift to K' = ss_lifted_k(K, n)) followed by the
+ * weight-sparse ss_spgemm_tiled, with the quantisation and the lift done by
+ * every workgroup of the product into LDS (the SlideSparse blog, section 3.2,
+ * fuses the lift into the quantisation; here both move into the product). The
+ * results equal the two calls bit for bit (INT8 and FP8: the same arithmetic
+ * and the same sum order as the few-token product). X [M][K] F32 or BF16 (ldx
+ * elements); q_dt I8 or FP8E4M3; tvals / tmeta / sw: the weight operand of
+ * ss_slide_decompose_tiled for N rows, K' and q_dt; y_dt BF16, F32 or I32 (I8
+ * only: the raw accumulator); Y [M][N] (ldy elements) as in ss_spgemm;
+ * sx_out: NULL or M floats that receive the per-token scales. Limits:
+ * 1 <= M <= 4, M * K' <= 131072, K <= 20480 (BF16) / 16384 (F32), else
+ * SS_ERR_UNSUPPORTED (then use the two calls). Every workgroup repeats the
+ * quantisation, so the call pays off where launches dominate: one or two
+ * tokens on layers with a short weight stream (measured ~2x on
+ * Qwen2.5-7B-shaped qkv at 1-2 tokens, 1.05-1.1x on gate_up and even on down
+ * at 1 token); with long K and more tokens the two calls are faster. */
+ss_status ss_quant_lift_spgemm_decode(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, int n,
+                                      ss_dtype q_dt, const void* tvals, const uint8_t* tmeta, const float* sw, int64_t N,
+                                      ss_dtype y_dt, void* Y, int64_t ldy, float* sx_out, void* stream);
+
 /* ---- Block-scaled FP8 -------------------------------------------------------
  * The W8A8-FP8_BLOCK scheme of the LLM Compressor "compression schemes" guide:
  * FP8 weights with one scale per block of 128 output channels x 128 positions

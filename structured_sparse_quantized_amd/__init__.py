@@ -69,16 +69,18 @@ lib.ss_spgemm_tiled_ws.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, 
 lib.ss_prune24_block.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _fp, _vp]
 lib.ss_quant_group_act.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _fp, _vp]
 lib.ss_spgemm_tiled_block.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
+lib.ss_quant_lift_spgemm_decode.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp, _vp, _fp, _i64, _int, _vp, _i64,
+                                            _fp, _vp]
 for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm", "ss_pack_sparse",
            "ss_prune24_act_tiled", "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_ws",
-           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block"):
+           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode"):
     getattr(lib, _f).restype = _int
 
 EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_error", "ss_version",
            "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm",
            "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_prune24_act_tiled",
            "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_workspace_bytes", "ss_spgemm_tiled_ws",
-           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block")
+           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode")
 
 
 class SSError(RuntimeError):
@@ -244,6 +246,18 @@ def spgemm_tiled(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta:
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.ss_spgemm_tiled_ws(side, M, N, Kc, ab, _ptr(tvals), _ptr(tmeta), _ptr(dense), _ld(dense),
                                   _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _ptr(ws), nbytes, _stream(dense.device)))
+    return Y
+
+
+def quant_lift_spgemm_decode(X: torch.Tensor, n: int, tvals: torch.Tensor, tmeta: torch.Tensor, sw: torch.Tensor,
+                             N: int, q_dtype="i8", y_dtype="bf16", out=None, sx_out=None):
+    """Few tokens (1..4): quant+lift and the weight-sparse product in one launch; Y [M, N]."""
+    M, K = X.shape
+    y = dtype_code(y_dtype)
+    Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=X.device)
+    _check(lib.ss_quant_lift_spgemm_decode(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), n, dtype_code(q_dtype),
+                                           _ptr(tvals), _ptr(tmeta), _ptr(sw), N, y, _ptr(Y), _ld(Y), _ptr(sx_out),
+                                           _stream(X.device)))
     return Y
 
 

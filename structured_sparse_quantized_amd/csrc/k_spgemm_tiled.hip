@@ -557,6 +557,196 @@ hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, co
   return hipGetLastError();
 }
 
+// Few tokens, quant+lift fused in (SlideSparse blog section 3.2 fuses the lift into the quantisation; here
+// both move into the product's prologue, which removes a launch and the X' round trip when the launches,
+// not the bytes, dominate): every workgroup reads the M <= 4 bf16/f32 token rows itself, reduces their
+// absmax, and writes their codes at the lifted positions X'[4(n-1)g + 4w + j] = q(X[2n g + 2w + j]) into
+// LDS; then, persistent, it runs the row-block product for row blocks blockIdx.x, + gridDim.x, ...,
+// reading the dense operand from LDS. Same arithmetic as quant_lift_kernel and decode_kernel<AB, YT, 1>
+// (same per-wave K split and partial-sum order), so the results equal the two calls bit for bit.
+constexpr int FMAXM = 4;  // tokens
+// 16-byte vectors of a token row held per thread: K <= 20480 (bf16) / 16384 (f32)
+template <typename TIn> constexpr int fmaxv() { return sizeof(TIn) == 2 ? 5 : 8; }
+
+template <int AB, int YT, typename TIn>
+__global__ __launch_bounds__(64 * NW, 1) void fused_decode_kernel(int R, int M, int K, int n, int KS,
+                                                                  const TIn* __restrict__ X, int64_t ldx,
+                                                                  const uint8_t* __restrict__ tv,
+                                                                  const uint8_t* __restrict__ tm,
+                                                                  const float* __restrict__ sw, void* __restrict__ Y,
+                                                                  int ldy, float* __restrict__ sx_out) {
+  using Acc = typename tiled::Mma<AB>::Acc;
+  using MT = tiled::Meta<AB>;
+  using MV = typename MT::V;
+  using Qz = Quant<AB == 1>;
+  constexpr int E = 16 / (int)sizeof(TIn);  // elements per 16-byte vector
+  constexpr int FMAXV = fmaxv<TIn>();
+  extern __shared__ __align__(16) uint8_t xl[];  // [M][Kc] lifted codes
+  __shared__ Acc red[NW][64];
+  __shared__ float wmax[FMAXM][NW];
+  __shared__ float s_x[FMAXM];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, jj = lane >> 4;
+  const int Kc = KS * 128, nvec = K / E, tail0 = nvec * E;
+
+  for (int o = tid * 16; o < M * Kc; o += 64 * NW * 16) *reinterpret_cast<uint4*>(xl + o) = make_uint4(0, 0, 0, 0);
+  auto elem = [&](const uint4& q, int e) -> float {
+    if constexpr (E == 8) {
+      const uint32_t w = (&q.x)[e >> 1];
+      return bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFF)));
+    } else {
+      return __uint_as_float((&q.x)[e]);
+    }
+  };
+  // codes at their lifted positions: element k = 2n g + r sits in the windows w with 2w <= r <= 2w + 3,
+  // at 4(n-1) g + 4w + (r - 2w) = 4(n-1) g + r + 2w; (g, r) is advanced element by element (no division
+  // per element)
+  const int n2 = 2 * n, gstride = 4 * (n - 1);
+  auto place = [&](uint8_t* row, int g, int r, uint32_t code) {
+    const int wlo = r >= 3 ? (r - 2) >> 1 : 0, whi = min(r >> 1, n - 2);
+    const int base = gstride * g + r;
+    row[base + 2 * wlo] = (uint8_t)code;
+    if (whi > wlo) row[base + 2 * whi] = (uint8_t)code;
+  };
+  // one token at a time, its row read twice (the absmax pass, then the codes; the second read hits the
+  // cache), so few registers are live and four workgroups fit a CU, as for the row-block kernel
+  for (int m = 0; m < M; ++m) {
+    const TIn* xr = X + (int64_t)m * ldx;
+    float tl = 0.0f;
+    if (tail0 + tid < K) {
+      if constexpr (E == 8) tl = bf16_to_f32(xr[tail0 + tid]);
+      else tl = xr[tail0 + tid];
+    }
+    float a = fabsf(tl);
+#pragma unroll
+    for (int i = 0; i < FMAXV; ++i) {
+      const int vi = tid + i * 64 * NW;
+      if (vi < nvec) {
+        const uint4 q = reinterpret_cast<const uint4*>(xr)[vi];
+#pragma unroll
+        for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(elem(q, e)));
+      }
+    }
+    a = wave_max(a);
+    if (lane == 0) wmax[m][wave] = a;
+    __syncthreads();  // (the first one also orders the clearing of xl before the scatter below)
+    a = wmax[m][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) a = fmaxf(a, wmax[m][w]);
+    const bool zero = a == 0.0f;
+    const float inv = zero ? 0.0f : Qz::Q / a;
+    if (tid == 0) {
+      const float sxm = zero ? 0.0f : a / Qz::Q;
+      s_x[m] = sxm;
+      if (sx_out && blockIdx.x == 0) sx_out[m] = sxm;
+    }
+    uint8_t* row = xl + m * Kc;
+#pragma unroll 1
+    for (int i = 0; i < FMAXV; ++i) {
+      const int vi = tid + i * 64 * NW;
+      if (vi >= nvec) continue;
+      const uint4 q = reinterpret_cast<const uint4*>(xr)[vi];
+      uint32_t c[E / 4];
+#pragma unroll
+      for (int h = 0; h < E / 4; ++h)
+        c[h] = zero ? 0u : Qz::pack4(elem(q, 4 * h), elem(q, 4 * h + 1), elem(q, 4 * h + 2), elem(q, 4 * h + 3), inv);
+      if (n == 2) {
+#pragma unroll
+        for (int h = 0; h < E / 4; ++h) *reinterpret_cast<uint32_t*>(row + vi * E + 4 * h) = c[h];
+      } else if (E == 8 && n == 4) {  // one 8-group: windows are bytes 0-3, 2-5, 4-7 of its codes
+        uint32_t* o = reinterpret_cast<uint32_t*>(row + vi * 12);
+        o[0] = c[0];
+        o[1] = (c[0] >> 16) | (c[E / 4 - 1] << 16);
+        o[2] = c[E / 4 - 1];
+      } else {
+        const int k0 = vi * E;
+        int g = k0 / n2, r = k0 - g * n2;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          place(row, g, r, (c[e >> 2] >> (8 * (e & 3))) & 0xFF);
+          if (++r == n2) {
+            r = 0;
+            ++g;
+          }
+        }
+      }
+    }
+    if (tail0 + tid < K) {
+      const int k = tail0 + tid, g = k / n2;
+      place(row, g, k - g * n2, zero ? 0u : (uint32_t)Qz::code(tl, inv));
+    }
+  }
+  __syncthreads();
+
+  // the row-block product (decode_kernel with one 16-token column tile), dense operand from LDS
+  const int KS4 = (KS + 3) / 4, KSP = 4 * KS4, nrb = (R + 15) / 16;
+  const int g0 = KS4 * wave / NW, g1 = KS4 * (wave + 1) / NW;
+  for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
+  Acc acc = Acc{0, 0, 0, 0};
+  if (g0 < g1) {
+    const uint8_t* pa = tv + (int64_t)rb * KSP * 1024 + lane * 16;
+    const uint8_t* pm = tm + (int64_t)rb * KS4 * MT::BLOCK + lane * (4 * MT::WB);
+    const SS_LDS uint8_t* pb = (const SS_LDS uint8_t*)xl + min(r16, M - 1) * Kc + 16 * jj;
+    tiled::v4i A[4], B[4][2];
+    MV mcur, mnxt;
+    auto load_step = [&](int slot, int k) {
+      const int kb = min(k, KS - 1);
+      A[slot] = *reinterpret_cast<const tiled::v4i*>(pa + (int64_t)k * 1024);
+      B[slot][0] = *reinterpret_cast<const SS_LDS tiled::v4i*>(pb + kb * 128);
+      B[slot][1] = *reinterpret_cast<const SS_LDS tiled::v4i*>(pb + kb * 128 + 64);
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_step(q, 4 * g0 + q);
+    mcur = *reinterpret_cast<const MV*>(pm + (int64_t)g0 * MT::BLOCK);
+    mnxt = *reinterpret_cast<const MV*>(pm + (int64_t)min(g0 + 1, KS4 - 1) * MT::BLOCK);
+    for (int g = g0; g < g1; ++g) {
+      const int kn = min(4 * (g + 1), KSP - 4);
+      auto one = [&](auto qc) {
+        constexpr int Q = decltype(qc)::value;
+        acc = tiled::mma_step<AB, Q>(A[Q], B[Q][0], B[Q][1], acc, mcur);
+        load_step(Q, kn + Q);
+      };
+      one(std::integral_constant<int, 0>{});
+      one(std::integral_constant<int, 1>{});
+      one(std::integral_constant<int, 2>{});
+      one(std::integral_constant<int, 3>{});
+      mcur = mnxt;
+      mnxt = *reinterpret_cast<const MV*>(pm + (int64_t)min(g + 2, KS4 - 1) * MT::BLOCK);
+    }
+  }
+  // Wait states between the last smfmac and the LDS store that reads its result: inside this row-block
+  // loop the compiler emitted the store right after the loop's exit branch with none (the smfmac result
+  // is not readable by a DS instruction for several cycles), so they are written out here.
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    Acc sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) sum += red[w][lane];
+    const int ar = rb * 16 + 4 * jj, bc = r16;
+    if (bc < M) {
+      float y[4];
+      int32_t yi[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (YT == 2) {
+          yi[q] = (int32_t)sum[q];
+        } else {
+          float f = (float)sum[q];
+          f = __fmul_rn(f, s_x[bc]);
+          f = __fmul_rn(f, sw[min(ar + q, R - 1)]);
+          y[q] = f;
+        }
+      }
+      store_out<YT, false>(Y, ldy, ar, bc, R, y, yi);
+    }
+  }
+  __syncthreads();  // red is rewritten by the next row block
+  }
+}
+
 }  // namespace decode
 
 // Split-K product for a few tokens (side W, C <= 64). A workgroup of 8 waves
@@ -817,6 +1007,42 @@ hipError_t launch_spgemm_tiled_block(int yt, int64_t R, int64_t C, int64_t Kc, c
   const int r = (int)R, c = (int)C, ks = (int)(Kc / 128), lb = (int)ldb_bytes, ly = (int)ldy;
   if (yt == 0) return tiled::launch<1, 0, false, true>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st);
   return tiled::launch<1, 1, false, true>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st);
+}
+
+bool quant_lift_spgemm_fits(bool x_bf16, int64_t M, int64_t K, int64_t Kc) {
+  const int64_t max_k = x_bf16 ? 8 * decode::fmaxv<uint16_t>() * 64 * decode::NW : 4 * decode::fmaxv<float>() * 64 * decode::NW;
+  return M >= 1 && M <= decode::FMAXM && M * Kc <= 131072 && K <= max_k;
+}
+
+hipError_t launch_quant_lift_spgemm(bool x_bf16, int ab, int yt, const void* X, int64_t ldx, int64_t M, int64_t K, int n,
+                                    int64_t N, int64_t Kc, const uint8_t* tv, const uint8_t* tm, const float* sw,
+                                    void* Y, int64_t ldy, float* sx_out, hipStream_t st) {
+  const int R = (int)N, m = (int)M, k = (int)K, ks = (int)(Kc / 128), ly = (int)ldy;
+  const size_t lds = (size_t)(M * Kc);
+  // persistent, two workgroups a CU where the LDS holds two (each quantises the tokens once; measured
+  // against one row block per workgroup and against up to four a CU, equal or faster on every shape)
+  const int64_t per_cu = 2 * (int64_t)(lds + 9 * 1024) <= 160 * 1024 ? 2 : 1;
+  const int64_t nrb = (N + 15) / 16;
+  const unsigned grid = (unsigned)std::min<int64_t>(nrb, per_cu * num_cus_p());
+  auto go = [&](auto kern, const auto* x) -> hipError_t {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * decode::NW), lds, st, R, m, k, n, ks, x, ldx, tv, tm, sw, Y, ly,
+                       sx_out);
+    return hipGetLastError();
+  };
+  const uint16_t* xb = static_cast<const uint16_t*>(X);
+  const float* xf = static_cast<const float*>(X);
+#define SS_FD(AB_, YT_) \
+  return x_bf16 ? go(decode::fused_decode_kernel<AB_, YT_, uint16_t>, xb) : go(decode::fused_decode_kernel<AB_, YT_, float>, xf)
+  if (ab == 0) {
+    if (yt == 0) SS_FD(0, 0);
+    if (yt == 1) SS_FD(0, 1);
+    SS_FD(0, 2);
+  }
+  if (yt == 0) SS_FD(1, 0);
+  SS_FD(1, 1);
+#undef SS_FD
 }
 
 int64_t spgemm_tiled_workspace_bytes(bool side_x, int ab, int64_t R, int64_t C, int64_t Kc) {

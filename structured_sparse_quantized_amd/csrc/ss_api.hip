@@ -404,4 +404,33 @@ ss_status ss_spgemm_tiled_block(int64_t M, int64_t N, int64_t Kc, const void* tv
                     "ss_spgemm_tiled_block launch");
 }
 
+ss_status ss_quant_lift_spgemm_decode(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, int n,
+                                      ss_dtype q_dt, const void* tvals, const uint8_t* tmeta, const float* sw, int64_t N,
+                                      ss_dtype y_dt, void* Y, int64_t ldy, float* sx_out, void* stream) {
+  if (n < 2 || n > 8) return fail(SS_ERR_PATTERN, "n=%d outside 2..8", n);
+  if (x_dt != SS_F32 && x_dt != SS_BF16) return fail(SS_ERR_DTYPE, "input must be F32 or BF16");
+  if (q_dt != SS_I8 && q_dt != SS_FP8E4M3) return fail(SS_ERR_DTYPE, "codes must be I8 or FP8E4M3");
+  if (y_dt != SS_BF16 && y_dt != SS_F32 && y_dt != SS_I32) return fail(SS_ERR_DTYPE, "output must be BF16, F32 or I32");
+  if (y_dt == SS_I32 && q_dt != SS_I8) return fail(SS_ERR_DTYPE, "I32 output needs I8 codes");
+  if (M < 0 || K < 0 || N < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (M == 0 || N == 0) return ok();
+  if (K == 0) return fail(SS_ERR_SHAPE, "K must be positive");
+  if (N > 0x7FFFFFF0LL || K > 0x3FFFFFF0LL || ldy > 0x7FFFFFFFLL) return fail(SS_ERR_SHAPE, "too large");
+  const int64_t Kc = ss_lifted_k(K, n);
+  if (!ss::quant_lift_spgemm_fits(x_dt == SS_BF16, M, K, Kc))
+    return fail(SS_ERR_UNSUPPORTED, "M=%lld, K=%lld: the fused path takes 1..4 tokens with M*K' <= 131072 and K <= %d",
+                (long long)M, (long long)K, x_dt == SS_BF16 ? 20480 : 16384);
+  ss_status s;
+  if ((s = check_mat("X", X, M, K, ldx, esize(x_dt))) != SS_OK) return s;
+  if ((s = check_mat("Y", Y, 1, N, ldy, esize(y_dt))) != SS_OK) return s;
+  if (!tvals || !tmeta) return fail(SS_ERR_NULL, "tiled operand is NULL");
+  if (!aligned16(tvals) || !aligned16(tmeta)) return fail(SS_ERR_ALIGN, "tiled operand is not 16-byte aligned");
+  if (!sw) return fail(SS_ERR_NULL, "sw is NULL");
+  return hip_status(ss::launch_quant_lift_spgemm(x_dt == SS_BF16, q_dt == SS_I8 ? 0 : 1,
+                                                 y_dt == SS_BF16 ? 0 : y_dt == SS_F32 ? 1 : 2, X, ldx, M, K, n, N, Kc,
+                                                 static_cast<const uint8_t*>(tvals), tmeta, sw, Y, ldy, sx_out,
+                                                 (hipStream_t)stream),
+                    "ss_quant_lift_spgemm_decode launch");
+}
+
 }  // extern "C"

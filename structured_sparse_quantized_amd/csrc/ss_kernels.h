@@ -45,6 +45,12 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
                                void* Y, int64_t ldy, void* ws, hipStream_t st);
 int64_t spgemm_tiled_workspace_bytes(bool side_x, int ab, int64_t R, int64_t C, int64_t Kc);
 
+// Few-token quant+lift fused into the weight-sparse row-block product (ab: 0 = int8, 1 = fp8; yt as above).
+bool quant_lift_spgemm_fits(bool x_bf16, int64_t M, int64_t K, int64_t Kc);
+hipError_t launch_quant_lift_spgemm(bool x_bf16, int ab, int yt, const void* X, int64_t ldx, int64_t M, int64_t K, int n,
+                                    int64_t N, int64_t Kc, const uint8_t* tv, const uint8_t* tm, const float* sw,
+                                    void* Y, int64_t ldy, float* sx_out, hipStream_t st);
+
 // Block-scaled FP8 (128 x 128 weight blocks, per-token groups of 128; 2:4 weights, K' = K = Kc):
 // weight prep into the tiled operand with scales [ceil(rows / 128)][Kc / 128], activation codes [M][Kc] with
 // scales [M][Kc / 128], and the weight-sparse product (yt: 0 = bf16, 1 = f32).

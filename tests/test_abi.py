@@ -204,3 +204,22 @@ def test_block_scaled_validation_statuses():
     assert g(ldd=100) == ss.SS_ERR_SHAPE and g(tv=odd) == ss.SS_ERR_ALIGN and g(d=odd) == ss.SS_ERR_ALIGN
     assert g(M=70000, ldd=65536, Kc=65536) == ss.SS_ERR_UNSUPPORTED
     assert g(M=0) == ss.SS_OK and g(N=0) == ss.SS_OK
+
+
+def test_fused_decode_validation_statuses():
+    import structured_sparse_quantized_amd as ss
+    L = ss.lib
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    def f(X=FAKE, xdt=ss.SS_BF16, M=2, K=3584, ldx=3584, n=3, q=ss.SS_I8, tv=FAKE, tm=FAKE, sw=FAKE, N=4608,
+          y=ss.SS_BF16, Y=FAKE, ldy=4608, sxo=None):
+        return L.ss_quant_lift_spgemm_decode(X, xdt, M, K, ldx, n, q, tv, tm, sw, N, y, Y, ldy, sxo, None)
+    assert f(n=1) == ss.SS_ERR_PATTERN and f(n=9) == ss.SS_ERR_PATTERN
+    assert f(xdt=ss.SS_I8) == ss.SS_ERR_DTYPE and f(q=ss.SS_BF16) == ss.SS_ERR_DTYPE
+    assert f(y=ss.SS_FP8E4M3) == ss.SS_ERR_DTYPE and f(q=ss.SS_FP8E4M3, y=ss.SS_I32) == ss.SS_ERR_DTYPE
+    assert f(M=5) == ss.SS_ERR_UNSUPPORTED                       # more than four tokens
+    assert f(M=4, K=20488, ldx=20488) == ss.SS_ERR_UNSUPPORTED    # bf16 row longer than the register share
+    assert f(M=4, K=18944, ldx=18944, n=8) == ss.SS_ERR_UNSUPPORTED  # 4 x K' > 128 KB of LDS
+    assert f(ldx=100) == ss.SS_ERR_SHAPE and f(X=None) == ss.SS_ERR_NULL and f(X=odd) == ss.SS_ERR_ALIGN
+    assert f(tv=None) == ss.SS_ERR_NULL and f(tm=odd) == ss.SS_ERR_ALIGN and f(sw=None) == ss.SS_ERR_NULL
+    assert f(K=0) == ss.SS_ERR_SHAPE and f(M=-1) == ss.SS_ERR_SHAPE
+    assert f(M=0) == ss.SS_OK and f(N=0) == ss.SS_OK
