@@ -470,6 +470,10 @@ def suite(ss, torch, dev, reps=10):
                     t_g = timed(graph.replay)
                     row.update({"graph_pair_us": t_g, "graph_tokens_per_s": M / (t_g * 1e-6)})
                     del graph
+                if M <= 4:  # the same layer in one launch: quant+lift inside the few-token product
+                    t_f = timed(lambda: ss.quant_lift_spgemm_decode(X, n, tv, tm, sw, Nout, "i8", "bf16", out=Y))
+                    row.update({"fused_us": t_f, "fused_tokens_per_s": M / (t_f * 1e-6),
+                                "fused_weight_stream_GBs": wbytes / t_f / 1e3})
                 qwen.append(row)
                 del X, xq, sx, Y, ws
             del tv, tm
