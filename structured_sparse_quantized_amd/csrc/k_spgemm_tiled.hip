@@ -565,6 +565,12 @@ hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, co
 // reading the dense operand from LDS. Same arithmetic as quant_lift_kernel and decode_kernel<AB, YT, 1>
 // (same per-wave K split and partial-sum order), so the results equal the two calls bit for bit.
 constexpr int FMAXM = 4;  // tokens
+// LDS bytes of the staging row of the lifts that gather from plain codes: K padded to whole 2n-groups,
+// plus the word the last window's read reaches into, rounded to 16
+__host__ __device__ inline int fused_stage_bytes(int64_t K, int n) {
+  const int64_t kpad = (K + 2 * n - 1) / (2 * n) * (2 * n);
+  return (int)((kpad + 4 + 15) / 16 * 16);
+}
 // 16-byte vectors of a token row held per thread: K <= 20480 (bf16) / 16384 (f32)
 template <typename TIn> constexpr int fmaxv() { return sizeof(TIn) == 2 ? 5 : 8; }
 
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fused_decode_kernel(int R, int M, 
   using Qz = Quant<AB == 1>;
   constexpr int E = 16 / (int)sizeof(TIn);  // elements per 16-byte vector
   constexpr int FMAXV = fmaxv<TIn>();
-  extern __shared__ __align__(16) uint8_t xl[];  // [M][Kc] lifted codes
+  extern __shared__ __align__(16) uint8_t xl[];  // [M][Kc] lifted codes, then (other lifts) a staging row
   __shared__ Acc red[NW][64];
   __shared__ float wmax[FMAXM][NW];
   __shared__ float s_x[FMAXM];
@@ -589,8 +595,15 @@ __global__ __launch_bounds__(64 * NW, 1) void fused_decode_kernel(int R, int M, 
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, jj = lane >> 4;
   const int Kc = KS * 128, nvec = K / E, tail0 = nvec * E;
+  // n = 2 (no lift) and 6:8 from bf16 write the lifted codes straight from registers; other lifts stage
+  // a token's plain codes in LDS and gather the windows from there (zero past K)
+  const bool gather = !(n == 2 || (E == 8 && n == 4));
+  const int Kpad = (K + 2 * n - 1) / (2 * n) * (2 * n);
+  const int nwin = Kpad / (2 * n) * (n - 1);  // 4-byte windows of a lifted row
+  uint8_t* st = xl + M * Kc;
+  const int lds_bytes = M * Kc + (gather ? fused_stage_bytes(K, n) : 0);
 
-  for (int o = tid * 16; o < M * Kc; o += 64 * NW * 16) *reinterpret_cast<uint4*>(xl + o) = make_uint4(0, 0, 0, 0);
+  for (int o = tid * 16; o < lds_bytes; o += 64 * NW * 16) *reinterpret_cast<uint4*>(xl + o) = make_uint4(0, 0, 0, 0);
   auto elem = [&](const uint4& q, int e) -> float {
     if constexpr (E == 8) {
       const uint32_t w = (&q.x)[e >> 1];
@@ -598,16 +611,6 @@ __global__ __launch_bounds__(64 * NW, 1) void fused_decode_kernel(int R, int M, 
     } else {
       return __uint_as_float((&q.x)[e]);
     }
-  };
-  // codes at their lifted positions: element k = 2n g + r sits in the windows w with 2w <= r <= 2w + 3,
-  // at 4(n-1) g + 4w + (r - 2w) = 4(n-1) g + r + 2w; (g, r) is advanced element by element (no division
-  // per element)
-  const int n2 = 2 * n, gstride = 4 * (n - 1);
-  auto place = [&](uint8_t* row, int g, int r, uint32_t code) {
-    const int wlo = r >= 3 ? (r - 2) >> 1 : 0, whi = min(r >> 1, n - 2);
-    const int base = gstride * g + r;
-    row[base + 2 * wlo] = (uint8_t)code;
-    if (whi > wlo) row[base + 2 * whi] = (uint8_t)code;
   };
   // one token at a time, its row read twice (the absmax pass, then the codes; the second read hits the
   // cache), so few registers are live and four workgroups fit a CU, as for the row-block kernel
@@ -651,30 +654,39 @@ __global__ __launch_bounds__(64 * NW, 1) void fused_decode_kernel(int R, int M, 
 #pragma unroll
       for (int h = 0; h < E / 4; ++h)
         c[h] = zero ? 0u : Qz::pack4(elem(q, 4 * h), elem(q, 4 * h + 1), elem(q, 4 * h + 2), elem(q, 4 * h + 3), inv);
-      if (n == 2) {
-#pragma unroll
-        for (int h = 0; h < E / 4; ++h) *reinterpret_cast<uint32_t*>(row + vi * E + 4 * h) = c[h];
-      } else if (E == 8 && n == 4) {  // one 8-group: windows are bytes 0-3, 2-5, 4-7 of its codes
+      if (E == 8 && n == 4) {  // one 8-group: windows are bytes 0-3, 2-5, 4-7 of its codes
         uint32_t* o = reinterpret_cast<uint32_t*>(row + vi * 12);
         o[0] = c[0];
         o[1] = (c[0] >> 16) | (c[E / 4 - 1] << 16);
         o[2] = c[E / 4 - 1];
-      } else {
-        const int k0 = vi * E;
-        int g = k0 / n2, r = k0 - g * n2;
+      } else {  // plain codes: the row itself (n = 2) or the staging row
+        uint8_t* dst = gather ? st : row;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          place(row, g, r, (c[e >> 2] >> (8 * (e & 3))) & 0xFF);
-          if (++r == n2) {
-            r = 0;
-            ++g;
-          }
-        }
+        for (int h = 0; h < E / 4; ++h) *reinterpret_cast<uint32_t*>(dst + vi * E + 4 * h) = c[h];
       }
     }
-    if (tail0 + tid < K) {
-      const int k = tail0 + tid, g = k / n2;
-      place(row, g, k - g * n2, zero ? 0u : (uint32_t)Qz::code(tl, inv));
+    if (tail0 + tid < K) {  // at most E - 1 elements past the last whole vector
+      const uint8_t code = zero ? 0 : Qz::code(tl, inv);
+      if (gather) {
+        st[tail0 + tid] = code;
+      } else if (n == 2) {
+        row[tail0 + tid] = code;
+      } else {  // 6:8: element k = 8g + r lies in the windows w = (r-2)/2 .. r/2 of 0..2, at 12g + r + 2w
+        const int k = tail0 + tid, g = k >> 3, r = k & 7;
+        for (int w = r >= 3 ? (r - 2) >> 1 : 0; w <= min(r >> 1, 2); ++w) row[12 * g + r + 2 * w] = code;
+      }
+    }
+    if (gather) {
+      __syncthreads();  // the staged codes are complete (the next token's first barrier guards their reuse)
+      // output-oriented iteration (SlideSparse blog section 3.2): window t = (n-1) g + w reads the 4 codes
+      // at 2n g + 2w, an even offset, from the two words around it
+      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(st);
+      uint32_t* o32 = reinterpret_cast<uint32_t*>(row);
+      for (int t = tid; t < nwin; t += 64 * NW) {
+        const int g = t / (n - 1), w = t - g * (n - 1), base = 2 * n * g + 2 * w;
+        const uint32_t lo = s32[base >> 2], hi = s32[(base >> 2) + 1];
+        o32[t] = (base & 2) ? ((lo >> 16) | (hi << 16)) : lo;
+      }
     }
   }
   __syncthreads();
@@ -1018,7 +1030,8 @@ hipError_t launch_quant_lift_spgemm(bool x_bf16, int ab, int yt, const void* X, 
                                     int64_t N, int64_t Kc, const uint8_t* tv, const uint8_t* tm, const float* sw,
                                     void* Y, int64_t ldy, float* sx_out, hipStream_t st) {
   const int R = (int)N, m = (int)M, k = (int)K, ks = (int)(Kc / 128), ly = (int)ldy;
-  const size_t lds = (size_t)(M * Kc);
+  const bool gather = !(n == 2 || (x_bf16 && n == 4));  // as in the kernel
+  const size_t lds = (size_t)(M * Kc) + (gather ? (size_t)decode::fused_stage_bytes(K, n) : 0);
   // persistent, two workgroups a CU where the LDS holds two (each quantises the tokens once; measured
   // against one row block per workgroup and against up to four a CU, equal or faster on every shape)
   const int64_t per_cu = 2 * (int64_t)(lds + 9 * 1024) <= 160 * 1024 ? 2 : 1;
