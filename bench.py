@@ -521,6 +521,44 @@ def suite(ss, torch, dev, reps=10):
         "speedup_vs_dense": t_dn / (t_pr + t_sp)}
     del X, Wb, tv, tm, Y
     torch.cuda.empty_cache()
+    # online 2:4 on the attention operand roles, bf16, one batched launch over 32 heads (Llama-3.1-8B: 32 heads
+    # of 128) at 4096 tokens: S = Q K^T with Q pruned along the head dimension (K' = 128 padded to 256, the
+    # product's step alignment), O = P V with the probabilities pruned along the keys; dense torch.bmm beside
+    H, L, d = 32, 4096, 128
+    Kq = ss.lifted_k(d, 2)
+    Q = randn((H * L, d), 1.0, torch.bfloat16)
+    Kp = torch.zeros((H, L, Kq), dtype=torch.bfloat16, device=dev)
+    Kp[:, :, :d] = randn((H, L, d), 1.0, torch.bfloat16)
+    nv, nm = ss.tiled_bytes(H * L, Kq, "bf16")
+    tvq = torch.empty(nv, dtype=torch.uint8, device=dev)
+    tmq = torch.empty(nm, dtype=torch.uint8, device=dev)
+    S = torch.empty((H, L, L), dtype=torch.bfloat16, device=dev)
+    t_pq = timed(lambda: ss.prune24_act_tiled(Q, "bf16", out=(tvq, tmq, None)))
+    t_qk = timed(lambda: ss.spgemm_tiled_batched(ss.SS_SPARSE_X, H, L, L, Kq, tvq, tmq, Kp, None, None, "bf16", out=S))
+    Qh, Kt = Q.view(H, L, d), Kp[:, :, :d].transpose(1, 2).contiguous()
+    t_qk_dn = timed(lambda: torch.bmm(Qh, Kt))
+    del Q, Kp, tvq, tmq, Qh, Kt
+    P = torch.softmax(randn((H * L, L), 2.0), dim=1).to(torch.bfloat16)
+    Vt = randn((H, d, L), 1.0, torch.bfloat16)
+    nv, nm = ss.tiled_bytes(H * L, L, "bf16")
+    tvp = torch.empty(nv, dtype=torch.uint8, device=dev)
+    tmp = torch.empty(nm, dtype=torch.uint8, device=dev)
+    O = torch.empty((H, L, d), dtype=torch.bfloat16, device=dev)
+    t_pp = timed(lambda: ss.prune24_act_tiled(P, "bf16", out=(tvp, tmp, None)))
+    t_pv = timed(lambda: ss.spgemm_tiled_batched(ss.SS_SPARSE_X, H, L, d, L, tvp, tmp, Vt, None, None, "bf16", out=O))
+    Ph, V = P.view(H, L, L), Vt.transpose(1, 2).contiguous()
+    t_pv_dn = timed(lambda: torch.bmm(Ph, V))
+    fl = 2.0 * H * L * L * d
+    res["attention_roles_bf16"] = {
+        "heads": H, "tokens": L, "head_dim": d,
+        "qk": {"prune_q_us": t_pq, "sparse_batched_us": t_qk, "dense_bmm_us": t_qk_dn,
+               "sparse_TFLOPS_dense_equiv": 2.0 * H * L * L * Kq / t_qk / 1e6,
+               "speedup_vs_dense": t_qk_dn / (t_pq + t_qk)},
+        "pv": {"prune_p_us": t_pp, "sparse_batched_us": t_pv, "dense_bmm_us": t_pv_dn,
+               "sparse_TFLOPS_dense_equiv": fl / t_pv / 1e6, "sparse_frac_of_5030": fl / t_pv / 1e6 / 5030.0,
+               "speedup_vs_dense": t_pv_dn / (t_pp + t_pv), "product_speedup_vs_dense": t_pv_dn / t_pv}}
+    del P, Vt, tvp, tmp, O, Ph, V, S
+    torch.cuda.empty_cache()
     # quant+lift on a large batch (launch latency amortised) and a plain device copy
     ql = {}
     for n in (2, 4):

@@ -265,6 +265,27 @@ ss_status ss_spgemm_tiled_ws(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_
                              const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
                              ss_dtype y_dt, void* Y, int64_t ldy, void* workspace, int64_t ws_bytes, void* stream);
 
+/* ss_spgemm_tiled_batched -- `batch` independent ss_spgemm_tiled products of
+ * one shape in one launch (the prefill kernel; problem b reads tvals + b *
+ * tvals_stride and tmeta + b * tmeta_stride (bytes), dense + b * dense_stride,
+ * sx + b * sx_stride, sw + b * sw_stride and writes Y + b * y_stride (all in
+ * elements)). For the online 2:4 operand roles of attention (deep reading,
+ * introduction: either operand of a product can be the 2:4 one, pruned on the
+ * fly), one problem per head: side SS_SPARSE_X with the pruned Q against K
+ * (reduction over the head dimension) or the pruned probabilities P against
+ * V^T (reduction over the keys; the dense operand's rows run along the
+ * reduction, so V is passed transposed). A tiled operand prepared in one pass
+ * for all problems (ss_prune24_act_tiled on the stacked rows) splits into
+ * problems when M is a multiple of 16: tvals_stride = ss_tiled_vals_bytes(M,
+ * Kc, ab_dt), tmeta_stride = ss_tiled_meta_bytes(M, Kc, ab_dt). Strides must
+ * keep each problem 16-byte aligned (SS_ERR_ALIGN); 0 <= batch <= 65535; other
+ * arguments and errors as ss_spgemm_tiled (a stride of 0 repeats an operand). */
+ss_status ss_spgemm_tiled_batched(ss_side side, int64_t batch, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt,
+                                  const void* tvals, int64_t tvals_stride, const uint8_t* tmeta, int64_t tmeta_stride,
+                                  const void* dense, int64_t ldd, int64_t dense_stride, const float* sx,
+                                  int64_t sx_stride, const float* sw, int64_t sw_stride, ss_dtype y_dt, void* Y,
+                                  int64_t ldy, int64_t y_stride, void* stream);
+
 /* ss_quant_lift_spgemm_decode -- few-token layer in one launch: ss_quant_lift_act
  * (per-token codes, lift to K' = ss_lifted_k(K, n)) followed by the
  * weight-sparse ss_spgemm_tiled, with the quantisation and the lift done by

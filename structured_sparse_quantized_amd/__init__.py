@@ -69,18 +69,22 @@ lib.ss_spgemm_tiled_ws.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, 
 lib.ss_prune24_block.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _fp, _vp]
 lib.ss_quant_group_act.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _fp, _vp]
 lib.ss_spgemm_tiled_block.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
+lib.ss_spgemm_tiled_batched.argtypes = [_int, _i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _fp,
+                                        _i64, _fp, _i64, _int, _vp, _i64, _i64, _vp]
 lib.ss_quant_lift_spgemm_decode.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _int, _vp, _vp, _fp, _i64, _int, _vp, _i64,
                                             _fp, _vp]
 for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm", "ss_pack_sparse",
            "ss_prune24_act_tiled", "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_ws",
-           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode"):
+           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode",
+           "ss_spgemm_tiled_batched"):
     getattr(lib, _f).restype = _int
 
 EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_error", "ss_version",
            "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm",
            "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_prune24_act_tiled",
            "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_workspace_bytes", "ss_spgemm_tiled_ws",
-           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode")
+           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode",
+           "ss_spgemm_tiled_batched")
 
 
 class SSError(RuntimeError):
@@ -246,6 +250,28 @@ def spgemm_tiled(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta:
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.ss_spgemm_tiled_ws(side, M, N, Kc, ab, _ptr(tvals), _ptr(tmeta), _ptr(dense), _ld(dense),
                                   _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _ptr(ws), nbytes, _stream(dense.device)))
+    return Y
+
+
+def spgemm_tiled_batched(side: int, batch: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta: torch.Tensor,
+                         dense: torch.Tensor, sx=None, sw=None, y_dtype="bf16", out=None, strides=None):
+    """`batch` same-shaped tiled products in one launch. ``dense`` is [batch, rows, Kc] (or any 3-D view with
+    row-major rows); ``tvals`` / ``tmeta`` hold the problems' tiled operands back to back (stride = the bytes of
+    one problem unless ``strides`` = (tv, tm) bytes is given); sx / sw are [batch, n] or None.
+    Returns Y [batch, M, N]."""
+    y = dtype_code(y_dtype)
+    ab = dtype_code(dense.dtype)
+    Y = out if out is not None else torch.empty((batch, M, N), dtype=_TORCH[y], device=dense.device)
+    rows = M if side == SS_SPARSE_X else N
+    if strides is None:
+        nv, nm = tiled_bytes(rows, Kc, ab)
+        strides = (nv, nm)
+    assert dense.dim() == 3 and dense.stride(2) == 1 and Y.dim() == 3 and Y.stride(2) == 1
+    def _s(t):
+        return 0 if t is None else (t.stride(0) if t.dim() == 2 else 0)
+    _check(lib.ss_spgemm_tiled_batched(side, batch, M, N, Kc, ab, _ptr(tvals), strides[0], _ptr(tmeta), strides[1],
+                                       _ptr(dense), dense.stride(1), dense.stride(0), _ptr(sx), _s(sx), _ptr(sw),
+                                       _s(sw), y, _ptr(Y), Y.stride(1), Y.stride(0), _stream(dense.device)))
     return Y
 
 

@@ -151,12 +151,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ v
 }
 
 // BS: block-scaled FP8 (AB == 1, side W); sx is [C][KS] and sw [ceil(R / 128)][KS].
-template <int AB, int YT, bool SIDE_X, bool BS = false>
-__global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS, const uint8_t* __restrict__ tv,
-                                                            const uint8_t* __restrict__ tm, const uint8_t* __restrict__ bd,
-                                                            int ldb, const float* __restrict__ sx,
-                                                            const float* __restrict__ sw, void* __restrict__ Y, int ldy,
-                                                            int tiles_r, int tiles_c) {
+// The body of the product kernel (one tile per workgroup: blockIdx.x of gridDim.x).
+template <int AB, int YT, bool SIDE_X, bool BS>
+__device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t* __restrict__ tv,
+                                            const uint8_t* __restrict__ tm, const uint8_t* __restrict__ bd, int ldb,
+                                            const float* __restrict__ sx, const float* __restrict__ sw,
+                                            void* __restrict__ Y, int ldy, int tiles_r, int tiles_c) {
   using Acc = typename Mma<AB>::Acc;
   using MT = Meta<AB>;
   using MV = typename MT::V;
@@ -433,6 +433,43 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS
       store_out<YT, SIDE_X>(Y, ldy, ar, bc, R, y, yi);
     }
   }
+}
+
+template <int AB, int YT, bool SIDE_X, bool BS = false>
+__global__ __launch_bounds__(64 * NW, 1) void spgemm_kernel(int R, int C, int KS, const uint8_t* __restrict__ tv,
+                                                            const uint8_t* __restrict__ tm, const uint8_t* __restrict__ bd,
+                                                            int ldb, const float* __restrict__ sx,
+                                                            const float* __restrict__ sw, void* __restrict__ Y, int ldy,
+                                                            int tiles_r, int tiles_c) {
+  spgemm_body<AB, YT, SIDE_X, BS>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, tiles_r, tiles_c);
+}
+
+// A batch of independent products of one shape (e.g. one per attention head): blockIdx.y selects the
+// problem and every operand advances by its own stride (bytes for the tiled operand and the dense rows,
+// elements for the scales and Y).
+template <int AB, int YT, bool SIDE_X>
+__global__ __launch_bounds__(64 * NW, 1) void spgemm_batched_kernel(
+    int R, int C, int KS, const uint8_t* __restrict__ tv, int64_t s_tv, const uint8_t* __restrict__ tm, int64_t s_tm,
+    const uint8_t* __restrict__ bd, int64_t s_bd, int ldb, const float* __restrict__ sx, int64_t s_sx,
+    const float* __restrict__ sw, int64_t s_sw, void* __restrict__ Y, int64_t s_y, int ldy, int tiles_r, int tiles_c) {
+  const int64_t b = blockIdx.y;
+  constexpr int64_t YB = YT == 0 ? 2 : 4;  // output element bytes
+  spgemm_body<AB, YT, SIDE_X, false>(R, C, KS, tv + b * s_tv, tm + b * s_tm, bd + b * s_bd, ldb,
+                                     sx ? sx + b * s_sx : nullptr, sw ? sw + b * s_sw : nullptr,
+                                     static_cast<uint8_t*>(Y) + b * s_y * YB, ldy, tiles_r, tiles_c);
+}
+
+template <int AB, int YT, bool SIDE_X>
+hipError_t launch_batched(int batch, int R, int C, int KS, const uint8_t* tv, int64_t s_tv, const uint8_t* tm,
+                          int64_t s_tm, const uint8_t* bd, int64_t s_bd, int ldb, const float* sx, int64_t s_sx,
+                          const float* sw, int64_t s_sw, void* Y, int64_t s_y, int ldy, hipStream_t st) {
+  auto kern = spgemm_batched_kernel<AB, YT, SIDE_X>;
+  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  if (e != hipSuccess) return e;
+  const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
+  hipLaunchKernelGGL(kern, dim3(tr * tc, batch), dim3(64 * NW), LDS, st, R, C, KS, tv, s_tv, tm, s_tm, bd, s_bd, ldb, sx,
+                     s_sx, sw, s_sw, Y, s_y, ldy, tr, tc);
+  return hipGetLastError();
 }
 
 template <int AB, int YT, bool SIDE_X, bool BS = false>
@@ -1011,6 +1048,32 @@ static bool few_tokens(bool side_x, int64_t R, int64_t C) {
 }
 // The split-K path (with a workspace) serves the few-token products with more than 16 tokens.
 static bool use_splitk(bool side_x, int64_t R, int64_t C) { return few_tokens(side_x, R, C) && C > 16; }
+
+hipError_t launch_spgemm_tiled_batched(bool side_x, int ab, int yt, int64_t batch, int64_t R, int64_t C, int64_t Kc,
+                                       const uint8_t* tv, int64_t s_tv, const uint8_t* tm, int64_t s_tm, const void* bd,
+                                       int64_t ldb_bytes, int64_t s_bd, const float* sx, int64_t s_sx, const float* sw,
+                                       int64_t s_sw, void* Y, int64_t ldy, int64_t s_y, hipStream_t st) {
+  const uint8_t* b = static_cast<const uint8_t*>(bd);
+  const int bt = (int)batch, r = (int)R, c = (int)C, ks = (int)(Kc * (ab == 2 ? 2 : 1) / 128), lb = (int)ldb_bytes,
+            ly = (int)ldy;
+#define SS_TB(AB_, YT_)                                                                                                 \
+  return side_x ? tiled::launch_batched<AB_, YT_, true>(bt, r, c, ks, tv, s_tv, tm, s_tm, b, s_bd, lb, sx, s_sx, sw,     \
+                                                        s_sw, Y, s_y, ly, st)                                           \
+                : tiled::launch_batched<AB_, YT_, false>(bt, r, c, ks, tv, s_tv, tm, s_tm, b, s_bd, lb, sx, s_sx, sw,    \
+                                                         s_sw, Y, s_y, ly, st)
+  if (ab == 0) {
+    if (yt == 0) SS_TB(0, 0);
+    if (yt == 1) SS_TB(0, 1);
+    SS_TB(0, 2);
+  }
+  if (ab == 1) {
+    if (yt == 0) SS_TB(1, 0);
+    SS_TB(1, 1);
+  }
+  if (yt == 0) SS_TB(2, 0);
+  SS_TB(2, 1);
+#undef SS_TB
+}
 
 hipError_t launch_spgemm_tiled_block(int yt, int64_t R, int64_t C, int64_t Kc, const uint8_t* tv, const uint8_t* tm,
                                      const void* bd, int64_t ldb_bytes, const float* sx, const float* sw, void* Y,

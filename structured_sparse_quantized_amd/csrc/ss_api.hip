@@ -404,6 +404,34 @@ ss_status ss_spgemm_tiled_block(int64_t M, int64_t N, int64_t Kc, const void* tv
                     "ss_spgemm_tiled_block launch");
 }
 
+ss_status ss_spgemm_tiled_batched(ss_side side, int64_t batch, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt,
+                                  const void* tvals, int64_t tvals_stride, const uint8_t* tmeta, int64_t tmeta_stride,
+                                  const void* dense, int64_t ldd, int64_t dense_stride, const float* sx,
+                                  int64_t sx_stride, const float* sw, int64_t sw_stride, ss_dtype y_dt, void* Y,
+                                  int64_t ldy, int64_t y_stride, void* stream) {
+  if (batch < 0) return fail(SS_ERR_SHAPE, "negative batch");
+  bool run = false;
+  const ss_status s = check_spgemm_tiled(side, M, N, Kc, ab_dt, tvals, tmeta, dense, ldd, sx, sw, y_dt, Y, ldy, &run);
+  if (s != SS_OK) return s;
+  if (!run || batch == 0) return ok();
+  if (batch > 65535) return fail(SS_ERR_SHAPE, "batch=%lld exceeds 65535", (long long)batch);
+  if (tvals_stride < 0 || tmeta_stride < 0 || dense_stride < 0 || sx_stride < 0 || sw_stride < 0 || y_stride < 0)
+    return fail(SS_ERR_SHAPE, "negative stride");
+  const int es = esize(ab_dt);
+  if (tvals_stride % 16 || tmeta_stride % 16 || (dense_stride * es) % 16 || (y_stride * esize(y_dt)) % 16)
+    return fail(SS_ERR_ALIGN, "operand strides must keep every problem 16-byte aligned");
+  const bool sx_side = (side == SS_SPARSE_X);
+  const int64_t R = sx_side ? M : N, C = sx_side ? N : M;
+  const int ab = ab_dt == SS_I8 ? 0 : ab_dt == SS_FP8E4M3 ? 1 : 2;
+  const int yt = y_dt == SS_BF16 ? 0 : y_dt == SS_F32 ? 1 : 2;
+  return hip_status(ss::launch_spgemm_tiled_batched(sx_side, ab, yt, batch, R, C, Kc, static_cast<const uint8_t*>(tvals),
+                                                    tvals_stride, tmeta, tmeta_stride, dense, ldd * es, dense_stride * es,
+                                                    y_dt == SS_I32 ? nullptr : sx, sx_stride,
+                                                    y_dt == SS_I32 ? nullptr : sw, sw_stride, Y, ldy, y_stride,
+                                                    (hipStream_t)stream),
+                    "ss_spgemm_tiled_batched launch");
+}
+
 ss_status ss_quant_lift_spgemm_decode(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, int n,
                                       ss_dtype q_dt, const void* tvals, const uint8_t* tmeta, const float* sw, int64_t N,
                                       ss_dtype y_dt, void* Y, int64_t ldy, float* sx_out, void* stream) {

@@ -45,6 +45,13 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
                                void* Y, int64_t ldy, void* ws, hipStream_t st);
 int64_t spgemm_tiled_workspace_bytes(bool side_x, int ab, int64_t R, int64_t C, int64_t Kc);
 
+// A batch of same-shaped tiled products (one launch; blockIdx.y = problem); strides in bytes for the tiled
+// operand and the dense operand, in elements for the scales and Y.
+hipError_t launch_spgemm_tiled_batched(bool side_x, int ab, int yt, int64_t batch, int64_t R, int64_t C, int64_t Kc,
+                                       const uint8_t* tv, int64_t s_tv, const uint8_t* tm, int64_t s_tm, const void* bd,
+                                       int64_t ldb_bytes, int64_t s_bd, const float* sx, int64_t s_sx, const float* sw,
+                                       int64_t s_sw, void* Y, int64_t ldy, int64_t s_y, hipStream_t st);
+
 // Few-token quant+lift fused into the weight-sparse row-block product (ab: 0 = int8, 1 = fp8; yt as above).
 bool quant_lift_spgemm_fits(bool x_bf16, int64_t M, int64_t K, int64_t Kc);
 hipError_t launch_quant_lift_spgemm(bool x_bf16, int ab, int yt, const void* X, int64_t ldx, int64_t M, int64_t K, int n,

@@ -223,3 +223,17 @@ def test_fused_decode_validation_statuses():
     assert f(tv=None) == ss.SS_ERR_NULL and f(tm=odd) == ss.SS_ERR_ALIGN and f(sw=None) == ss.SS_ERR_NULL
     assert f(K=0) == ss.SS_ERR_SHAPE and f(M=-1) == ss.SS_ERR_SHAPE
     assert f(M=0) == ss.SS_OK and f(N=0) == ss.SS_OK
+
+
+def test_batched_validation_statuses():
+    import structured_sparse_quantized_amd as ss
+    L = ss.lib
+    def b(batch=2, M=64, N=64, Kc=256, tvs=16384, tms=4096, ldd=256, ds=64 * 256, y=ss.SS_BF16, ldy=64, ys=64 * 64,
+          side=ss.SS_SPARSE_X, ab=ss.SS_I8, sx=FAKE, sw=FAKE):
+        return L.ss_spgemm_tiled_batched(side, batch, M, N, Kc, ab, FAKE, tvs, FAKE, tms, FAKE, ldd, ds, sx, 64, sw, 64,
+                                         y, FAKE, ldy, ys, None)
+    assert b(batch=-1) == ss.SS_ERR_SHAPE and b(batch=65536) == ss.SS_ERR_SHAPE
+    assert b(tvs=8) == ss.SS_ERR_ALIGN and b(tms=4) == ss.SS_ERR_ALIGN and b(ds=8) == ss.SS_ERR_ALIGN
+    assert b(ys=4) == ss.SS_ERR_ALIGN and b(tvs=-16) == ss.SS_ERR_SHAPE
+    assert b(Kc=100) == ss.SS_ERR_SHAPE and b(ab=ss.SS_F32) == ss.SS_ERR_DTYPE and b(sx=None) == ss.SS_ERR_NULL
+    assert b(batch=0) == ss.SS_OK and b(M=0) == ss.SS_OK
