@@ -267,15 +267,22 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # the three outputs of one step, kept on the host for the parity check against the oracle below
+    y_gpu = {k: bufs[0][k].view(torch.int16).cpu().numpy().view(np.uint16) for k in ("y68", "y24", "yx")}
+
     suite_res = None
     if not (args.no_suite or args.kernels_only):
         del bufs
         torch.cuda.empty_cache()
         suite_res = suite(ss, torch, dev)
 
-    cpu = None
+    cpu, parity = None, None
     if not (args.no_cpu or args.kernels_only):
-        cpu = cpu_baseline(X_np, W_np, Kc68, Kc24)
+        y_ref, cpu = cpu_baseline(X_np, W_np, Kc68, Kc24)
+        # INT8 path: every output of the benchmarked step must equal the oracle's bf16 bits
+        parity = {k: {"bit_exact": bool(np.array_equal(y_gpu[k], y_ref[k])),
+                      "mismatches": int(np.count_nonzero(y_gpu[k] != y_ref[k]))} for k in y_gpu}
+        parity["checked"] = f"all {M}x{N} outputs of each product, bf16 bits against the oracle on the same inputs"
 
     out = {
         "metric": METRIC, "value": M / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -294,6 +301,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
         "rotating_buffer_sets": NBUF,
         "sclk_MHz_during_spgemm_68": sclk,
         "per_call_sum_ms": sum(per_kernel_ms.values()),
@@ -641,22 +649,26 @@ def cpu_baseline(X_np, W_np, Kc68, Kc24):
         threads = 1
     print("[bench] CPU oracle: three full steps", file=sys.stderr, flush=True)
 
+    outs = {}
+
     def one_step():
         t0 = time.perf_counter()
         w68 = oracle.slide_decompose(W_np, PAT, "i8")
         x68 = oracle.quant_lift_act(X_np, PAT, "i8")
-        oracle.spgemm("W", w68[0], w68[1], x68[0], Kc68, "i8", x68[1], w68[2], "bf16")
+        y68 = oracle.spgemm("W", w68[0], w68[1], x68[0], Kc68, "i8", x68[1], w68[2], "bf16")
         w24 = oracle.prune24(W_np, "i8")
         x24 = oracle.quant_lift_act(X_np, 2, "i8")
-        oracle.spgemm("W", w24[0], w24[1], x24[0], Kc24, "i8", x24[1], w24[2], "bf16")
+        y24 = oracle.spgemm("W", w24[0], w24[1], x24[0], Kc24, "i8", x24[1], w24[2], "bf16")
         xs = oracle.prune24_act(X_np, "i8")
         wq = oracle.quant_lift_act(W_np, 2, "i8")
-        oracle.spgemm("X", xs[0], xs[1], wq[0], Kc24, "i8", xs[2], wq[1], "bf16")
-        return time.perf_counter() - t0
+        yx = oracle.spgemm("X", xs[0], xs[1], wq[0], Kc24, "i8", xs[2], wq[1], "bf16")
+        dt = time.perf_counter() - t0
+        outs.update(y68=y68, y24=y24, yx=yx)
+        return dt
 
     times = sorted(one_step() for _ in range(3))
     t = times[1]
-    return {"value": M / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return outs, {"value": M / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole step (the same 9 calls; the tiled layout is a GPU storage detail with no oracle "
                       f"counterpart, M={M} tokens), median of 3 runs: {t:.2f} s (runs {times[0]:.2f}-{times[2]:.2f} s); "
                       f"products in float64 BLAS ({threads} threads), element-wise steps single-threaded NumPy; "
