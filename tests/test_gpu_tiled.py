@@ -228,7 +228,10 @@ def test_activation_sparse_path_tiled_bf16(ss):
     assert rel_fro(Y, exp) <= TOL
 
 
-PRUNE_TILED_SHAPES = [(1, 8), (7, 24), (16, 512), (33, 4096), (130, 520), (2, 18944), (300, 1000)]
+# K = 4096 / 6000 / 18944 hold one / two / no groups per wave in registers (8-bit codes); K = 100 and 1004
+# end inside a 16-byte chunk of the row, K = 520 and 1000 inside a 16-element unit
+PRUNE_TILED_SHAPES = [(1, 8), (7, 24), (5, 100), (16, 512), (33, 4096), (130, 520), (2, 18944), (300, 1000),
+                      (9, 1004), (20, 6000)]
 
 
 @pytest.mark.parametrize("out", ["i8", "fp8", "bf16"])
@@ -241,7 +244,12 @@ def test_prune24_act_tiled(ss, out, shape):
     X = synth.f32_to_bf16_bits(synth.normal_f32(rng, (M, K)))
     if M > 3:
         X[3] = 0  # an all-zero token
-    xd = dev_bf16(X)
+    # rows start 16-byte aligned: ragged K lives in a wider buffer, whose columns past K hold 1024.0 (read
+    # into the last chunk's registers, they must not reach the absmax or the selection)
+    ldk = -(-K // 8) * 8
+    xp = np.full((M, ldk), 0x4480, np.uint16)
+    xp[:, :K] = X
+    xd = dev_bf16(xp)[:, :K]
     tv, tm, sx = ss.prune24_act_tiled(xd, out)
     ov, om, osx = oracle.prune24_act(X, out)
     es = 2 if out == "bf16" else 1
