@@ -113,11 +113,16 @@ template <typename TIn> __device__ __forceinline__ void load_unit(Unit<TIn>& u, 
 // As load_unit, but the ragged end of the row is read with the same 16-byte loads: a 16-byte chunk
 // (16-byte aligned, as rows are) that starts before K is loaded whole and its elements at K and beyond
 // are zeroed in registers; chunks that start at or past K are not read. No element-wise loads (their
-// staging array costs registers in kernels that hold several units).
-template <typename TIn>
+// staging array costs registers). WHOLE: whole units take one unmasked load first (fewer instructions
+// per unit; the row kernels), else every chunk goes through the mask (fewer registers; the lane kernel).
+template <typename TIn, bool WHOLE = true>
 __device__ __forceinline__ void load_unit_vec(Unit<TIn>& u, const TIn* xr, int64_t unit, int64_t K) {
   constexpr int CE = 16 / (int)sizeof(TIn), NC = 16 / CE;  // elements per chunk, chunks per unit
   const int64_t e0 = unit * 16;
+  if (WHOLE && e0 + 16 <= K) {
+    u.load(xr + e0);
+    return;
+  }
   uint4 ch[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(kBlock, (PIPE || UPT > 2) ? 2 : ((UPT > 1 || TILED)
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
       const int un = tid + i * kBlock;
-      if (un < data_units && r < M) load_unit(u[i], xr, un, K);
+      if (un < data_units && r < M) load_unit_vec(u[i], xr, un, K);
       else u[i] = Unit<TIn>{};
     }
   };
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(kBlock) void prune24_long_kernel(const TIn* __restr
     float amax = 0.0f;
     for (int64_t un = threadIdx.x; un < data_units; un += kBlock) {
       Unit<TIn> t;
-      load_unit(t, xr, un, K);
+      load_unit_vec(t, xr, un, K);
       amax = fmaxf(amax, unit_absmax(t));
     }
     amax = block_max(amax, red);
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(kBlock) void prune24_long_kernel(const TIn* __restr
   }
   for (int64_t un = threadIdx.x; un < units; un += kBlock) {
     Unit<TIn> t{};
-    if (un < data_units) load_unit(t, xr, un, K);
+    if (un < data_units) load_unit_vec(t, xr, un, K);
     if constexpr (TILED) emit_unit_tiled<TIn, OUT>(t, zero_row, inv, vals, meta, (int)row, (int)un, KSP);
     else emit_unit<TIn, OUT>(t, zero_row, inv, vals + row * ldv_bytes, meta + row * ldm, un);
   }
@@ -272,7 +277,7 @@ __global__ __launch_bounds__(512) void prune24_act_tiled_bf16_kernel(const uint1
 #pragma unroll
     for (int q = 0; q < 4; ++q) {  // a step is 64 K positions: 4 units, one per lane chunk
       const int unit = (4 * g + q) * 4 + c;
-      if (live && unit * 16 < K) load_unit_vec(x[q], xr, unit, K);
+      if (live && unit * 16 < K) load_unit_vec<uint16_t, false>(x[q], xr, unit, K);
       else x[q] = Unit<uint16_t>{};
     }
   };
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(kBlock) void prune24_block_kernel(const TIn* __rest
   for (int j = 0; j < 4; ++j) {
     const int lu = threadIdx.x + kBlock * j, row = b * 128 + (lu >> 3), unit = g * 8 + (lu & 7);
     u[j] = Unit<TIn>{};
-    if (row < rows && g < KS) load_unit(u[j], W + (int64_t)row * ldw, unit, K);
+    if (row < rows && g < KS) load_unit_vec(u[j], W + (int64_t)row * ldw, unit, K);
     amax = fmaxf(amax, unit_absmax(u[j]));
   }
   amax = block_max(amax, red);
