@@ -98,23 +98,12 @@ __device__ __forceinline__ void emit_unit_tiled(const Unit<TIn>& u, bool zero_ro
   }
 }
 
-template <typename TIn> __device__ __forceinline__ void load_unit(Unit<TIn>& u, const TIn* xr, int64_t unit, int64_t K) {
-  const int64_t e0 = unit * 16;
-  if (e0 + 16 <= K) {
-    u.load(xr + e0);
-  } else {  // ragged end of the row (K % 16 != 0) and padding units: zeros beyond K
-    alignas(16) TIn tmp[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tmp[i] = (e0 + i < K) ? xr[e0 + i] : (TIn)0;
-    u.load(tmp);
-  }
-}
-
-// As load_unit, but the ragged end of the row is read with the same 16-byte loads: a 16-byte chunk
-// (16-byte aligned, as rows are) that starts before K is loaded whole and its elements at K and beyond
-// are zeroed in registers; chunks that start at or past K are not read. No element-wise loads (their
-// staging array costs registers). WHOLE: whole units take one unmasked load first (fewer instructions
-// per unit; the row kernels), else every chunk goes through the mask (fewer registers; the lane kernel).
+// Load unit `unit` (elements 16*unit .. 16*unit + 15) of a row, zeros past K. The row's end is read with
+// the same 16-byte loads: a 16-byte chunk (16-byte aligned, as rows are) that starts before K is loaded
+// whole and its elements at K and beyond are zeroed in registers; chunks that start at or past K are not
+// read. No element-wise loads (their staging array costs registers). WHOLE: whole units take one
+// unmasked load first (fewer instructions per unit; the row kernels), else every chunk goes through the
+// mask (fewer registers; the lane kernel).
 template <typename TIn, bool WHOLE = true>
 __device__ __forceinline__ void load_unit_vec(Unit<TIn>& u, const TIn* xr, int64_t unit, int64_t K) {
   constexpr int CE = 16 / (int)sizeof(TIn), NC = 16 / CE;  // elements per chunk, chunks per unit
