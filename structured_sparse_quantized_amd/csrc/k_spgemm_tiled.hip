@@ -193,8 +193,8 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
   for (int t = 0; t < TI; ++t)
     pmt[t] = tm + (int64_t)min(r0 / 16 + wm * TI + t, nrb - 1) * KS4 * MT::BLOCK + lane * (4 * MT::WB);
 
-  // Step k goes to slot k % S. Steps past the end re-read the last step (in
-  // bounds, never consumed) so that every step issues the same loads.
+  // Step k goes to slot k % S. Padding steps of the dense operand (KS <= k < KSP)
+  // re-read its last step (in bounds; the sparse operand's padding steps are zero).
   auto issue = [&](int k) {
     SS_LDS uint8_t* base = (SS_LDS uint8_t*)smem + (k % S) * STAGE;
     const int ka = min(k, KSP - 1), kb = min(k, KS - 1);
@@ -297,13 +297,15 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
   // most N of this wave's loads are outstanding, N = the loads issued after
   // stage k+1: the S-3 later stages (LPW each) plus the index groups issued
   // since (TI each; one is issued at every step with q == 0 except in the last
-  // group, where none is).
+  // group, where none is). The last group issues no stage past the end, so its
+  // step q counts only the real stages after k+1: min(S-3, 2-q).
   auto wait_next = [&](auto qc, auto lastc) {
     constexpr int Q = decltype(qc)::value;
     constexpr bool LAST = decltype(lastc)::value;
     constexpr int lo = Q + 6 - S, hi = Q + 3;
     constexpr int nm = LAST ? 0 : (hi >= 4 && lo <= 4 ? 1 : 0) + (hi >= 8 && lo <= 8 ? 1 : 0);
-    constexpr int N = (S - 3) * LPW + nm * (TI + (BS ? 1 : 0));
+    constexpr int later = LAST ? (S - 3 < 2 - Q ? S - 3 : 2 - Q) : S - 3;
+    constexpr int N = later * LPW + nm * (TI + (BS ? 1 : 0));
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   };
   constexpr int RD = TI + 2 * TJ, NM = TI * TJ;
@@ -318,7 +320,8 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
     wait_next(qc, lastc);
     __builtin_amdgcn_s_barrier();  // every wave's loads of stage j+1 landed; slot (j-1) % S is free
     __builtin_amdgcn_sched_barrier(0);
-    issue(j + S - 1);
+    // the last group (j = KSP-4+q) issues only stages before the end
+    if constexpr (!LAST || Q + S - 1 <= 3) issue(j + S - 1);
     if (Q == 0 && !LAST) {
       // block-scaled runs the last group in the loop too: its "next" group is a re-read, never used
       const int gn = BS ? min(j / 4 + 1, KS4 - 1) : j / 4 + 1;
