@@ -303,7 +303,12 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
     constexpr int Q = decltype(qc)::value;
     constexpr bool LAST = decltype(lastc)::value;
     constexpr int lo = Q + 6 - S, hi = Q + 3;
-    constexpr int nm = LAST ? 0 : (hi >= 4 && lo <= 4 ? 1 : 0) + (hi >= 8 && lo <= 8 ? 1 : 0);
+    // block-scaled steps issue their index loads after the stage (counted from steps j+2-S .. j-1); the
+    // others before it (counted from steps j+3-S .. j-1), which leaves the stage loads free to interleave
+    // with the smfmacs
+    constexpr int nm = LAST ? 0
+                       : BS ? (hi >= 4 && lo <= 4 ? 1 : 0) + (hi >= 8 && lo <= 8 ? 1 : 0)
+                            : (hi >= 4 && lo + 1 <= 4 ? 1 : 0) + (hi >= 8 && lo + 1 <= 8 ? 1 : 0);
     constexpr int later = LAST ? (S - 3 < 2 - Q ? S - 3 : 2 - Q) : S - 3;
     constexpr int N = later * LPW + nm * (TI + (BS ? 1 : 0));
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
@@ -320,15 +325,20 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
     wait_next(qc, lastc);
     __builtin_amdgcn_s_barrier();  // every wave's loads of stage j+1 landed; slot (j-1) % S is free
     __builtin_amdgcn_sched_barrier(0);
-    // the last group (j = KSP-4+q) issues only stages before the end
-    if constexpr (!LAST || Q + S - 1 <= 3) issue(j + S - 1);
-    if (Q == 0 && !LAST) {
-      // block-scaled runs the last group in the loop too: its "next" group is a re-read, never used
-      const int gn = BS ? min(j / 4 + 1, KS4 - 1) : j / 4 + 1;
-      load_meta(mnxt, gn);
-      load_sx(gn);
+    if constexpr (!BS) {
+      // index words of the next group, then (below) the stage loads spread among the smfmacs
+      if (Q == 0 && !LAST) load_meta(mnxt, j / 4 + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      issue(j + S - 1);
+      if (Q == 0) {
+        // block-scaled runs the last group in the loop too: its "next" group is a re-read, never used
+        const int gn = min(j / 4 + 1, KS4 - 1);
+        load_meta(mnxt, gn);
+        load_sx(gn);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
     if constexpr (BS) {
       read_scales(snxt, j + 1);
       step_bs(cur.a, nxt.a, qc, std::true_type{}, scur, j + 1);
@@ -342,10 +352,14 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
     } else {
       read(nxt, j + 1);
       mma(cur, qc);
+      // the last group (j = KSP-4+q) issues only stages before the end
+      constexpr bool ISSUE = !LAST || Q + S - 1 <= 3;
+      if constexpr (ISSUE) issue(j + S - 1);
 #pragma unroll
       for (int p = 0; p < NM; ++p) {
         if (p < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one smfmac
+        if (ISSUE && (p & 1) == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // a stage load
       }
     }
     __builtin_amdgcn_sched_barrier(0);
