@@ -71,6 +71,8 @@ constexpr int A_BYTES = BM * 64, STAGE = A_BYTES + BN * 128;   // 32 KB
 constexpr int LDS = S * STAGE;                                 // 128 KB
 constexpr int SX_BYTES = 128 * 4 * 4;                          // block-scaled: token scales of one 4-step group
 constexpr int LDS_BS = LDS + 2 * SX_BYTES;
+constexpr int SC_BYTES = (BM + BN) * 4;                        // epilogue scales of one tile (A rows, B rows)
+constexpr int LDS_SC = LDS + SC_BYTES;
 static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN, "load split");
 static_assert(S >= 3 && S <= 5, "wait counts below assume 3..5 stages");
 
@@ -374,6 +376,18 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
 
   load_meta(mcur, 0);
   load_sx(0);
+  // Epilogue scales of the tile (A rows, then B rows; indices clamped) go to LDS by DMA before the first
+  // stage, so the first wait covers them and the epilogue reads them without a global round trip.
+  const float* sa = SIDE_X ? sx : sw;  // scale indexed by A row
+  const float* sb = SIDE_X ? sw : sx;  // scale indexed by B row
+  static_assert(BM % 64 == 0 && (BM + BN) / 64 <= NW, "one 64-scale load per wave, A and B scales apart");
+  if (!BS && wave < (BM + BN) / 64) {
+    const int i = wave * 64 + lane;  // this lane's slot of the tile's BM + BN scales
+    const float* src = i < BM ? (sa ? sa + min(r0 + i, R - 1) : nullptr) : (sb ? sb + min(c0 + i - BM, C - 1) : nullptr);
+    if (src)
+      __builtin_amdgcn_global_load_lds((const void*)src, (SS_LDS void*)((SS_LDS uint8_t*)smem + LDS + wave * 256), 4,
+                                       0, 0);
+  }
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(s);
   Frag f0, f1;
@@ -413,17 +427,16 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
   }
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // no load may outlive the workgroup
 
-  // Epilogue: y = fl32(fl32(float(acc) * sx[m]) * sw[n]); scales loaded up front
-  // (indices clamped; out-of-range results are never stored).
+  // Epilogue: y = fl32(fl32(float(acc) * sx[m]) * sw[n]), the scales from LDS (staged in the prologue;
+  // out-of-range results are never stored).
   float s_a[TI][4], s_b[TJ];
-  const float* sa = SIDE_X ? sx : sw;  // scale indexed by A row
-  const float* sb = SIDE_X ? sw : sx;  // scale indexed by B row
+  const float* scl = reinterpret_cast<const float*>(smem + LDS);
 #pragma unroll
   for (int t = 0; t < TI; ++t)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_a[t][q] = (sa && !BS) ? sa[min(r0 + (wm * TI + t) * 16 + 4 * jj + q, R - 1)] : 1.0f;
+    for (int q = 0; q < 4; ++q) s_a[t][q] = (sa && !BS) ? scl[(wm * TI + t) * 16 + 4 * jj + q] : 1.0f;
 #pragma unroll
-  for (int u = 0; u < TJ; ++u) s_b[u] = (sb && !BS) ? sb[min(c0 + (wn * TJ + u) * 16 + r16, C - 1)] : 1.0f;
+  for (int u = 0; u < TJ; ++u) s_b[u] = (sb && !BS) ? scl[BM + (wn * TJ + u) * 16 + r16] : 1.0f;
 #pragma unroll
   for (int t = 0; t < TI; ++t) {
 #pragma unroll
@@ -482,10 +495,10 @@ hipError_t launch_batched(int batch, int R, int C, int KS, const uint8_t* tv, in
                           int64_t s_tm, const uint8_t* bd, int64_t s_bd, int ldb, const float* sx, int64_t s_sx,
                           const float* sw, int64_t s_sw, void* Y, int64_t s_y, int ldy, hipStream_t st) {
   auto kern = spgemm_batched_kernel<AB, YT, SIDE_X>;
-  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_SC);
   if (e != hipSuccess) return e;
   const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
-  hipLaunchKernelGGL(kern, dim3(tr * tc, batch), dim3(64 * NW), LDS, st, R, C, KS, tv, s_tv, tm, s_tm, bd, s_bd, ldb, sx,
+  hipLaunchKernelGGL(kern, dim3(tr * tc, batch), dim3(64 * NW), LDS_SC, st, R, C, KS, tv, s_tv, tm, s_tm, bd, s_bd, ldb, sx,
                      s_sx, sw, s_sw, Y, s_y, ldy, tr, tc);
   return hipGetLastError();
 }
@@ -494,7 +507,7 @@ template <int AB, int YT, bool SIDE_X, bool BS = false>
 hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb,
                   const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
   auto kern = spgemm_kernel<AB, YT, SIDE_X, BS>;
-  constexpr int lds = BS ? LDS_BS : LDS;
+  constexpr int lds = BS ? LDS_BS : LDS_SC;
   // set at every launch: the attribute is per device, and the call is cheap and thread-safe
   const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
