@@ -764,6 +764,12 @@ __global__ __launch_bounds__(64 * NW, 1) void fused_decode_kernel(int R, int M, 
   const int g0 = KS4 * wave / NW, g1 = KS4 * (wave + 1) / NW;
   for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
   Acc acc = Acc{0, 0, 0, 0};
+  // the epilogue's channel scales (wave 0 writes the block), loaded before the product
+  float esw[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  if (YT != 2 && wave == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) esw[q] = sw[min(rb * 16 + 4 * jj + q, R - 1)];
+  }
   if (g0 < g1) {
     const uint8_t* pa = tv + (int64_t)rb * KSP * 1024 + lane * 16;
     const uint8_t* pm = tm + (int64_t)rb * KS4 * MT::BLOCK + lane * (4 * MT::WB);
@@ -816,7 +822,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fused_decode_kernel(int R, int M, 
         } else {
           float f = (float)sum[q];
           f = __fmul_rn(f, s_x[bc]);
-          f = __fmul_rn(f, sw[min(ar + q, R - 1)]);
+          f = __fmul_rn(f, esw[q]);
           y[q] = f;
         }
       }
