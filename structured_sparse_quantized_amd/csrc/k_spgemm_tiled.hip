@@ -270,6 +270,7 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
   auto step_bs = [&](const v4i* acur, v4i* anxt, auto qc, auto readc, const float* sc, int knext) {
     constexpr int Q = decltype(qc)::value;
     constexpr bool READ = decltype(readc)::value;
+    Acc pp[TI];  // the previous column's partial tiles, scaled while this column's smfmacs run
 #pragma unroll
     for (int u = 0; u < TJ; ++u) {
       Acc p[TI];
@@ -279,11 +280,19 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
         read_b(u, knext);
         anxt[u] = *reinterpret_cast<const v4i*>(smem + (knext % S) * STAGE + (wm * TI + u) * 1024 + lane * 16);
       }
+      if (u > 0) {
 #pragma unroll
-      for (int t = 0; t < TI; ++t)
+        for (int t = 0; t < TI; ++t)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[t][u][q] = __builtin_fmaf(p[t][q], sc[u], acc[t][u][q]);
+          for (int q = 0; q < 4; ++q) acc[t][u - 1][q] = __builtin_fmaf(pp[t][q], sc[u - 1], acc[t][u - 1][q]);
+      }
+#pragma unroll
+      for (int t = 0; t < TI; ++t) pp[t] = p[t];
     }
+#pragma unroll
+    for (int t = 0; t < TI; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[t][TJ - 1][q] = __builtin_fmaf(pp[t][q], sc[TJ - 1], acc[t][TJ - 1][q]);
   };
   // Block-scaled: the scales of step k for this lane's TJ B rows: s_x[token][k] * s_w[block][k].
   auto read_scales = [&](float* sc, int k) {
@@ -340,8 +349,9 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
       for (int u = 0; u < TJ; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, TI, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4 * TI, 0);
+        if (u > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4 * TI, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x002, 4 * TI, 0);
       // the step's loads after its smfmacs and fragment reads (4-7% faster than before them); same
       // order (stage, then index words and token scales), so the waits count them as before
       __builtin_amdgcn_sched_barrier(0);
