@@ -1,34 +1,40 @@
 """Benchmark of the structured-sparse quantised linear path on one MI355X.
 
-A step is one pass of every kernel on the path over one batch of the
-6:8 sliding-window INT8 workload (W 4096x4096 N(0, 0.02^2) float32, X
-2048x4096 bf16 N(0,1) with 1% outlier columns x20), all INT8:
+Headline workload: the four projection layers of one Llama-3.1-8B-shaped
+decoder layer (qkv 4096->6144, o 4096->4096, gate_up 4096->28672, down
+14336->4096) in 2:4 FP8-E4M3 with per-channel weight scales and dynamic
+per-token activation scales, bf16 output, 16384 tokens (prefill). Weights are
+W ~ N(0, 0.02^2), activations X ~ N(0, 1) in bf16, seeded on the GPU; no model
+weight or dataset is involved.
 
-  slide_decompose_tiled(W, n=4) -> quant_lift_act(X, n=4) -> spgemm_tiled(sparse W')   6:8
-  slide_decompose_tiled(W, n=2) -> quant_lift_act(X, n=2) -> spgemm_tiled(sparse W)    2:4
-  prune24_act_tiled(X), quant_lift_act(W, n=2) -> spgemm_tiled(sparse X)              2:4 on X
+A step is the online path of that layer: for each of the four linears the
+per-token FP8 quantisation of its input (``ss_quant_lift_act``, n = 2) and the
+sparse product with the rescale epilogue (``ss_spgemm_tiled``). The offline
+weight preparation (2:4 prune or 6:8 decomposition straight into the
+product's tiled layout) runs once per model, not per token; it is timed apart
+and reported beside the headline. ``value`` = tokens per second of the step
+(16384 tokens per step) from K steps launched back to back between one pair of
+events; per-call times come from medians of 5 samples of at least 20 ms each,
+over rotating buffer sets whose working set is at least twice the 256 MB
+Infinity Cache.
 
-The weight-side preparation (decompose or prune, written straight into the
-product's tiled layout) runs offline in a deployment; it is timed here per
-step all the same.
+The last stdout line is one compact JSON object (the headline, the roofline of
+the dominant kernel, the CPU oracle baseline, parity on sampled outputs, and a
+few summary figures of other rows). Every other row -- per-call times, the
+6:8 layers, the M = 4096 layer, the Qwen2.5-7B-shaped 4:6 / 8:10 rows at
+decode and prefill token counts against dense INT8, the online activation
+prune, block-scaled FP8, the attention operand roles, quant+lift bandwidth --
+goes to stderr (one JSON object per line) and to ``--detail`` (a JSON file).
 
-``value`` is tokens per second of the whole step (M tokens per step), from K
-steps launched back to back between one pair of events. Per-kernel times come
-from a second timed region in which each call runs K times back to back
-between its own pair of events (an event between every two launches would
-drain the queue and add ~3.5 us per event). The JSON line carries these
-per-kernel times with their throughput against the roofline, the online 6:8 prefill rate (quant_lift + spgemm only), the dense
-INT8 comparator, the roofline of the dominant kernel and the CPU oracle
-baseline. Inputs are seeded and synthetic; NBUF rotating buffer sets keep the
-working set above the 256 MB Infinity Cache so kernels stream from HBM.
-
-  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-suite] [--kernels-only]
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
+import statistics
 import sys
 import time
 
@@ -36,29 +42,52 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse GEMM TOPS & prefill tokens/s (2:4, 6:8) vs dense; quant+lift GB/s"
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-INT8_DENSE_PEAK_TOPS = 5000.0  # MI355X dense INT8 MFMA (ops counted on kept values only)
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+DENSE_PEAK_T = {"fp8": 5000.0, "i8": 5000.0, "bf16": 2500.0}  # dense MFMA, TFLOP/s (TOPS for INT8)
+PEAK_UNIT = {"fp8": "TFLOP/s", "i8": "TOPS", "bf16": "TFLOP/s"}
+MALL_BYTES = 256 << 20          # Infinity Cache
+HEAD_M = 16384
+LLAMA_LAYERS = 32               # decoder layers of Llama-3.1-8B (public model config)
+QWEN_LAYERS = 28                # decoder layers of Qwen2.5-7B
+NBUF = 3                        # rotating buffer sets of the headline layer
 
-M, N, K, PAT = 2048, 4096, 4096, 4
-NBUF = 3
 
-
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--kernels-only", action="store_true", help="skip the dense comparator and CPU baseline")
-    p.add_argument("--no-clock", action="store_true", help="skip the engine-clock sampling loop")
-    p.add_argument("--no-suite", action="store_true", help="skip the Llama/Qwen-shaped layer suite")
+    p.add_argument("--tokens", type=int, default=HEAD_M, help="tokens per step of the headline layer")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and the parity check")
+    p.add_argument("--no-suite", action="store_true", help="skip the rows beyond the headline")
+    p.add_argument("--kernels-only", action="store_true",
+                   help="only the timed headline steps (for counter runs); no comparators, suite or CPU leg")
     p.add_argument("--calib-copy", action="store_true",
-                   help="also run a plain 256 MiB device copy (the reference for HBM byte counters)")
-    return p.parse_args()
+                   help="end with three plain 256 MiB device copies (the reference for HBM byte counters)")
+    p.add_argument("--cpu-tokens", type=int, default=256, help="tokens of the CPU oracle sample")
+    p.add_argument("--cpu-channels", type=int, default=768, help="output channels per linear of the CPU sample")
+    p.add_argument("--detail", default=os.path.join(ROOT, "gpurun_out", "bench_detail.json"),
+                   help="where the full results go (JSON); empty to skip")
+    return p.parse_args(argv)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def row(name, **kw):
+    """One result row on stderr (one JSON object per line)."""
+    d = {"row": name, **kw}
+    log(json.dumps(d, default=_round))
+    return d
+
+
+def _round(x):
+    return float(x)
 
 
 def traffic_record(kernel):
-    """HBM traffic per launch measured with rocprofv3 counters, if it was taken
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
     on the current source of the kernel (else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -73,467 +102,560 @@ def traffic_record(kernel):
     return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
 
 
-def tiled_bytes(rows, Kc):
-    """Bytes of the tiled operand (values, metadata), as include/ss.h defines them."""
-    g = -(-(Kc // 128) // 4)
+def tiled_bytes(rows, Kc, es=1):
+    """Bytes of the tiled operand (values, metadata) as include/ss.h defines them (es = value bytes)."""
+    g = -(-(Kc * es // 128) // 4)
     rb = -(-rows // 16)
-    return rb * g * 4 * 1024, rb * g * 1024
+    return rb * g * 4 * 1024, rb * g * 256 * (4 // es)
 
 
-def kernel_work(name, Kc68, Kc24):
-    """Algorithmic bytes (HBM-bound kernels) or ops (products) per launch."""
-    b = {
-        # weight preparation written in the tiled layout: W read once, tiled operand + scales written
-        "slide_decompose_tiled_68": 4 * N * K + sum(tiled_bytes(N, Kc68)) + 4 * N,
-        "quant_lift_68": 2 * M * K + M * Kc68 + 4 * M,
-        "prune24_w_tiled": 4 * N * K + sum(tiled_bytes(N, Kc24)) + 4 * N,
-        "quant_lift_24": 2 * M * K + M * Kc24 + 4 * M,
-        # online prune of X written in the tiled layout: X read once, tiled operand + scales written
-        "prune24_act_tiled": 2 * M * K + sum(tiled_bytes(M, Kc24)) + 4 * M,
-        "quant_w": 4 * N * K + N * Kc24 + 4 * N,
-    }
-    # products: multiply-adds on the kept values only (K'/2 per row), x2 ops
-    ops = {
-        "spgemm_68": 2 * M * N * (Kc68 // 2),
-        "spgemm_24": 2 * M * N * (Kc24 // 2),
-        "spgemm_x": 2 * M * N * (Kc24 // 2),
-    }
-    if name in b:
-        return "hbm", b[name]
-    return "mfma", ops[name]
+def product_ops(M, N, Kc):
+    """Operations of one sparse product: multiply-adds on the kept values only (K'/2 per row), x2. Priced
+    against the dense matrix-core peak this is the same fraction as the dense-equivalent count 2 M N K'
+    against the sparse peak."""
+    return 2 * M * N * (Kc // 2)
 
 
-def main():
-    args = parse()
+def quant_bytes(M, K, Kc, code_bytes=1):
+    """Algorithmic bytes of quant(+lift): bf16 rows read once, codes and one scale per token written."""
+    return 2 * M * K + code_bytes * M * Kc + 4 * M
+
+
+def prep_bytes(N, K, Kc, es=1):
+    """Algorithmic bytes of weight prep into the tiled layout: float32 W read once, operand + scales written."""
+    return 4 * N * K + sum(tiled_bytes(N, Kc, es)) + 4 * N
+
+
+def median_us(torch, fns, min_ms=20.0, samples=5):
+    """Per-call time (us): the median of ``samples`` samples, each running the callables of ``fns`` round robin
+    (one per rotating buffer set) enough times to last at least ``min_ms``, between one pair of events on the
+    launch stream (torch's current stream)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for f in fns:
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    est = max(e0.elapsed_time(e1) / len(fns), 1e-3)
+    reps = len(fns) * max(1, math.ceil(min_ms / est / len(fns)))
+    out = []
+    for _ in range(samples):
+        e0.record()
+        for i in range(reps):
+            fns[i % len(fns)]()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / reps * 1e3)
+    return statistics.median(out)
+
+
+def rotation(nbytes, floor=2 * MALL_BYTES, cap=8):
+    """Buffer copies so that ``nbytes`` per copy add up to at least ``floor`` bytes."""
+    return max(1, min(cap, math.ceil(floor / max(nbytes, 1))))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# ------------------------------------------------------------------------------------------------------------
+# the Llama-shaped layer
+
+
+class Layer:
+    """The four Llama-3.1-8B-shaped linears on the GPU: float32 W, the prepared sparse operand (tiled layout),
+    dense per-channel codes for the comparator, and ``nbuf`` sets of activations, codes and outputs."""
+
+    def __init__(self, ss, torch, dev, gen, M, n, q, nbuf, dense=True, keep_w=False):
+        import synth
+        self.ss, self.torch, self.M, self.n, self.q = ss, torch, M, n, q
+        qdt = torch.int8 if q == "i8" else torch.float8_e4m3fn
+        self.lin = {}
+        for name, (K, N) in synth.LLAMA31_8B_LINEARS.items():
+            W = torch.randn((N, K), generator=gen, device=dev) * 0.02
+            Kc = ss.lifted_k(K, n)
+            tv, tm, sw = ss.slide_decompose_tiled(W, n, q)
+            L = dict(K=K, N=N, Kc=Kc, tv=tv, tm=tm, sw=sw, W=W if keep_w else None)
+            if dense:
+                L["wq"], L["swd"] = ss.quant_lift_act(W, 2, q)
+            del W
+            X = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+            sets = []
+            for i in range(nbuf):
+                s = dict(X=X if i == 0 else X.clone(), xq=torch.empty((M, Kc), dtype=qdt, device=dev),
+                         sx=torch.empty(M, dtype=torch.float32, device=dev),
+                         Y=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+                if dense and n != 2:  # the dense comparator quantises without the lift
+                    s["xd"] = torch.empty((M, K), dtype=qdt, device=dev)
+                    s["sxd"] = torch.empty(M, dtype=torch.float32, device=dev)
+                sets.append(s)
+            L["sets"] = sets
+            self.lin[name] = L
+        self.nbuf = nbuf
+
+    def quant(self, name, b):
+        L, s = self.lin[name], self.lin[name]["sets"][b]
+        return lambda: self.ss.quant_lift_act(s["X"], self.n, self.q, out=(s["xq"], s["sx"]))
+
+    def gemm(self, name, b):
+        L, s = self.lin[name], self.lin[name]["sets"][b]
+        ss = self.ss
+        return lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, self.M, L["N"], L["Kc"], L["tv"], L["tm"], s["xq"], s["sx"],
+                                       L["sw"], "bf16", out=s["Y"], workspace=False)
+
+    def calls(self, b):
+        """The step on buffer set b: (name, callable) in launch order."""
+        out = []
+        for name in self.lin:
+            out.append((f"quant_{name}", self.quant(name, b)))
+            out.append((f"gemm_{name}", self.gemm(name, b)))
+        return out
+
+    def dense_calls(self, b):
+        """The same layer dense: per-token quantisation (no lift) + hipBLASLt (torch._scaled_mm with the same
+        per-token x per-channel scales, bf16 out; INT8: torch._int_mm, int32 out and no rescale)."""
+        torch, ss = self.torch, self.ss
+        out = []
+        for name, L in self.lin.items():
+            s = L["sets"][b]
+            if self.n == 2:
+                xq, sx = s["xq"], s["sx"]
+                out.append((f"quant_{name}", self.quant(name, b)))
+            else:
+                xq, sx = s["xd"], s["sxd"]
+                out.append((f"quant_{name}", lambda s=s: ss.quant_lift_act(s["X"], 2, self.q, out=(s["xd"], s["sxd"]))))
+            wq, swd = L["wq"], L["swd"]
+            if self.q == "i8":
+                out.append((f"gemm_{name}", lambda xq=xq, wq=wq: torch._int_mm(xq, wq.t())))
+            else:
+                out.append((f"gemm_{name}", lambda xq=xq, wq=wq, sx=sx, swd=swd: torch._scaled_mm(
+                    xq, wq.t(), scale_a=sx[:, None], scale_b=swd[None, :], out_dtype=torch.bfloat16)))
+        return out
+
+
+def time_steps(torch, layer_calls, steps, warmup, mark=None):
+    """K steps launched back to back (rotating buffer sets) between one pair of events, after W warm-up
+    steps; ``mark`` names one call whose launches are also bracketed by events inside the timed region.
+    Returns (ms per step, average ms of the marked call or None)."""
+    nb = len(layer_calls)
+    for s in range(warmup):
+        for _, c in layer_calls[s % nb]:
+            c()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    marks = [(ev(), ev()) for _ in range(steps)] if mark else None
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    e0.record()
+    for s in range(steps):
+        for name, c in layer_calls[s % nb]:
+            if marks and name == mark:
+                marks[s][0].record()
+                c()
+                marks[s][1].record()
+            else:
+                c()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    mk = statistics.fmean(a.elapsed_time(b) for a, b in marks) if marks else None
+    return ms, mk
+
+
+def per_call(torch, layer_calls):
+    """Median per-call us of every call of the step, each over the rotating buffer sets."""
+    names = [n for n, _ in layer_calls[0]]
+    return {n: median_us(torch, [dict(c)[n] for c in layer_calls]) for n in names}
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
-        print(json.dumps({"error": "bench.py measures one GPU; run with --gpus 1",
+        print(json.dumps({"error": "bench.py measures one GPU (this build runs on one); run with --gpus 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
-    import numpy as np
     import torch
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     import structured_sparse_quantized_amd as ss
-    import synth
 
     dev = torch.device("cuda:0")
-    Kc68, Kc24 = ss.lifted_k(K, PAT), ss.lifted_k(K, 2)
-    print(f"[bench] generating inputs M={M} N={N} K={K}", file=sys.stderr, flush=True)
-    X_np, W_np, _ = synth.workload(0, M, N, K, x_kind="bf16", outlier_frac=0.01)
-    X0 = torch.from_numpy(X_np.view(np.int16)).view(torch.bfloat16).to(dev)
-    W0 = torch.from_numpy(W_np).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261203)
+    M = args.tokens
+    detail = {"data": "synthetic: W ~ N(0, 0.02^2) float32, X ~ N(0, 1) bf16, generated on the GPU (seeded)"}
 
-    def mk(shape, dt):
-        return torch.empty(shape, dtype=dt, device=dev)
-
-    bufs = []
-    for i in range(NBUF):
-        bufs.append(dict(
-            X=X0.clone(), W=W0.clone(),
-            t68=tuple(mk(nb, torch.uint8) for nb in tiled_bytes(N, Kc68)) + (mk(N, torch.float32),),
-            t24=tuple(mk(nb, torch.uint8) for nb in tiled_bytes(N, Kc24)) + (mk(N, torch.float32),),
-            tx=tuple(mk(nb, torch.uint8) for nb in tiled_bytes(M, Kc24)),
-            x68=(mk((M, Kc68), torch.int8), mk(M, torch.float32)),
-            y68=mk((M, N), torch.bfloat16),
-            x24=(mk((M, Kc24), torch.int8), mk(M, torch.float32)),
-            y24=mk((M, N), torch.bfloat16),
-            xs=(mk(M, torch.float32),),
-            wq=(mk((N, Kc24), torch.int8), mk(N, torch.float32)),
-            yx=mk((M, N), torch.bfloat16),
-        ))
-    names = ["slide_decompose_tiled_68", "quant_lift_68", "spgemm_68", "prune24_w_tiled", "quant_lift_24",
-             "spgemm_24", "prune24_act_tiled", "quant_w", "spgemm_x"]
-
-    def calls(b):
-        return [
-            lambda: ss.slide_decompose_tiled(b["W"], PAT, "i8", out=b["t68"]),
-            lambda: ss.quant_lift_act(b["X"], PAT, "i8", out=b["x68"]),
-            lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc68, b["t68"][0], b["t68"][1], b["x68"][0], b["x68"][1],
-                                    b["t68"][2], "bf16", out=b["y68"]),
-            lambda: ss.slide_decompose_tiled(b["W"], 2, "i8", out=b["t24"]),
-            lambda: ss.quant_lift_act(b["X"], 2, "i8", out=b["x24"]),
-            lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc24, b["t24"][0], b["t24"][1], b["x24"][0], b["x24"][1],
-                                    b["t24"][2], "bf16", out=b["y24"]),
-            lambda: ss.prune24_act_tiled(b["X"], "i8", out=(b["tx"][0], b["tx"][1], b["xs"][0])),
-            lambda: ss.quant_lift_act(b["W"], 2, "i8", out=b["wq"]),
-            lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, Kc24, b["tx"][0], b["tx"][1], b["wq"][0], b["xs"][0],
-                                    b["wq"][1], "bf16", out=b["yx"]),
-        ]
-
-    steps_calls = [calls(b) for b in bufs]
-
-    def step(s):
-        for c in steps_calls[s % NBUF]:
-            c()
-
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-
-    # Timed region 1: K whole steps back to back, no per-call events (a timing
-    # event between two launches costs the GPU ~3.5 us: it drains the queue).
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for s in range(args.steps):
-        step(s)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr, flush=True)
-
-    # Timed region 2: per-call durations. Each call of the step runs K times
-    # back to back (rotating buffer sets) between one pair of events on the
-    # stream the kernels are launched on; duration = elapsed / K.
-    per_kernel_ms = {}
-    for i, n in enumerate(names):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for s in range(args.steps):
-            steps_calls[s % NBUF][i]()
-        e1.record()
-        torch.cuda.synchronize()
-        per_kernel_ms[n] = e0.elapsed_time(e1) / args.steps
-    print("[bench] per-call us: " + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in per_kernel_ms.items()),
-          file=sys.stderr, flush=True)
-
-    kernels = {}
-    for n in names:
-        kind, work = kernel_work(n, Kc68, Kc24)
-        t = per_kernel_ms[n] * 1e-3
-        if kind == "hbm":
-            a = work / t / 1e9
-            kernels[n] = {"us": per_kernel_ms[n] * 1e3, "bound": "hbm", "GB/s": a, "frac": a / HBM_PEAK_GBS,
-                          "bytes": work}
-        else:
-            a = work / t / 1e12
-            kernels[n] = {"us": per_kernel_ms[n] * 1e3, "bound": "mfma", "TOPS": a,
-                          "frac": a / INT8_DENSE_PEAK_TOPS, "ops": work,
-                          "dense_equiv_TOPS": 2 * a}
-    dom = max(names, key=lambda n: per_kernel_ms[n])
-    dk = kernels[dom]
-    roofline = {
-        "kernel": dom, "bound": dk["bound"],
-        "achieved": dk["GB/s"] if dk["bound"] == "hbm" else dk["TOPS"],
-        "peak": HBM_PEAK_GBS if dk["bound"] == "hbm" else INT8_DENSE_PEAK_TOPS,
-        "unit": "GB/s" if dk["bound"] == "hbm" else "TFLOP/s",
-        "frac": dk["frac"], "traffic": traffic_record(dom),
-    }
-    # the three outputs of one step, kept on the host for the parity check against the oracle below (not in
-    # the counter runs, whose last dispatches must be the calibration copies)
-    check_parity = not (args.no_cpu or args.kernels_only)
-    y_gpu = ({k: bufs[0][k].view(torch.int16).cpu().numpy().view(np.uint16) for k in ("y68", "y24", "yx")}
-             if check_parity else None)
-    online68_s = (per_kernel_ms["quant_lift_68"] + per_kernel_ms["spgemm_68"]) * 1e-3
-    online24_s = (per_kernel_ms["quant_lift_24"] + per_kernel_ms["spgemm_24"]) * 1e-3
-    # sparse-activation layer: online prune + pack of X, then the product (W quantised offline)
-    onlinex_s = (per_kernel_ms["prune24_act_tiled"] + per_kernel_ms["spgemm_x"]) * 1e-3
-
-    # dense INT8 comparator: our per-token quantiser + hipBLASLt int8 GEMM (torch._int_mm)
-    dense = None
-    if not args.kernels_only:
-        try:
-            b = bufs[0]
-            wq = b["wq"][0][:, :K].contiguous()
-            xq = b["x24"][0][:, :K].contiguous()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            for _ in range(3):
-                torch._int_mm(xq, wq.t())
-            torch.cuda.synchronize()
-            reps = 20
-            e0.record()
-            for _ in range(reps):
-                torch._int_mm(xq, wq.t())
-            e1.record()
-            torch.cuda.synchronize()
-            t_mm = e0.elapsed_time(e1) / reps * 1e-3
-            t_q = per_kernel_ms["quant_lift_24"] * 1e-3
-            dense = {"gemm_us": t_mm * 1e6, "quant_us": t_q * 1e6, "gemm_TOPS": 2 * M * N * K / t_mm / 1e12,
-                     "library": "hipBLASLt via torch._int_mm (int32 out, no rescale)",
-                     "speedup_68": (t_mm + t_q) / online68_s, "speedup_24": (t_mm + t_q) / online24_s}
-        except Exception as e:  # comparator unavailable on this stack
-            dense = {"error": repr(e)[:200]}
-
-    # engine clock while the product runs back to back (sysfs; None where it is not readable)
-    sclk = None
-    if not (args.kernels_only or args.no_clock):
-        sclk = sample_sclk(lambda: steps_calls[0][names.index("spgemm_68")](), torch, seconds=0.3)
-
-    if args.calib_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-
-    suite_res = None
-    if not (args.no_suite or args.kernels_only):
-        del bufs
-        torch.cuda.empty_cache()
-        suite_res = suite(ss, torch, dev)
-
-    cpu, parity = None, None
-    if check_parity:
-        y_ref, cpu = cpu_baseline(X_np, W_np, Kc68, Kc24)
-        # INT8 path: every output of the benchmarked step must equal the oracle's bf16 bits
-        parity = {k: {"bit_exact": bool(np.array_equal(y_gpu[k], y_ref[k])),
-                      "mismatches": int(np.count_nonzero(y_gpu[k] != y_ref[k]))} for k in y_gpu}
-        parity["checked"] = f"all {M}x{N} outputs of each product, bf16 bits against the oracle on the same inputs"
-
+    # ---- headline: the Llama-shaped layer, 2:4 FP8, M tokens ----
+    log(f"[bench] headline layer: 2:4 FP8, {M} tokens, {NBUF} buffer sets")
+    lay = Layer(ss, torch, dev, gen, M, 2, "fp8", NBUF, dense=not args.kernels_only, keep_w=not args.kernels_only)
+    steps_calls = [lay.calls(b) for b in range(NBUF)]
+    ms_step, ms_gate = time_steps(torch, steps_calls, args.steps, args.warmup, mark="gemm_gate_up")
+    log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step; gate_up product {ms_gate * 1e3:.1f} us (live)")
+    gu = lay.lin["gate_up"]
+    gu_ops = product_ops(M, gu["N"], gu["Kc"])
+    roof = {"bound": "mfma", "achieved": gu_ops / (ms_gate * 1e-3) / 1e12, "peak": DENSE_PEAK_T["fp8"],
+            "unit": PEAK_UNIT["fp8"]}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_record(f"gemm_gate_up_{M}")
+    roof["kernel"] = "spgemm_tiled gate_up 16384x28672x4096 (2:4 fp8)" if M == 16384 else f"gate_up M={M}"
     out = {
         "metric": METRIC, "value": M / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
-        "config": {"workload": "6:8 sliding-window INT8 linear, W 4096x4096 -> K'=6144, X 2048x4096 bf16 "
-                               "with 1% outlier channels; plus 2:4 on W and 2:4 on X of the same batch",
-                   "M": M, "N": N, "K": K, "K_prime": Kc68, "global_batch": M, "parallelism": "none (1 GPU)"},
-        "online_68_tokens_per_s": M / online68_s,
-        "online_24_tokens_per_s": M / online24_s,
-        "online_x_tokens_per_s": M / onlinex_s,
-        "gemm_68_dense_equiv_TOPS": kernels["spgemm_68"]["dense_equiv_TOPS"],
-        "gemm_24_dense_equiv_TOPS": kernels["spgemm_24"]["dense_equiv_TOPS"],
-        "quant_lift_68_GBs": kernels["quant_lift_68"]["GB/s"],
-        "dense_int8": dense,
-        "kernels": kernels,
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "parity_vs_oracle": parity,
-        "rotating_buffer_sets": NBUF,
-        "sclk_MHz_during_spgemm_68": sclk,
-        "per_call_sum_ms": sum(per_kernel_ms.values()),
-        "suite": suite_res,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+        "config": {"workload": f"Llama-3.1-8B-shaped layer linears qkv+o+gate_up+down, 2:4 FP8-e4m3 W per-channel, "
+                               f"dynamic per-token FP8 X, bf16 out, {M} tokens (online quant + sparse GEMM)",
+                   "tokens": M, "global_batch": M, "parallelism": "none (1 GPU)"},
+        "model_tokens_per_s": M / (ms_step * 1e-3) / LLAMA_LAYERS,
+        "roofline": roof,
     }
-    print(json.dumps(out))
+    if args.kernels_only:
+        if args.calib_copy:
+            calib_copy(torch, dev)
+        print(json.dumps(out, default=_round))
+        return
+
+    pc = per_call(torch, steps_calls)
+    calls = {}
+    for name, L in lay.lin.items():
+        tq, tg = pc[f"quant_{name}"], pc[f"gemm_{name}"]
+        ops = product_ops(M, L["N"], L["Kc"])
+        qb = quant_bytes(M, L["K"], L["Kc"])
+        calls[name] = {"quant_us": tq, "quant_GBs": qb / tq / 1e3, "quant_frac": qb / tq / 1e3 / HBM_PEAK_GBS,
+                       "gemm_us": tg, "gemm_TFLOPs": ops / tg / 1e6, "gemm_frac": ops / tg / 1e6 / DENSE_PEAK_T["fp8"]}
+    detail["headline_per_call"] = row("headline_per_call", tokens=M, rotating_sets=NBUF, calls=calls)
+    # dense FP8 comparator on the same buffers
+    dense_calls = [lay.dense_calls(b) for b in range(NBUF)]
+    try:
+        ms_dense, _ = time_steps(torch, dense_calls, args.steps, args.warmup)
+        pcd = per_call(torch, dense_calls)
+    except Exception as e:  # noqa: BLE001 -- the comparator library may be missing on a stack
+        ms_dense, pcd = None, {"error": repr(e)[:200]}
+    detail["headline_dense"] = row("headline_dense_fp8", ms_per_step=ms_dense, per_call_us=pcd,
+                                   library="hipBLASLt via torch._scaled_mm (bf16 out, same scales)")
+    # offline weight preparation of the layer (2:4 prune + FP8 codes into the tiled layout), per call
+    prep = {}
+    for name, L in lay.lin.items():
+        W = L["W"]
+        bufs = [(torch.empty_like(L["tv"]), torch.empty_like(L["tm"]), torch.empty_like(L["sw"]))
+                for _ in range(rotation(W.numel() * 4))]
+        t = median_us(torch, [lambda o=o: ss.slide_decompose_tiled(W, 2, "fp8", out=o) for o in bufs])
+        b = prep_bytes(L["N"], L["K"], L["Kc"])
+        prep[name] = {"us": t, "GBs": b / t / 1e3, "frac": b / t / 1e3 / HBM_PEAK_GBS}
+        del bufs
+    detail["weight_prep_24_fp8"] = row("weight_prep_24_fp8", per_linear=prep)
+
+    parity, cpu = None, None
+    if not args.no_cpu:
+        parity, cpu = cpu_leg(torch, lay, M, args.cpu_tokens, args.cpu_channels)
+        detail["parity_vs_oracle"] = row("parity_vs_oracle", **parity)
+    out.update({
+        "vs_dense": None if ms_dense is None else ms_dense / ms_step,
+        "gemm_frac": {k: round(v["gemm_frac"], 3) for k, v in calls.items()},
+        "quant_GBs": round(calls["qkv"]["quant_GBs"], 1),
+        "weight_prep_us": round(sum(v["us"] for v in prep.values()), 1),
+    })
+    del lay, steps_calls, dense_calls
+    torch.cuda.empty_cache()
+
+    # ---- the same layer at 4096 tokens, and with 6:8 (INT8 and FP8) ----
+    if not args.no_suite:
+        extra = layer_rows(ss, torch, dev, gen, args, detail)
+        out.update(extra)
+        suite(ss, torch, dev, gen, detail)
+    out["cpu_baseline"] = cpu
+    out["parity_vs_oracle"] = None if parity is None else {
+        k: parity[k] for k in ("ok", "codes_bit_exact", "max_rel_fro", "max_elem_over_bound", "sample")}
+    if args.detail:
+        try:
+            os.makedirs(os.path.dirname(args.detail), exist_ok=True)
+            detail["line"] = out
+            with open(args.detail, "w") as f:
+                json.dump(detail, f, indent=1, default=_round)
+            out["detail"] = os.path.relpath(args.detail, ROOT)
+        except OSError:
+            pass
+    if args.calib_copy:
+        calib_copy(torch, dev)
+    print(json.dumps(out, default=_round, separators=(",", ":")))
 
 
-def suite(ss, torch, dev, reps=10):
-    """Layer-shaped products on synthetic data (seeded on the GPU): Llama-3.1-8B-shaped 2:4 FP8 weight
-    GEMMs at M = 2048..16384 against dense FP8 (hipBLASLt through torch._scaled_mm, same per-token /
-    per-channel scales) and in block-scaled FP8; Qwen2.5-7B-shaped 4:6 and 8:10 INT8 GEMMs at decode and prefill M; the
-    sparse-activation FP8 layer; quant+lift bandwidth on a large batch and a plain device copy."""
+def calib_copy(torch, dev):
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def layer_rows(ss, torch, dev, gen, args, detail):
+    """The 2:4 FP8 layer at 4096 tokens and the 6:8 layers (INT8, FP8) at 4096 tokens, each against dense;
+    returns the summary fields of the last line."""
+    res = {}
+    for (n, q, M) in ((2, "fp8", 4096), (4, "i8", 4096), (4, "fp8", 4096), (4, "i8", 16384), (4, "fp8", 16384)):
+        log(f"[bench] layer n={n} {q} M={M}")
+        lay = Layer(ss, torch, dev, gen, M, n, q, NBUF)
+        sc = [lay.calls(b) for b in range(NBUF)]
+        dc = [lay.dense_calls(b) for b in range(NBUF)]
+        ms, _ = time_steps(torch, sc, args.steps, 2)
+        try:
+            msd, _ = time_steps(torch, dc, args.steps, 2)
+        except Exception:  # noqa: BLE001
+            msd = None
+        pc = per_call(torch, sc)
+        fr = {name: product_ops(M, L["N"], L["Kc"]) / pc[f"gemm_{name}"] / 1e6 / DENSE_PEAK_T[q]
+              for name, L in lay.lin.items()}
+        speed = None if msd is None else msd / ms
+        theo = n / (n - 1)
+        key = f"{'24' if n == 2 else '68'}_{q}_{M}"
+        detail[f"layer_{key}"] = row(f"layer_{key}", pattern="2:4" if n == 2 else "6:8", q=q, tokens=M,
+                                     ms_per_step=ms, dense_ms_per_step=msd, tokens_per_s=M / (ms * 1e-3),
+                                     vs_dense=speed, efficiency=None if speed is None else speed / theo,
+                                     per_call_us=pc, gemm_frac=fr,
+                                     dense_library="torch._int_mm (int32 out, no rescale)" if q == "i8" else
+                                     "torch._scaled_mm (bf16 out)")
+        res[f"l{key}"] = {"tps": round(M / (ms * 1e-3)), "vs_dense": None if speed is None else round(speed, 3),
+                          "gemm_frac_max": round(max(fr.values()), 3)}
+        del lay, sc, dc
+        torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------------------------------------------------
+# CPU oracle baseline and parity on sampled outputs
+
+
+def cpu_leg(torch, lay, M, n_tok, n_ch, seed=7):
+    """The oracle, as it stands, on a sample of the headline layer: ``n_tok`` tokens through all four linears'
+    quantisation and ``n_ch`` output channels of each product (first and last 128 channels plus random ones,
+    so tile edges are covered). The same sample checks the GPU's codes, scales and outputs of the timed steps:
+    codes and scales bit for bit, products against the oracle's exact float64 sums within 1e-2 relative
+    Frobenius error and element by element within 4e-5 sum|terms| + 2^-7 |y| (the matrix core's FP8 sum
+    precision, then one bf16 rounding step)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    log(f"[bench] CPU oracle on {n_tok} tokens x {n_ch} channels per linear")
+    rng = np.random.default_rng(seed)
+    toks = np.unique(np.concatenate([[0, M - 1], rng.choice(M, n_tok - 2, replace=False)]))
+    per_token_s, prep_s = 0.0, 0.0
+    ok, codes_ok, worst_fro, worst_elem = True, True, 0.0, 0.0
+    tok_d = torch.from_numpy(toks).to(lay.lin["qkv"]["sw"].device)
+    for name, L in lay.lin.items():
+        N, K, Kc = L["N"], L["K"], L["Kc"]
+        chans = np.unique(np.concatenate([np.arange(128), np.arange(N - 128, N),
+                                          rng.choice(N, max(n_ch - 256, 0), replace=False)]))
+        ch_d = torch.from_numpy(chans).to(tok_d.device)
+        s = L["sets"][0]
+        Wh = L["W"].index_select(0, ch_d).cpu().numpy()
+        Xh = s["X"].index_select(0, tok_d).view(torch.int16).cpu().numpy().view(np.uint16)
+        yg = s["Y"].index_select(0, tok_d).index_select(1, ch_d).view(torch.int16).cpu().numpy().view(np.uint16)
+        xq_g = s["xq"].index_select(0, tok_d).view(torch.uint8).cpu().numpy()
+        sx_g = s["sx"].index_select(0, tok_d).cpu().numpy()
+        sw_g = L["sw"].index_select(0, ch_d).cpu().numpy()
+        t0 = time.perf_counter()
+        ow = oracle.prune24(Wh, "fp8")  # offline weight prep of the sampled channels (not in the rate)
+        prep_s += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        ox = oracle.quant_lift_act(Xh, 2, "fp8")
+        t_q = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        y = oracle.spgemm("W", ow[0], ow[1], ox[0], Kc, "fp8", ox[1], ow[2], "bf16")
+        t_p = time.perf_counter() - t0
+        per_token_s += t_q / len(toks) + t_p / len(toks) * N / len(chans)
+        codes_ok &= bool(np.array_equal(xq_g, ox[0]) and np.array_equal(sx_g, ox[1]) and np.array_equal(sw_g, ow[2]))
+        # products: sum of |terms| for the element-wise bound
+        a = np.abs(oracle.decompress24(oracle.e4m3_decode(ow[0])[:, : Kc // 2], ow[1], Kc))
+        b = np.abs(oracle.e4m3_decode(ox[0]))[:, :Kc]
+        terms = (b @ a.T) * ox[1].astype(np.float64)[:, None] * ow[2].astype(np.float64)[None, :]
+        yr, yv = _bf16(y), _bf16(yg)
+        den = np.linalg.norm(yr)
+        fro = float(np.linalg.norm(yv - yr) / (den if den > 0 else 1.0))
+        bound = 4e-5 * terms + 2.0 ** -7 * np.abs(yr)
+        elem = float(np.max(np.abs(yv - yr) / np.maximum(bound, 1e-30)))
+        worst_fro, worst_elem = max(worst_fro, fro), max(worst_elem, elem)
+        ok &= fro <= 1e-2 and elem <= 1.0
+    ok &= codes_ok
+    parity = {"ok": bool(ok), "codes_bit_exact": bool(codes_ok), "max_rel_fro": worst_fro,
+              "max_elem_over_bound": worst_elem,
+              "sample": f"{len(toks)} tokens x >= {n_ch} channels per linear, set 0 of the timed steps"}
+    cpu = {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "cpu": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+           "sample": f"{len(toks)} tokens through the four linears: per-token FP8 quant of all K and the product "
+                     f"over >= {n_ch} of each linear's channels, scaled to all channels; float64 BLAS "
+                     f"({threads} threads), element-wise steps single-threaded NumPy; weight prep "
+                     f"({prep_s:.1f} s, offline) not counted"}
+    log(f"[bench] CPU oracle: {cpu['value']:.1f} tokens/s; parity {parity}")
+    return parity, cpu
+
+
+def _bf16(bits):
+    import numpy as np
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------------------------------------------------
+# the other rows
+
+
+def suite(ss, torch, dev, gen, detail):
+    """Rows beyond the Llama layers (stderr + detail file)."""
     import synth
-    print("[bench] layer suite", file=sys.stderr, flush=True)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(20261203)
 
     def randn(shape, std=1.0, dtype=torch.float32):
-        return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std).to(dtype)
+        return (torch.randn(shape, generator=gen, device=dev) * std).to(dtype)
 
-    def timed(fn, n=reps):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n * 1e3  # us
-
-    res = {"data": "synthetic: W ~ N(0, 0.02^2) float32, X ~ N(0, 1) bf16, generated on the GPU (seeded)"}
-    # Llama-3.1-8B-shaped 2:4 FP8 weight GEMMs
-    llama = {}
-    for M in (2048, 4096, 8192, 16384):
-        rows, tot_sp, tot_dn = [], 0.0, 0.0
-        for name, (K, Nout) in synth.LLAMA31_8B_LINEARS.items():
+    # Qwen2.5-7B-shaped 4:6 and 8:10 INT8 linears at decode and prefill token counts, against dense INT8
+    qwen = []
+    for n in (3, 5):
+        tot = {}
+        for name, (K, Nout) in synth.QWEN25_7B_LINEARS.items():
             W = randn((Nout, K), 0.02)
-            wv, wm, sw = ss.prune24(W, "fp8")
-            tv, tm = ss.pack_sparse(wv, wm)
-            wq, swd = ss.quant_lift_act(W, 2, "fp8")
-            del W, wv, wm
-            X = randn((M, K), 1.0, torch.bfloat16)
-            xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
-            sx = torch.empty(M, dtype=torch.float32, device=dev)
-            Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
-            t_q = timed(lambda: ss.quant_lift_act(X, 2, "fp8", out=(xq, sx)))
-            t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, K, tv, tm, xq, sx, sw, "bf16", out=Y))
-            try:
-                t_dn = timed(lambda: torch._scaled_mm(xq, wq.t(), scale_a=sx[:, None], scale_b=swd[None, :],
-                                                      out_dtype=torch.bfloat16))
-            except Exception:
-                t_dn = None
-            dense_eq = 2.0 * M * Nout * K
-            rows.append({"layer": name, "K": K, "N": Nout, "quant_us": t_q, "sparse_gemm_us": t_sp,
-                         "sparse_TOPS_dense_equiv": dense_eq / t_sp / 1e6,
-                         "sparse_frac_of_10070": dense_eq / t_sp / 1e6 / 10070.0,
-                         "dense_fp8_gemm_us": t_dn,
-                         "dense_TFLOPS": None if t_dn is None else dense_eq / t_dn / 1e6})
-            tot_sp += t_q + t_sp
-            tot_dn += t_q + (t_dn if t_dn is not None else float("nan"))
-            del tv, tm, wq, swd, X, xq, sx, Y
-        llama[str(M)] = {"layers": rows, "sparse_tokens_per_s": M / (tot_sp * 1e-6),
-                         "dense_tokens_per_s": M / (tot_dn * 1e-6), "speedup": tot_dn / tot_sp}
-        torch.cuda.empty_cache()
-    res["llama31_8b_24_fp8"] = llama
-    # the same Llama-shaped 2:4 layers with block-scaled FP8 (LLM Compressor W8A8-FP8_BLOCK: 128 x 128 weight
-    # blocks, per-token groups of 128): weight prep, group quant and the product with per-step promotion
-    blk = {}
-    for M in (4096, 8192):
-        rows, tot = [], 0.0
+            tv, tm, sw = ss.slide_decompose_tiled(W, n, "i8")
+            wq, swd = ss.quant_lift_act(W, 2, "i8")
+            del W
+            Kc = ss.lifted_k(K, n)
+            wbytes = tv.numel() + tm.numel() + 4 * Nout
+            nrot = rotation(wbytes)  # weight copies so decode streams them from HBM, not the Infinity Cache
+            ops = [(tv, tm, sw)] + [(tv.clone(), tm.clone(), sw.clone()) for _ in range(nrot - 1)]
+            dops = [wq] + [wq.clone() for _ in range(rotation(wq.numel()) - 1)]
+            for M in (1, 16, 64, 4096):
+                X = randn((M, K), 1.0, torch.bfloat16)
+                xq = torch.empty((M, Kc), dtype=torch.int8, device=dev)
+                xd = torch.empty((M, K), dtype=torch.int8, device=dev)
+                sx = torch.empty(M, dtype=torch.float32, device=dev)
+                sxd = torch.empty(M, dtype=torch.float32, device=dev)
+                Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+                need = ss.spgemm_tiled_workspace_bytes(ss.SS_SPARSE_W, M, Nout, Kc, "i8")
+                ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else False
+                t_q = median_us(torch, [lambda: ss.quant_lift_act(X, n, "i8", out=(xq, sx))])
+                t_sp = median_us(torch, [lambda o=o: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, o[0], o[1], xq, sx,
+                                                                     o[2], "bf16", out=Y, workspace=ws) for o in ops])
+                t_dq = median_us(torch, [lambda: ss.quant_lift_act(X, 2, "i8", out=(xd, sxd))])
+                r = {"pattern": f"{2 * n - 2}:{2 * n}", "layer": name, "M": M, "K": K, "K_prime": Kc, "N": Nout,
+                     "quant_lift_us": t_q, "sparse_gemm_us": t_sp, "weight_copies": nrot,
+                     "sparse_TOPS_dense_equiv": 2.0 * M * Nout * Kc / t_sp / 1e6,
+                     "weight_stream_GBs": wbytes / t_sp / 1e3, "dense_quant_us": t_dq}
+                if M > 16:  # hipBLASLt int8 needs M > 16 through torch._int_mm
+                    try:
+                        t_dn = median_us(torch, [lambda d=d: torch._int_mm(xd, d.t()) for d in dops])
+                    except Exception as e:  # noqa: BLE001
+                        t_dn, r["dense_error"] = None, repr(e)[:120]
+                else:
+                    t_dn = None
+                    r["dense"] = "not measured: torch._int_mm (hipBLASLt int8) requires more than 16 rows"
+                if t_dn is not None:
+                    sp = (t_dq + t_dn) / (t_q + t_sp)
+                    r.update({"dense_gemm_us": t_dn, "vs_dense": sp, "efficiency": sp / (n / (n - 1)),
+                              "gemm_vs_dense": t_dn / t_sp})
+                if M <= 4:  # the same layer in one launch: quant+lift inside the few-token product
+                    t_f = median_us(torch, [lambda o=o: ss.quant_lift_spgemm_decode(X, n, o[0], o[1], o[2], Nout, "i8",
+                                                                                    "bf16", out=Y) for o in ops])
+                    r.update({"fused_us": t_f, "fused_weight_stream_GBs": wbytes / t_f / 1e3})
+                tot.setdefault(M, [0.0, 0.0])
+                tot[M][0] += t_q + t_sp
+                tot[M][1] += (t_dq + t_dn) if t_dn is not None else float("nan")
+                qwen.append(row("qwen25_7b", **r))
+                del X, xq, xd, sx, sxd, Y, ws
+            del ops, dops, tv, tm, sw, wq, swd
+            torch.cuda.empty_cache()
+        for M, (ts, td) in tot.items():
+            sp = td / ts
+            qwen.append(row("qwen25_7b_layer", pattern=f"{2 * n - 2}:{2 * n}", M=M,
+                            tokens_per_s_layer=M / (ts * 1e-6), tokens_per_s_model=M / (ts * 1e-6) / QWEN_LAYERS,
+                            vs_dense=None if math.isnan(sp) else sp,
+                            efficiency=None if math.isnan(sp) else sp / (n / (n - 1))))
+    detail["qwen25_7b_slide_int8"] = qwen
+
+    # online 2:4 prune of activations (X 8192x4096) with FP8 codes, dense FP8 W, against dense FP8
+    M, K, Nout = 8192, 4096, 4096
+    Xs = [randn((M, K), 1.0, torch.bfloat16)]
+    Xs += [Xs[0].clone() for _ in range(rotation(2 * M * K) - 1)]
+    wq, swd = ss.quant_lift_act(randn((Nout, K), 0.02), 2, "fp8")
+    sx = torch.empty(M, dtype=torch.float32, device=dev)
+    nv, nm = ss.tiled_bytes(M, K, "fp8")
+    tv = torch.empty(nv, dtype=torch.uint8, device=dev)
+    tm = torch.empty(nm, dtype=torch.uint8, device=dev)
+    Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+    xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+    t_pr = median_us(torch, [lambda X=X: ss.prune24_act_tiled(X, "fp8", out=(tv, tm, sx)) for X in Xs])
+    t_sp = median_us(torch, [lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, Nout, K, tv, tm, wq, sx, swd, "bf16", out=Y)])
+    t_q = median_us(torch, [lambda X=X: ss.quant_lift_act(X, 2, "fp8", out=(xq, sx)) for X in Xs])
+    try:
+        t_dn = median_us(torch, [lambda: torch._scaled_mm(xq, wq.t(), scale_a=sx[:, None], scale_b=swd[None, :],
+                                                          out_dtype=torch.bfloat16)])
+    except Exception:  # noqa: BLE001
+        t_dn = None
+    pb = 2 * M * K + nv + nm + 4 * M
+    detail["sparse_activation_fp8"] = row(
+        "sparse_activation_fp8", M=M, K=K, N=Nout, prune24_act_tiled_us=t_pr, prune_GBs=pb / t_pr / 1e3,
+        prune_frac=pb / t_pr / 1e3 / HBM_PEAK_GBS, sparse_gemm_us=t_sp,
+        gemm_frac=product_ops(M, Nout, K) / t_sp / 1e6 / DENSE_PEAK_T["fp8"], dense_quant_us=t_q,
+        dense_fp8_gemm_us=t_dn, vs_dense=None if t_dn is None else (t_q + t_dn) / (t_pr + t_sp),
+        input_copies=len(Xs))
+    del Xs, wq, swd, sx, tv, tm, Y, xq
+    torch.cuda.empty_cache()
+
+    # quant+lift bandwidth on 2048 and 16384 tokens (K = 4096), inputs rotated out of the Infinity Cache
+    ql = []
+    for M in (2048, 16384):
+        for n in (2, 4):
+            K = 4096
+            Kc = ss.lifted_k(K, n)
+            byts = quant_bytes(M, K, Kc)
+            nr = rotation(byts)
+            bufs = [(randn((M, K), 1.0, torch.bfloat16), torch.empty((M, Kc), dtype=torch.int8, device=dev),
+                     torch.empty(M, dtype=torch.float32, device=dev)) for _ in range(nr)]
+            t = median_us(torch, [lambda b=b: ss.quant_lift_act(b[0], n, "i8", out=(b[1], b[2])) for b in bufs])
+            ql.append(row("quant_lift_int8", M=M, K=K, n=n, K_prime=Kc, us=t, GBs=byts / t / 1e3,
+                          frac=byts / t / 1e3 / HBM_PEAK_GBS, buffer_sets=nr, working_set_MB=nr * byts / 1e6))
+            del bufs
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = median_us(torch, [lambda: dst.copy_(src)])
+    ql.append(row("device_copy_1GiB", GBs=2 * (1 << 30) / t / 1e3))
+    del src, dst
+    torch.cuda.empty_cache()
+    detail["quant_lift"] = ql
+
+    # block-scaled FP8 (128 x 128 weight blocks, per-token groups of 128) on the Llama-shaped 2:4 layers
+    blk = []
+    for M in (4096,):
+        tot = 0.0
         for name, (K, Nout) in synth.LLAMA31_8B_LINEARS.items():
             W = randn((Nout, K), 0.02)
             tv, tm, sw = ss.prune24_block(W)
-            t_w = timed(lambda: ss.prune24_block(W, out=(tv, tm, sw)), n=3) if M == 4096 else None
             del W
             Kc = ss.lifted_k(K, 2)
             X = randn((M, K), 1.0, torch.bfloat16)
             xq = torch.empty((M, Kc), dtype=torch.float8_e4m3fn, device=dev)
             sx = torch.empty((M, Kc // 128), dtype=torch.float32, device=dev)
             Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
-            t_q = timed(lambda: ss.quant_group_act(X, out=(xq, sx)))
-            t_sp = timed(lambda: ss.spgemm_tiled_block(M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y))
-            hw = 2.0 * M * Nout * Kc
-            qbytes = 2 * M * K + M * Kc + 4 * M * (Kc // 128)
-            row = {"layer": name, "K": K, "N": Nout, "quant_group_us": t_q, "quant_group_GBs": qbytes / t_q / 1e3,
-                   "sparse_gemm_us": t_sp, "sparse_TOPS_dense_equiv": hw / t_sp / 1e6,
-                   "sparse_frac_of_10070": hw / t_sp / 1e6 / 10070.0}
-            if t_w is not None:
-                wbytes = 4 * Nout * K + Nout * Kc // 2 + Nout * Kc // 8 + 4 * ((Nout + 127) // 128) * (Kc // 128)
-                row.update({"prune24_block_us": t_w, "prune24_block_GBs": wbytes / t_w / 1e3})
-            rows.append(row)
+            t_q = median_us(torch, [lambda: ss.quant_group_act(X, out=(xq, sx))])
+            t_sp = median_us(torch, [lambda: ss.spgemm_tiled_block(M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y)])
             tot += t_q + t_sp
+            blk.append(row("block_fp8", layer=name, M=M, K=K, N=Nout, quant_group_us=t_q, sparse_gemm_us=t_sp,
+                           gemm_frac=product_ops(M, Nout, Kc) / t_sp / 1e6 / DENSE_PEAK_T["fp8"]))
             del tv, tm, sw, X, xq, sx, Y
-        blk[str(M)] = {"layers": rows, "sparse_tokens_per_s": M / (tot * 1e-6),
-                       "time_vs_per_channel_24_fp8": llama[str(M)]["sparse_tokens_per_s"] / (M / (tot * 1e-6))}
+        blk.append(row("block_fp8_layer", M=M, tokens_per_s=M / (tot * 1e-6)))
         torch.cuda.empty_cache()
-    res["llama31_8b_24_fp8_block"] = blk
-    # the same Llama-shaped layers with 6:8 (K' = 1.5 K) at M >= 4096, INT8 and FP8, against dense
-    llama68 = {}
-    for q in ("i8", "fp8"):
-        for M in (4096, 8192):
-            rows, tot_sp, tot_dn = [], 0.0, 0.0
-            for name, (K, Nout) in synth.LLAMA31_8B_LINEARS.items():
-                W = randn((Nout, K), 0.02)
-                tv, tm, sw = ss.slide_decompose_tiled(W, 4, q)
-                wq, swd = ss.quant_lift_act(W, 2, q)
-                del W
-                Kc = ss.lifted_k(K, 4)
-                X = randn((M, K), 1.0, torch.bfloat16)
-                qdt = torch.int8 if q == "i8" else torch.float8_e4m3fn
-                xl = torch.empty((M, Kc), dtype=qdt, device=dev)
-                xq = torch.empty((M, K), dtype=qdt, device=dev)
-                sx = torch.empty(M, dtype=torch.float32, device=dev)
-                sx2 = torch.empty(M, dtype=torch.float32, device=dev)
-                Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
-                t_q = timed(lambda: ss.quant_lift_act(X, 4, q, out=(xl, sx)))
-                t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, tv, tm, xl, sx, sw, "bf16", out=Y))
-                t_dq = timed(lambda: ss.quant_lift_act(X, 2, q, out=(xq, sx2)))
-                try:
-                    if q == "i8":
-                        t_dn = timed(lambda: torch._int_mm(xq, wq.t()))
-                    else:
-                        t_dn = timed(lambda: torch._scaled_mm(xq, wq.t(), scale_a=sx2[:, None], scale_b=swd[None, :],
-                                                              out_dtype=torch.bfloat16))
-                except Exception:
-                    t_dn = None
-                hw = 2.0 * M * Nout * Kc
-                rows.append({"layer": name, "K": K, "K_prime": Kc, "N": Nout, "quant_lift_us": t_q,
-                             "sparse_gemm_us": t_sp, "sparse_TOPS_dense_equiv": hw / t_sp / 1e6,
-                             "sparse_frac_of_10070": hw / t_sp / 1e6 / 10070.0,
-                             "effective_TOPS": 2.0 * M * Nout * K / t_sp / 1e6,
-                             "dense_quant_us": t_dq, "dense_gemm_us": t_dn})
-                tot_sp += t_q + t_sp
-                tot_dn += t_dq + (t_dn if t_dn is not None else float("nan"))
-                del tv, tm, sw, wq, swd, X, xl, xq, sx, sx2, Y
-            llama68[f"{q}_{M}"] = {"layers": rows, "sparse_tokens_per_s": M / (tot_sp * 1e-6),
-                                   "dense_tokens_per_s": M / (tot_dn * 1e-6), "speedup": tot_dn / tot_sp,
-                                   "dense_library": "hipBLASLt (torch._int_mm int32 out / torch._scaled_mm bf16 out)"}
-            torch.cuda.empty_cache()
-    res["llama31_8b_68"] = llama68
-    # Qwen2.5-7B-shaped sliding-window INT8 GEMMs, decode and prefill token counts
-    qwen = []
-    for n in (3, 5):
-        for name, (K, Nout) in synth.QWEN25_7B_LINEARS.items():
-            W = randn((Nout, K), 0.02)
-            wv, wm, sw = ss.slide_decompose(W, n, "i8")
-            tv, tm = ss.pack_sparse(wv, wm)
-            Kc = ss.lifted_k(K, n)
-            del W, wv, wm
-            for M in (1, 16, 64, 4096):
-                X = randn((M, K), 1.0, torch.bfloat16)
-                xq = torch.empty((M, Kc), dtype=torch.int8, device=dev)
-                sx = torch.empty(M, dtype=torch.float32, device=dev)
-                Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
-                need = ss.spgemm_tiled_workspace_bytes(ss.SS_SPARSE_W, M, Nout, Kc, "i8")
-                ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else False
-                t_q = timed(lambda: ss.quant_lift_act(X, n, "i8", out=(xq, sx)))
-                t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y,
-                                                     workspace=ws))
-                wbytes = tv.numel() + tm.numel()
-                row = {"pattern": f"{2 * n - 2}:{2 * n}", "layer": name, "M": M, "K": K, "K_prime": Kc,
-                       "N": Nout, "quant_lift_us": t_q, "sparse_gemm_us": t_sp, "split_k_workspace_bytes": need,
-                       "sparse_TOPS_dense_equiv": 2.0 * M * Nout * Kc / t_sp / 1e6,
-                       "weight_stream_GBs": wbytes / t_sp / 1e3,
-                       "tokens_per_s": M / ((t_q + t_sp) * 1e-6)}
-                if M <= 64:  # decode: the quant+lift / product pair replayed from a HIP graph (no launch gaps)
-                    graph = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(graph):
-                        ss.quant_lift_act(X, n, "i8", out=(xq, sx))
-                        ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, tv, tm, xq, sx, sw, "bf16", out=Y, workspace=ws)
-                    t_g = timed(graph.replay)
-                    row.update({"graph_pair_us": t_g, "graph_tokens_per_s": M / (t_g * 1e-6)})
-                    del graph
-                if M <= 4:  # the same layer in one launch: quant+lift inside the few-token product
-                    t_f = timed(lambda: ss.quant_lift_spgemm_decode(X, n, tv, tm, sw, Nout, "i8", "bf16", out=Y))
-                    row.update({"fused_us": t_f, "fused_tokens_per_s": M / (t_f * 1e-6),
-                                "fused_weight_stream_GBs": wbytes / t_f / 1e3})
-                qwen.append(row)
-                del X, xq, sx, Y, ws
-            del tv, tm
-            torch.cuda.empty_cache()
-    res["qwen25_7b_slide_int8"] = qwen
-    # sparse-activation layer: X 8192x4096 pruned 2:4 online (FP8), dense W 4096x4096 FP8
-    M, K, Nout = 8192, 4096, 4096
-    X = randn((M, K), 1.0, torch.bfloat16)
-    wq, swd = ss.quant_lift_act(randn((Nout, K), 0.02), 2, "fp8")
-    sx = torch.empty(M, dtype=torch.float32, device=dev)
-    nv, nm = ss.tiled_bytes(M, K)
-    tv = torch.empty(nv, dtype=torch.uint8, device=dev)
-    tm = torch.empty(nm, dtype=torch.uint8, device=dev)
-    Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
-    xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
-    t_pr = timed(lambda: ss.prune24_act_tiled(X, "fp8", out=(tv, tm, sx)))
-    t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, Nout, K, tv, tm, wq, sx, swd, "bf16", out=Y))
-    t_q = timed(lambda: ss.quant_lift_act(X, 2, "fp8", out=(xq, sx)))
-    try:
-        t_dn = timed(lambda: torch._scaled_mm(xq, wq.t(), scale_a=sx[:, None], scale_b=swd[None, :],
-                                              out_dtype=torch.bfloat16))
-    except Exception:
-        t_dn = None
-    res["sparse_activation_fp8"] = {
-        "M": M, "K": K, "N": Nout, "prune24_act_tiled_us": t_pr, "sparse_gemm_us": t_sp,
-        "sparse_TOPS_dense_equiv": 2.0 * M * Nout * K / t_sp / 1e6, "dense_quant_us": t_q,
-        "dense_fp8_gemm_us": t_dn,
-        "speedup_vs_dense": None if t_dn is None else (t_q + t_dn) / (t_pr + t_sp)}
-    del X, wq, swd, sx, tv, tm, Y, xq
-    torch.cuda.empty_cache()
-    # the same layer in bf16 (no quantisation): online prune + pack + product against dense bf16 (hipBLASLt)
-    X = randn((M, K), 1.0, torch.bfloat16)
-    Wb = randn((Nout, K), 0.02, torch.bfloat16)
-    nv, nm = ss.tiled_bytes(M, K, "bf16")
-    tv = torch.empty(nv, dtype=torch.uint8, device=dev)
-    tm = torch.empty(nm, dtype=torch.uint8, device=dev)
-    Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
-    t_pr = timed(lambda: ss.prune24_act_tiled(X, "bf16", out=(tv, tm, None)))
-    t_sp = timed(lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, Nout, K, tv, tm, Wb, None, None, "bf16", out=Y))
-    t_dn = timed(lambda: torch.matmul(X, Wb.t()))
-    res["sparse_activation_bf16"] = {
-        "M": M, "K": K, "N": Nout, "prune24_act_tiled_us": t_pr, "sparse_gemm_us": t_sp,
-        "sparse_TFLOPS_dense_equiv": 2.0 * M * Nout * K / t_sp / 1e6,
-        "sparse_frac_of_5030": 2.0 * M * Nout * K / t_sp / 1e6 / 5030.0, "dense_bf16_gemm_us": t_dn,
-        "speedup_vs_dense": t_dn / (t_pr + t_sp)}
-    del X, Wb, tv, tm, Y
-    torch.cuda.empty_cache()
-    # online 2:4 on the attention operand roles, bf16, one batched launch over 32 heads (Llama-3.1-8B: 32 heads
-    # of 128) at 4096 tokens: S = Q K^T with Q pruned along the head dimension (K' = 128 padded to 256, the
-    # product's step alignment), O = P V with the probabilities pruned along the keys; dense torch.bmm beside
+    detail["block_fp8"] = blk
+
+    # online 2:4 on the attention operand roles (bf16), 32 heads x 4096 tokens x 128, one batched launch
     H, L, d = 32, 4096, 128
     Kq = ss.lifted_k(d, 2)
     Q = randn((H * L, d), 1.0, torch.bfloat16)
@@ -543,138 +665,32 @@ def suite(ss, torch, dev, reps=10):
     tvq = torch.empty(nv, dtype=torch.uint8, device=dev)
     tmq = torch.empty(nm, dtype=torch.uint8, device=dev)
     S = torch.empty((H, L, L), dtype=torch.bfloat16, device=dev)
-    t_pq = timed(lambda: ss.prune24_act_tiled(Q, "bf16", out=(tvq, tmq, None)))
-    t_qk = timed(lambda: ss.spgemm_tiled_batched(ss.SS_SPARSE_X, H, L, L, Kq, tvq, tmq, Kp, None, None, "bf16", out=S))
+    t_pq = median_us(torch, [lambda: ss.prune24_act_tiled(Q, "bf16", out=(tvq, tmq, None))])
+    t_qk = median_us(torch, [lambda: ss.spgemm_tiled_batched(ss.SS_SPARSE_X, H, L, L, Kq, tvq, tmq, Kp, None, None,
+                                                             "bf16", out=S)])
     Qh, Kt = Q.view(H, L, d), Kp[:, :, :d].transpose(1, 2).contiguous()
-    t_qk_dn = timed(lambda: torch.bmm(Qh, Kt))
-    del Q, Kp, tvq, tmq, Qh, Kt
+    t_qk_dn = median_us(torch, [lambda: torch.bmm(Qh, Kt)])
+    del Q, Kp, tvq, tmq, Qh, Kt, S
     P = torch.softmax(randn((H * L, L), 2.0), dim=1).to(torch.bfloat16)
     Vt = randn((H, d, L), 1.0, torch.bfloat16)
     nv, nm = ss.tiled_bytes(H * L, L, "bf16")
     tvp = torch.empty(nv, dtype=torch.uint8, device=dev)
     tmp = torch.empty(nm, dtype=torch.uint8, device=dev)
     O = torch.empty((H, L, d), dtype=torch.bfloat16, device=dev)
-    t_pp = timed(lambda: ss.prune24_act_tiled(P, "bf16", out=(tvp, tmp, None)))
-    t_pv = timed(lambda: ss.spgemm_tiled_batched(ss.SS_SPARSE_X, H, L, d, L, tvp, tmp, Vt, None, None, "bf16", out=O))
+    t_pp = median_us(torch, [lambda: ss.prune24_act_tiled(P, "bf16", out=(tvp, tmp, None))])
+    t_pv = median_us(torch, [lambda: ss.spgemm_tiled_batched(ss.SS_SPARSE_X, H, L, d, L, tvp, tmp, Vt, None, None,
+                                                             "bf16", out=O)])
     Ph, V = P.view(H, L, L), Vt.transpose(1, 2).contiguous()
-    t_pv_dn = timed(lambda: torch.bmm(Ph, V))
-    fl = 2.0 * H * L * L * d
-    res["attention_roles_bf16"] = {
-        "heads": H, "tokens": L, "head_dim": d,
-        "qk": {"prune_q_us": t_pq, "sparse_batched_us": t_qk, "dense_bmm_us": t_qk_dn,
-               "sparse_TFLOPS_dense_equiv": 2.0 * H * L * L * Kq / t_qk / 1e6,
-               "speedup_vs_dense": t_qk_dn / (t_pq + t_qk)},
-        "pv": {"prune_p_us": t_pp, "sparse_batched_us": t_pv, "dense_bmm_us": t_pv_dn,
-               "sparse_TFLOPS_dense_equiv": fl / t_pv / 1e6, "sparse_frac_of_5030": fl / t_pv / 1e6 / 5030.0,
-               "speedup_vs_dense": t_pv_dn / (t_pp + t_pv), "product_speedup_vs_dense": t_pv_dn / t_pv}}
-    del P, Vt, tvp, tmp, O, Ph, V, S
+    t_pv_dn = median_us(torch, [lambda: torch.bmm(Ph, V)])
+    detail["attention_roles_bf16"] = row(
+        "attention_roles_bf16", heads=H, tokens=L, head_dim=d,
+        qk={"prune_q_us": t_pq, "sparse_batched_us": t_qk, "dense_bmm_us": t_qk_dn,
+            "vs_dense": t_qk_dn / (t_pq + t_qk)},
+        pv={"prune_p_us": t_pp, "sparse_batched_us": t_pv, "dense_bmm_us": t_pv_dn,
+            "gemm_frac": 2.0 * H * L * L * d / 2 / t_pv / 1e6 / DENSE_PEAK_T["bf16"],
+            "vs_dense": t_pv_dn / (t_pp + t_pv), "product_vs_dense": t_pv_dn / t_pv})
+    del P, Vt, tvp, tmp, O, Ph, V
     torch.cuda.empty_cache()
-    # quant+lift on a large batch (launch latency amortised) and a plain device copy
-    ql = {}
-    for n in (2, 4):
-        M, K = 16384, 4096
-        X = randn((M, K), 1.0, torch.bfloat16)
-        Kc = ss.lifted_k(K, n)
-        xq = torch.empty((M, Kc), dtype=torch.int8, device=dev)
-        sx = torch.empty(M, dtype=torch.float32, device=dev)
-        t = timed(lambda: ss.quant_lift_act(X, n, "i8", out=(xq, sx)))
-        byts = 2 * M * K + M * Kc + 4 * M
-        ql[f"n{n}"] = {"M": M, "K": K, "K_prime": Kc, "us": t, "GB/s": byts / t / 1e3,
-                       "frac_of_8000": byts / t / 1e3 / 8000.0}
-        del X, xq, sx
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    t = timed(lambda: dst.copy_(src), n=5)
-    ql["device_copy_1GiB_GBs"] = 2 * (1 << 30) / t / 1e3
-    del src, dst
-    torch.cuda.empty_cache()
-    res["quant_lift_large_int8"] = ql
-    return res
-
-
-def read_sclk_mhz():
-    """Current engine clock from the amdgpu sysfs DPM table (the level marked '*'), or None."""
-    import glob
-    import re
-    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            for line in open(path).read().splitlines():
-                if line.rstrip().endswith("*"):
-                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
-                    if m:
-                        return int(m.group(1))
-        except OSError:
-            continue
-    return None
-
-
-def sample_sclk(launch, torch, seconds=0.3, period=0.002):
-    """Launch `launch` back to back for `seconds` while a thread samples the engine clock."""
-    import statistics
-    import threading
-    if read_sclk_mhz() is None:
-        return {"error": "no readable pp_dpm_sclk"}
-    samples, stop = [], threading.Event()
-
-    def run():
-        while not stop.is_set():
-            v = read_sclk_mhz()
-            if v is not None:
-                samples.append(v)
-            time.sleep(period)
-
-    th = threading.Thread(target=run)
-    launch()
-    torch.cuda.synchronize()
-    th.start()
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for _ in range(50):
-            launch()
-        torch.cuda.synchronize()
-    stop.set()
-    th.join()
-    if not samples:
-        return {"error": "no samples"}
-    return {"samples": len(samples), "median": statistics.median(samples), "min": min(samples),
-            "max": max(samples), "idle_after": read_sclk_mhz()}
-
-
-def cpu_baseline(X_np, W_np, Kc68, Kc24):
-    """The oracle, as it stands, on one whole step of the same batch."""
-    import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
-    print("[bench] CPU oracle: three full steps", file=sys.stderr, flush=True)
-
-    outs = {}
-
-    def one_step():
-        t0 = time.perf_counter()
-        w68 = oracle.slide_decompose(W_np, PAT, "i8")
-        x68 = oracle.quant_lift_act(X_np, PAT, "i8")
-        y68 = oracle.spgemm("W", w68[0], w68[1], x68[0], Kc68, "i8", x68[1], w68[2], "bf16")
-        w24 = oracle.prune24(W_np, "i8")
-        x24 = oracle.quant_lift_act(X_np, 2, "i8")
-        y24 = oracle.spgemm("W", w24[0], w24[1], x24[0], Kc24, "i8", x24[1], w24[2], "bf16")
-        xs = oracle.prune24_act(X_np, "i8")
-        wq = oracle.quant_lift_act(W_np, 2, "i8")
-        yx = oracle.spgemm("X", xs[0], xs[1], wq[0], Kc24, "i8", xs[2], wq[1], "bf16")
-        dt = time.perf_counter() - t0
-        outs.update(y68=y68, y24=y24, yx=yx)
-        return dt
-
-    times = sorted(one_step() for _ in range(3))
-    t = times[1]
-    return outs, {"value": M / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole step (the same 9 calls; the tiled layout is a GPU storage detail with no oracle "
-                      f"counterpart, M={M} tokens), median of 3 runs: {t:.2f} s (runs {times[0]:.2f}-{times[2]:.2f} s); "
-                      f"products in float64 BLAS ({threads} threads), element-wise steps single-threaded NumPy; "
-                      f"host CPUs visible: {len(os.sched_getaffinity(0))}"}
 
 
 if __name__ == "__main__":

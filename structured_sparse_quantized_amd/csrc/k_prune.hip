@@ -11,6 +11,9 @@
 
 #include <algorithm>
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 namespace ss {
 
@@ -399,6 +402,37 @@ hipError_t launch_prune24_block(bool in_bf16, const void* W, int64_t ldw, int64_
     hipLaunchKernelGGL(prune24_block_kernel<float>, grid, dim3(kBlock), 0, st, static_cast<const float*>(W), ldw,
                        (int)rows, (int)K, KS, KSP, v, tm, sw);
   return hipGetLastError();
+}
+
+// Dynamic-LDS limit of a kernel, raised once per device and kernel: the attribute persists, so later launches
+// that need no more bytes skip the runtime call.
+hipError_t lds_limit(const void* kern, int bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> have;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> g(mu);
+  int& cur = have[{kern, dev}];
+  if (cur >= bytes) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) cur = bytes;
+  return e;
+}
+
+// Resident workgroups per CU of a kernel at a block size and dynamic LDS size, cached per device.
+int occupancy_p(const void* kern, int block, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, int, size_t>, int> have;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> g(mu);
+  const auto key = std::make_tuple(kern, dev, block, lds);
+  const auto it = have.find(key);
+  if (it != have.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, block, lds) != hipSuccess || n < 1) n = 1;
+  have[key] = n;
+  return n;
 }
 
 int num_cus_p() {

@@ -512,7 +512,7 @@ hipError_t launch_one(const TIn* W, int64_t ldw, int64_t rows, int64_t K, uint8_
   if (!small) {
     const void* fn = (const void*)slide_kernel<TIn, N, OUT, TILED>;
     if (image > 64 * 1024) {
-      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)image);
+      const hipError_t e = lds_limit(fn, (int)image);
       if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((slide_kernel<TIn, N, OUT, TILED>), dim3((unsigned)nrows), dim3(kBlock), image, st, W, ldw, rows,
@@ -523,11 +523,11 @@ hipError_t launch_one(const TIn* W, int64_t ldw, int64_t rows, int64_t K, uint8_
   // per CU; a multiple of 8 when it is smaller than the row count (xcd_row order)
   auto go = [&](auto kern) -> hipError_t {
     if (staged > 64 * 1024) {
-      const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)staged);
+      const hipError_t e = lds_limit((const void*)kern, (int)staged);
       if (e != hipSuccess) return e;
     }
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, staged) != hipSuccess || per_cu < 1) per_cu = 1;
+    per_cu = occupancy_p((const void*)kern, kBlock, staged);
     per_cu = std::min(per_cu, 8);
     const unsigned grid = (unsigned)std::min<int64_t>(nrows, (int64_t)num_cus_p() * per_cu);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), staged, st, W, ldw, (int)rows, (int)K, v, ldv_bytes, meta, ldm,

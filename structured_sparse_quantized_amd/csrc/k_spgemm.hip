@@ -417,8 +417,7 @@ static hipError_t launch_sg2(bool side_x, int64_t R, int64_t C, int64_t Kc, cons
     const int tr = (int)((R + pipe8::BM - 1) / pipe8::BM), tc = (int)((C + pipe8::BN - 1) / pipe8::BN);
     const int KT = (int)(Kc / 256);
     auto kern = side_x ? pipe8::spgemm8_kernel<AB, YT, true> : pipe8::spgemm8_kernel<AB, YT, false>;
-    // set at every launch: the attribute is per device, and the call is cheap and thread-safe
-    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, pipe8::LDS);
+    const hipError_t e = lds_limit((const void*)kern, pipe8::LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * pipe8::NW), pipe8::LDS, st, (int)R, (int)C, KT, av, (int)lda, am,
                        (int)ldm, bd, (int)ldb, sx, sw, Y, (int)ldy, tr, tc);

@@ -505,7 +505,7 @@ hipError_t launch_batched(int batch, int R, int C, int KS, const uint8_t* tv, in
                           int64_t s_tm, const uint8_t* bd, int64_t s_bd, int ldb, const float* sx, int64_t s_sx,
                           const float* sw, int64_t s_sw, void* Y, int64_t s_y, int ldy, hipStream_t st) {
   auto kern = spgemm_batched_kernel<AB, YT, SIDE_X>;
-  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_SC);
+  const hipError_t e = lds_limit((const void*)kern, LDS_SC);
   if (e != hipSuccess) return e;
   const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
   hipLaunchKernelGGL(kern, dim3(tr * tc, batch), dim3(64 * NW), LDS_SC, st, R, C, KS, tv, s_tv, tm, s_tm, bd, s_bd, ldb, sx,
@@ -518,8 +518,7 @@ hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, co
                   const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
   auto kern = spgemm_kernel<AB, YT, SIDE_X, BS>;
   constexpr int lds = BS ? LDS_BS : LDS_SC;
-  // set at every launch: the attribute is per device, and the call is cheap and thread-safe
-  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const hipError_t e = lds_limit((const void*)kern, lds);
   if (e != hipSuccess) return e;
   const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
   hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * NW), lds, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, tr, tc);
@@ -1051,7 +1050,7 @@ hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, co
   const int nrg = ((R + 15) / 16 + NW - 1) / NW;
   const dim3 grid((unsigned)nrg, (unsigned)p.splits);
   auto go = [&](auto kern) -> hipError_t {
-    const hipError_t a = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    const hipError_t a = lds_limit((const void*)kern, LDS);
     if (a != hipSuccess) return a;
     hipLaunchKernelGGL(kern, grid, dim3(64 * NW), LDS, st, R, C, KS, p.gps, tv, tm, bd, ldb, ws, p.rp);
     return hipGetLastError();
@@ -1148,7 +1147,7 @@ hipError_t launch_quant_lift_spgemm(bool x_bf16, int ab, int yt, const void* X, 
   const int64_t nrb = (N + 15) / 16;
   const unsigned grid = (unsigned)std::min<int64_t>(nrb, per_cu * num_cus_p());
   auto go = [&](auto kern, const auto* x) -> hipError_t {
-    const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = lds_limit((const void*)kern, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * decode::NW), lds, st, R, m, k, n, ks, x, ldx, tv, tm, sw, Y, ly,
                        sx_out);

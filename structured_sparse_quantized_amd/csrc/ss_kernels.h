@@ -7,6 +7,11 @@ namespace ss {
 
 // Compute units of the current device (cached).
 int num_cus_p();
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device (the runtime call runs once per device,
+// kernel and larger size).
+hipError_t lds_limit(const void* kern, int bytes);
+// Resident workgroups per CU (cached per device, kernel, block size and LDS bytes; at least 1).
+int occupancy_p(const void* kern, int block, size_t lds);
 
 hipError_t launch_quant_lift(bool x_bf16, bool fp8, const void* X, int64_t ldx, int64_t M, int64_t K, int n,
                              void* Xq, int64_t ldq, int64_t Kc, float* sx, hipStream_t st);
