@@ -54,14 +54,12 @@
 
 #include "ss_device.h"
 #include "ss_kernels.h"
+#include "ss_mma.h"
 #include "ss_store.h"
 
 namespace ss {
 namespace tiled {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 #define SS_LDS __attribute__((address_space(3)))
 
 constexpr int BM = 256, BN = 128, WGM = 4, WGN = 2, NW = WGM * WGN, S = 4;
@@ -75,52 +73,6 @@ constexpr int SC_BYTES = (BM + BN) * 4;                        // epilogue scale
 constexpr int LDS_SC = LDS + SC_BYTES;
 static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN, "load split");
 static_assert(S >= 3 && S <= 5, "wait counts below assume 3..5 stages");
-
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v16bf __attribute__((ext_vector_type(16)));
-
-// AB: 0 = int8, 1 = fp8 (16x16x128), 2 = bf16 (16x16x64; HALF selects the 16-bit index half)
-template <int AB> struct Mma;
-template <> struct Mma<0> {
-  using Acc = v4i;
-  template <int HALF> __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
-    return __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, idx, 0, 0);
-  }
-};
-template <> struct Mma<1> {
-  using Acc = v4f;
-  template <int HALF> __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
-    return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, idx,
-                                                          0, 0);
-  }
-};
-template <> struct Mma<2> {
-  using Acc = v4f;
-  template <int HALF> __device__ static Acc run(v4i a, v4i b0, v4i b1, Acc c, int idx) {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
-        __builtin_bit_cast(v8bf, a), __builtin_bit_cast(v16bf, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7)), c,
-        idx, 0, HALF);
-  }
-};
-
-// Per element size: index bytes per lane per step, and the block of one row block's 4-step index group.
-template <int AB> struct Meta {
-  static constexpr int ES = AB == 2 ? 2 : 1;  // value bytes
-  static constexpr int WB = 4 / ES;           // index bytes per lane per step
-  static constexpr int BLOCK = 256 * WB;      // bytes of one row block's 4-step group
-  using V = typename std::conditional<AB == 2, v2i, v4i>::type;
-  // the 32-bit word holding step q's index (bf16: two steps per word)
-  __device__ static int word(const V& m, int q) { return AB == 2 ? m[q >> 1] : m[q]; }
-};
-// one instruction with step q's index
-template <int AB, int Q, typename Acc>
-__device__ __forceinline__ Acc mma_step(v4i a, v4i b0, v4i b1, Acc c, const typename Meta<AB>::V& m) {
-  return Mma<AB>::template run<AB == 2 ? (Q & 1) : 0>(a, b0, b1, c, Meta<AB>::word(m, Q));
-}
-
-// B rows in LDS: 8 rows x 128 bytes per 1 KB block; chunk c of row r sits at chunk position c ^ (r % 8).
-__device__ __forceinline__ int swz(int c, int r16) { return c ^ (r16 & 7); }
 
 // One thread per (row block, 4-step group, lane); 4 row blocks per workgroup. ES = value bytes; ldv in
 // bytes.
@@ -1092,6 +1044,14 @@ static bool few_tokens(bool side_x, int64_t R, int64_t C) {
   const int64_t tiles = ((R + tiled::BM - 1) / tiled::BM) * ((C + tiled::BN - 1) / tiled::BN);
   return !side_x && C <= 64 && (C <= 8 || tiles < 128);
 }
+// The wide-tile prefill kernel (k_spgemm_wide.hip) on the weight-sparse side: large problems only, where
+// its 256 x 256 tiles still give every CU four or more tiles and the sparse operand is tall (N >= 16384) or
+// the reduction long (K' >= 8192 positions of 8-bit codes). Measured 1.1-1.25x the 256 x 128 kernel on
+// Llama-shaped gate_up (4096 and 16384 tokens) and down (16384 tokens); slower on the smaller layers.
+static bool use_wide(bool side_x, int64_t R, int64_t C, int64_t KS) {
+  const int64_t tiles = ((R + 255) / 256) * ((C + 255) / 256);
+  return !side_x && tiles >= 4 * (int64_t)num_cus_p() && (R >= 16384 || KS >= 64);
+}
 // The split-K path (with a workspace) serves the few-token products with more than 16 tokens.
 static bool use_splitk(bool side_x, int64_t R, int64_t C) { return few_tokens(side_x, R, C) && C > 16; }
 
@@ -1180,6 +1140,8 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
   // few tokens: split-K when a workspace is given and the problem uses one, else the row-block decode kernel
   const bool dec = few_tokens(side_x, R, C);
   const bool spk = ws != nullptr && use_splitk(side_x, R, C);
+  if (!spk && !dec && use_wide(side_x, R, C, ks))
+    return launch_spgemm_wide(ab, yt, r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st);
 #define SS_TL(AB_, YT_)                                                                                   \
   return spk      ? splitk::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, ws, st)               \
          : dec    ? decode::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)                   \

@@ -1,0 +1,407 @@
+// Wide-tile prefill product on the tiled sparse operand (gfx950 v_smfmac), with the per-token x
+// per-channel rescale epilogue. Deep reading of arXiv 2610.28947 (introduction: one operand keeps two of
+// every four along the accumulate axis; section 3.1: sparse W or sparse X); LLM Compressor W8A8 scales.
+//
+// C[r][c] = sum_k A[r][k] B[c][k]; A = the tiled compressed operand (rows r), B = the dense operand (rows c),
+// as in the 256 x 128 product of k_spgemm_tiled.hip, whose tiled layout this kernel reads unchanged.
+//
+// Why a wider tile: a 16x16x128 sparse instruction does the work of a dense 16x16x128 one in half the
+// matrix-core cycles, so per cycle it needs twice the operand bytes. A 256 x 256 tile moves 48 KB of
+// operands (16 KB of compressed A values, 32 KB of dense B rows) into LDS per 128-position step for
+// 16.8 M dense-equivalent operations -- 25% fewer L2 -> LDS bytes per operation than 256 x 128 -- and
+// waves of 128 x 128 read 25% fewer LDS bytes per operation than waves of 64 x 64.
+//
+// Workgroup: four waves (one per SIMD) in a 2 x 2 grid, each 128 A rows x 128 B rows = 8 x 8 instructions
+// per step; the 256 accumulator registers per lane sit in the accumulation registers, and the A and B
+// fragments are double-buffered in ordinary registers (the fragments of step j+1 are read from LDS while
+// the instructions of step j run), column by column of B.
+// LDS: a ring of three stages (48 KB each) filled by LDS DMA (global_load_lds, 1 KB per wave instruction;
+// B rows swizzled so fragment reads are conflict-free), and one 16 KB slot holding the index words of the
+// current 4-step group (the tiled layout's metadata block of each of the 16 row blocks, brought in by DMA
+// one group ahead and read into registers after the last instruction of the group before). The slot takes the
+// tile's epilogue scales during the last group.
+// Synchronisation: one barrier per step. At the top of step j every wave waits until its own loads of
+// stage j+1 have landed (loads complete in issue order, so this is a wait for a fixed count of later
+// loads) and its own LDS reads are done, then the barrier makes stage j+1 visible and frees the slot of
+// stage j (read during step j-1), into which stage j+3 is issued.
+#include <algorithm>
+
+#include "ss_device.h"
+#include "ss_kernels.h"
+#include "ss_mma.h"
+#include "ss_store.h"
+
+namespace ss {
+namespace wide {
+
+using tiled::Meta;
+using tiled::Mma;
+using tiled::swz;
+using tiled::v4i;
+#define SS_LDS __attribute__((address_space(3)))
+
+constexpr int BM = 256, BN = 256, NW = 4, WGN = 2, S = 3;
+constexpr int TI = 8, TJ = 8;                         // 8 x 8 instructions per wave per step
+constexpr int RBT = BM / 16;                          // row blocks of the sparse operand per tile
+constexpr int PA = RBT / NW, PB = BN / 8 / NW;        // LDS DMA loads per wave per step (1 KB each): 4 + 8
+constexpr int LPW = PA + PB;
+constexpr int A_BYTES = BM * 64, STAGE = A_BYTES + BN * 128;  // 16 KB + 32 KB
+constexpr int META = S * STAGE;                               // index-word slot (then the epilogue scales)
+constexpr int NSC = 2;                                        // scale loads per wave (A rows, B rows)
+template <int AB> constexpr int meta_slot() { return RBT * Meta<AB>::BLOCK; }           // 16 KB / 8 KB
+template <int AB> constexpr int mpw() { return meta_slot<AB>() / 1024 / NW; }          // meta loads per wave
+template <int AB> constexpr int lds_bytes() { return META + meta_slot<AB>(); }
+static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN, "load split");
+static_assert((BM + BN) * 4 <= 8 * 1024, "the epilogue scales fit the index-word slot");
+
+constexpr int vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }  // s_waitcnt vmcnt(n)
+
+template <int AB, int YT, bool SIDE_X, int GR>
+__global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, const uint8_t* __restrict__ tv,
+                                                          const uint8_t* __restrict__ tm,
+                                                          const uint8_t* __restrict__ bd, int ldb,
+                                                          const float* __restrict__ sx, const float* __restrict__ sw,
+                                                          void* __restrict__ Y, int ldy, int tiles_r, int tiles_c) {
+  using Acc = typename Mma<AB>::Acc;
+  using MT = Meta<AB>;
+  using MV = typename MT::V;
+  constexpr int MPW = mpw<AB>();
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int r16 = lane & 15, jj = lane >> 4;
+
+  // Tile order: workgroups are dealt to the 8 XCDs round-robin; each XCD takes a contiguous run of tiles,
+  // walked in groups of GR A-row tiles, so the tiles that share operands also share an L2.
+  const int nb = gridDim.x;
+  int bid = blockIdx.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int group = bid / (GR * tiles_c), first_r = group * GR, gsize = min(tiles_r - first_r, GR);
+  const int tr = first_r + (bid % (GR * tiles_c)) % gsize, tc = (bid % (GR * tiles_c)) / gsize;
+  const int r0 = tr * BM, c0 = tc * BN;
+  const int nrb = (R + 15) / 16, KS4 = (KS + 3) / 4, KSP = 4 * KS4, G = KS4;
+
+  // Per-lane DMA sources. Rows past the end are clamped to the last row (block); their results are never
+  // stored. Sparse rows past R inside the last row block are zero in the tiled layout.
+  // (uniform bases in scalar registers, one 32-bit lane offset)
+  const uint32_t l16 = lane * 16;
+  const uint8_t* pa[PA];
+#pragma unroll
+  for (int q = 0; q < PA; ++q) pa[q] = tv + (int64_t)min(r0 / 16 + wave + q * NW, nrb - 1) * KSP * 1024;
+  uint32_t offb[PB];
+#pragma unroll
+  for (int q = 0; q < PB; ++q) {
+    const int b = (wave + q * NW) * 8 + (lane >> 3);
+    offb[q] = (uint32_t)min(c0 + b, C - 1) * (uint32_t)ldb + swz(lane & 7, b & 15) * 16;
+  }
+  // index-word DMA: instruction i of this wave brings bytes 1024 (wave + NW i) + 16 lane of the slot, i.e.
+  // row block rb of the tile at offset off of its group block
+  // (8-bit: one row block per instruction; bf16: two 512-byte blocks, the upper half of the wave the second)
+  const uint8_t* pm[MPW];
+  const uint32_t moff = MT::BLOCK == 1024 ? l16 : (lane & 31) * 16;
+#pragma unroll
+  for (int i = 0; i < MPW; ++i) {
+    const int rb = (wave + NW * i) * (1024 / MT::BLOCK) + (MT::BLOCK == 1024 ? 0 : (lane >> 5));
+    pm[i] = tm + (int64_t)min(r0 / 16 + rb, nrb - 1) * KS4 * MT::BLOCK;
+  }
+  const float* sa = SIDE_X ? sx : sw;  // scale indexed by A row
+  const float* sb = SIDE_X ? sw : sx;  // scale indexed by B row
+
+  // Sources are a uniform base (scalar registers) plus a 32-bit lane offset; the stage's LDS offset is
+  // uniform too.
+  auto issue = [&](int k, uint32_t so) {  // stage k into the slot at LDS offset so
+    SS_LDS uint8_t* base = (SS_LDS uint8_t*)smem + so;
+    const int kb = min(k, KS - 1);  // padding steps re-read the dense operand's last step (the sparse one is zero)
+    const uint8_t* bk = bd + (uint32_t)kb * 128;
+#pragma unroll
+    for (int q = 0; q < PA; ++q) {
+      const uint8_t* ak = pa[q] + (int64_t)k * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)(ak + l16), (SS_LDS void*)(base + (wave + q * NW) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < PB; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(bk + offb[q]),
+                                       (SS_LDS void*)(base + A_BYTES + (wave + q * NW) * 1024), 16, 0, 0);
+  };
+  auto issue_meta = [&](int g) {  // the index words of 4-step group g into the slot
+#pragma unroll
+    for (int i = 0; i < MPW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(pm[i] + (int64_t)g * MT::BLOCK + moff),
+                                       (SS_LDS void*)((SS_LDS uint8_t*)smem + META + (wave + NW * i) * 1024), 16, 0, 0);
+  };
+  auto issue_scales = [&]() {  // the tile's epilogue scales into the slot: A rows at 0, B rows at 1 KB
+    const int i = wave * 64 + lane;
+    // a missing scale vector loads junk from a valid address (never used), so every wave issues NSC loads
+    const float* s1 = sa ? sa + min(r0 + i, R - 1) : reinterpret_cast<const float*>(tm) + lane;
+    const float* s2 = sb ? sb + min(c0 + i, C - 1) : reinterpret_cast<const float*>(tm) + lane;
+    __builtin_amdgcn_global_load_lds((const void*)s1, (SS_LDS void*)((SS_LDS uint8_t*)smem + META + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)s2,
+                                     (SS_LDS void*)((SS_LDS uint8_t*)smem + META + 1024 + wave * 256), 4, 0, 0);
+  };
+
+  Acc acc[TI][TJ];
+#pragma unroll
+  for (int t = 0; t < TI; ++t)
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) acc[t][u] = Acc{0, 0, 0, 0};
+
+  // fragments: A double-buffered (a[2]), B single-buffered (each column refilled right after its use)
+  v4i a0[TI], a1[TI], b[TJ][2];
+  MV mcur[TI];
+  // LDS addresses: one per-lane base per operand (constant across steps) plus the stage's offset, so every
+  // fragment read is that sum plus an immediate (all fragment offsets of a stage are below 48 KB).
+  const uint32_t la = (wm * TI) * 1024 + lane * 16;
+  const uint32_t lb0 = A_BYTES + (wn * TJ * 2 + (r16 >> 3)) * 1024 + (r16 & 7) * 128 + swz(jj, r16) * 16;
+  const uint32_t lb1 = A_BYTES + (wn * TJ * 2 + (r16 >> 3)) * 1024 + (r16 & 7) * 128 + swz(4 + jj, r16) * 16;
+  const uint32_t lm = META + (wm * TI) * MT::BLOCK + lane * (4 * MT::WB);
+  auto lds = [&](uint32_t off) -> const SS_LDS uint8_t* { return (const SS_LDS uint8_t*)smem + off; };
+  // va/vb0/vb1: the three per-lane bases plus a stage offset, computed once per step (kept opaque so the
+  // compiler does not keep one address register per fragment)
+  struct Addr {
+    uint32_t a, b0, b1;
+  };
+  auto addr = [&](uint32_t so) {
+    Addr r{so + la, so + lb0, so + lb1};
+    asm volatile("" : "+v"(r.a), "+v"(r.b0), "+v"(r.b1));
+    return r;
+  };
+  auto read_a = [&](v4i* a, int t, const Addr& ad) { a[t] = *reinterpret_cast<const SS_LDS v4i*>(lds(ad.a) + t * 1024); };
+  auto read_b = [&](int u, const Addr& ad) {
+    b[u][0] = *reinterpret_cast<const SS_LDS v4i*>(lds(ad.b0) + u * 2048);
+    b[u][1] = *reinterpret_cast<const SS_LDS v4i*>(lds(ad.b1) + u * 2048);
+  };
+  auto read_meta = [&](MV* m, int t) { m[t] = *reinterpret_cast<const SS_LDS MV*>(lds(lm) + t * MT::BLOCK); };
+
+  // Step j = 4g + Q: wait for stage j+1, barrier, issue stage j+3 (and the next group's index words, or at
+  // the last group the epilogue scales), then the 64 instructions of step j on (acur, b, mcur) column by
+  // column, each column followed by the reads of stage j+1's B column and one A fragment into anxt; at
+  // Q = 3 the next group's index words replace mcur after the last column.
+  // sl = slot of stage j (= slot of stage j + 3), sl1 = slot of stage j + 1 (LDS offsets)
+  auto step = [&](int j, auto qc, auto lastc, v4i* acur, v4i* anxt, uint32_t sl, uint32_t sl1) {
+    constexpr int Q = decltype(qc)::value;
+    constexpr bool LAST = decltype(lastc)::value;
+    // loads issued after this wave's stage j+1: stage j+2 (if it exists) and the index words or scales
+    // issued at steps j-2 / j-1 after their stage
+    constexpr bool NEXT = !(LAST && Q == 3);                  // stage j+1 exists
+    constexpr bool S2 = !LAST || Q < 2;                        // stage j+2 exists
+    constexpr int N = (S2 ? LPW : 0) + (!LAST ? ((Q == 1 || Q == 2) ? MPW : 0) : (Q == 1 || Q == 2 ? NSC : 0));
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NEXT) {
+      __builtin_amdgcn_s_waitcnt(vm(N));
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads of stage j (and the slot) are done
+      __builtin_amdgcn_s_barrier();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!LAST) {
+      issue(j + 3, sl);
+      if constexpr (Q == 0) issue_meta(j / 4 + 1);
+    } else if constexpr (Q == 0) {
+      issue(j + 3, sl);
+      issue_scales();
+    }
+    const Addr st = addr(sl1);
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) {
+#pragma unroll
+      for (int t = 0; t < TI; ++t)
+        acc[t][u] = tiled::mma_step<AB, Q>(acur[t], b[u][0], b[u][1], acc[t][u], mcur[t]);
+      if constexpr (NEXT) {
+        read_b(u, st);
+        read_a(anxt, u, st);
+      }
+    }
+    if constexpr (Q == 3 && !LAST) {  // after the step's last use of this group's words
+#pragma unroll
+      for (int t = 0; t < TI; ++t) read_meta(mcur, t);
+    }
+    // schedule: per column its 8 instructions, then its 3 fragment reads; stage loads among the columns
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, TI, 0);
+      if (NEXT) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      if ((!LAST || Q == 0) && u < 6) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
+  using NotLast = std::false_type;
+  using Last = std::true_type;
+
+  // prologue: group 0's index words, stages 0..2; wait for stage 0
+  issue_meta(0);
+  issue(0, 0);
+  issue(1, STAGE);
+  issue(2, 2 * STAGE);
+  __builtin_amdgcn_s_waitcnt(vm(2 * LPW));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const Addr st = addr(0);
+#pragma unroll
+    for (int t = 0; t < TI; ++t) read_a(a0, t, st);
+#pragma unroll
+    for (int u = 0; u < TJ; ++u) read_b(u, st);
+#pragma unroll
+    for (int t = 0; t < TI; ++t) read_meta(mcur, t);
+  }
+  // slot offsets of stages j, j+1, j+2 (uniform), rotated every step
+  uint32_t s0 = 0, s1 = STAGE, s2 = 2 * STAGE;
+  auto rot = [&]() {
+    const uint32_t t = s0;
+    s0 = __builtin_amdgcn_readfirstlane(s1);
+    s1 = __builtin_amdgcn_readfirstlane(s2);
+    s2 = __builtin_amdgcn_readfirstlane(t);
+  };
+  for (int g = 0; g + 1 < G; ++g) {
+    const int j = 4 * g;
+    step(j, Q0{}, NotLast{}, a0, a1, s0, s1);
+    rot();
+    step(j + 1, Q1{}, NotLast{}, a1, a0, s0, s1);
+    rot();
+    step(j + 2, Q2{}, NotLast{}, a0, a1, s0, s1);
+    rot();
+    step(j + 3, Q3{}, NotLast{}, a1, a0, s0, s1);
+    rot();
+  }
+  {
+    const int j = KSP - 4;
+    step(j, Q0{}, Last{}, a0, a1, s0, s1);
+    rot();
+    step(j + 1, Q1{}, Last{}, a1, a0, s0, s1);
+    rot();
+    step(j + 2, Q2{}, Last{}, a0, a1, s0, s1);
+    rot();
+    step(j + 3, Q3{}, Last{}, a1, a0, s0, s1);
+  }
+  __builtin_amdgcn_s_waitcnt(vm(0));  // the scales (and no load may outlive the workgroup)
+  __builtin_amdgcn_s_barrier();
+
+  // Epilogue: y = fl32(fl32(float(acc) * sx[m]) * sw[n]); out-of-range results are never stored.
+  const float* scl = reinterpret_cast<const float*>(smem + META);
+  float s_b[TJ];
+#pragma unroll
+  for (int u = 0; u < TJ; ++u) s_b[u] = sb ? scl[256 + (wn * TJ + u) * 16 + r16] : 1.0f;
+  // lane's 4 results of instruction tile (t, u): A rows 16 t + 4 jj + q, B row 16 u + r16 (wave-local)
+  auto result = [&](int t, int u, float* y, int32_t* yi) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (YT == 2) {
+        yi[q] = (int32_t)acc[t][u][q];
+      } else {
+        const float s_a = sa ? scl[(wm * TI + t) * 16 + 4 * jj + q] : 1.0f;
+        float f = (float)acc[t][u][q];
+        // the token scale first, then the channel scale
+        const float s1 = SIDE_X ? s_a : s_b[u], s2 = SIDE_X ? s_b[u] : s_a;
+        if (sx) f = __fmul_rn(f, s1);
+        if (sw) f = __fmul_rn(f, s2);
+        y[q] = f;
+      }
+    }
+  };
+  if constexpr (SIDE_X) {
+#pragma unroll
+    for (int t = 0; t < TI; ++t) {
+      const int ar = r0 + (wm * TI + t) * 16 + 4 * jj;  // 4 consecutive A rows
+#pragma unroll
+      for (int u = 0; u < TJ; ++u) {
+        const int bc = c0 + (wn * TJ + u) * 16 + r16;  // one B row
+        if (bc >= C) continue;
+        float y[4];
+        int32_t yi[4];
+        result(t, u, y, yi);
+        store_out<YT, SIDE_X>(Y, ldy, ar, bc, R, y, yi);
+      }
+    }
+  } else {
+    // Side W writes Y[B row][A row]: each lane holds 4 consecutive A rows of one B row (8 or 16 bytes). The
+    // wave's 128 x 128 results go through its own part of the (now idle) stage ring, rows padded by 16 bytes
+    // so both the writes and the reads are free of bank conflicts, and leave as 16-byte pieces that cover
+    // whole output rows (4-byte results in two passes of 64 rows).
+    constexpr int EB = YT == 0 ? 2 : 4;             // output element bytes
+    constexpr int NP = EB == 2 ? 1 : 2, UP = TJ / NP;  // passes; B fragments per pass
+    constexpr int RP = 16 * UP, STRIDE = 128 * EB + 16, CPR = 128 * EB / 16;  // rows, row bytes, 16-byte chunks
+    static_assert(NW * RP * STRIDE <= META, "staging fits the stage ring");
+    SS_LDS uint8_t* stg = (SS_LDS uint8_t*)smem + wave * RP * STRIDE;
+    const bool vec = ((int64_t)ldy * EB) % 16 == 0;
+    uint8_t* Yb = static_cast<uint8_t*>(Y);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+#pragma unroll
+      for (int uu = 0; uu < UP; ++uu) {
+#pragma unroll
+        for (int t = 0; t < TI; ++t) {
+          float y[4];
+          int32_t yi[4];
+          result(t, p * UP + uu, y, yi);
+          SS_LDS uint8_t* d = stg + (uu * 16 + r16) * STRIDE + (t * 16 + 4 * jj) * EB;
+          if constexpr (YT == 0) {
+            const uint32_t lo = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+            *reinterpret_cast<SS_LDS tiled::v2i*>(d) = tiled::v2i{(int)lo, (int)hi};
+          } else if constexpr (YT == 1) {
+            *reinterpret_cast<SS_LDS v4i*>(d) = v4i{__float_as_int(y[0]), __float_as_int(y[1]), __float_as_int(y[2]),
+                                                    __float_as_int(y[3])};
+          } else {
+            *reinterpret_cast<SS_LDS v4i*>(d) = v4i{yi[0], yi[1], yi[2], yi[3]};
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll 4
+      for (int i = lane; i < RP * CPR; i += 64) {
+        const int row = i / CPR, ch = i % CPR;
+        const v4i v = *reinterpret_cast<const SS_LDS v4i*>(stg + row * STRIDE + ch * 16);
+        const int bc = c0 + (wn * TJ + p * UP) * 16 + row;
+        const int ar = r0 + wm * TI * 16 + ch * (16 / EB);
+        if (bc >= C) continue;
+        uint8_t* dst = Yb + ((int64_t)bc * ldy + ar) * EB;
+        if (vec && ar + 16 / EB <= R) {
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));  // whole rows: no line left to merge in L2
+        } else {
+          const uint32_t w[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+#pragma unroll
+          for (int e = 0; e < 16 / EB; ++e) {
+            if (ar + e >= R) break;
+            if constexpr (EB == 2) reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            else reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+template <int AB, int YT, bool SIDE_X, int GR = 8>
+hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb, const float* sx,
+                  const float* sw, void* Y, int ldy, hipStream_t st) {
+  auto kern = wide_kernel<AB, YT, SIDE_X, GR>;
+  constexpr int lds = lds_bytes<AB>();
+  const hipError_t e = lds_limit((const void*)kern, lds);
+  if (e != hipSuccess) return e;
+  const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
+  hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * NW), lds, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, tr, tc);
+  return hipGetLastError();
+}
+
+}  // namespace wide
+
+hipError_t launch_spgemm_wide(int ab, int yt, int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd,
+                              int ldb, const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
+  if (ab == 0) {
+    if (yt == 0) return wide::launch<0, 0, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 1) return wide::launch<0, 1, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    return wide::launch<0, 2, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  }
+  if (ab == 1) {
+    if (yt == 0) return wide::launch<1, 0, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    return wide::launch<1, 1, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  }
+  if (yt == 0) return wide::launch<2, 0, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  return wide::launch<2, 1, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+}
+
+}  // namespace ss

@@ -102,3 +102,47 @@ def test_pv_with_probabilities_pruned_along_keys(ss, shape):
         vals, meta, _ = oracle.prune24_act(p[h], "bf16")
         exp = oracle.spgemm("X", vals, meta, vt[h], Kc, "bf16", None, None, "bf16")
         assert rel_fro(got[h], bf16_to_f64(exp)) <= 1e-2
+
+
+@pytest.mark.parametrize("shape", [(2, 256, 128), (3, 512, 64), (2, 1000, 128)])
+def test_qk_with_k_pruned_along_head_dim(ss, shape):
+    """S = Q K^T with the keys pruned 2:4 along the head dimension: K is the sparse operand (side W of the
+    batched product, one row per key), Q the dense one."""
+    H, L, d = shape
+    q, k, _, _ = _heads(3 * H + L + d, H, L, d)
+    Kc = ss.lifted_k(d, 2)
+    qd = np.zeros((H, L, Kc), np.uint16)
+    qd[:, :, :d] = q
+    got = []
+    if L % 16 == 0:
+        tv, tm, _ = ss.prune24_act_tiled(dev_bf16(k.reshape(H * L, d)), "bf16")
+        S = ss.spgemm_tiled_batched(ss.SS_SPARSE_W, H, L, L, Kc, tv, tm, dev_bf16(qd), None, None, "f32")
+        got = host(S).astype(np.float64)
+    else:  # keys per head not a multiple of 16: one tiled operand per head
+        for h in range(H):
+            tv, tm, _ = ss.prune24_act_tiled(dev_bf16(k[h]), "bf16")
+            got.append(host(ss.spgemm_tiled(ss.SS_SPARSE_W, L, L, Kc, tv, tm, dev_bf16(qd[h]), None, None, "f32")))
+        got = np.stack(got).astype(np.float64)
+    for h in range(H):
+        vals, meta, _ = oracle.prune24_act(k[h], "bf16")
+        exp = oracle.spgemm_acc("W", vals, meta, qd[h], Kc, "bf16")
+        assert rel_fro(got[h], exp) <= 1e-2
+
+
+@pytest.mark.parametrize("shape", [(2, 256, 128), (3, 512, 64), (2, 768, 128)])
+def test_pv_with_v_pruned_along_keys(ss, shape):
+    """O = P V with V pruned 2:4 along the keys (the reduction): V^T [d, L] is the sparse operand (side W,
+    one row per head dimension), the probabilities P the dense one."""
+    H, L, d = shape
+    _, _, v, p = _heads(5 * L + d, H, L, d)
+    Kc = ss.lifted_k(L, 2)
+    vt = np.ascontiguousarray(v.transpose(0, 2, 1))  # [H, d, L]
+    pd = np.zeros((H, L, Kc), np.uint16)
+    pd[:, :, :L] = p
+    tv, tm, _ = ss.prune24_act_tiled(dev_bf16(vt.reshape(H * d, L)), "bf16")
+    O = ss.spgemm_tiled_batched(ss.SS_SPARSE_W, H, L, d, Kc, tv, tm, dev_bf16(pd), None, None, "bf16")
+    got = bf16_to_f64(host(O))
+    for h in range(H):
+        vals, meta, _ = oracle.prune24_act(vt[h], "bf16")
+        exp = oracle.spgemm("W", vals, meta, pd[h], Kc, "bf16", None, None, "bf16")
+        assert rel_fro(got[h], bf16_to_f64(exp)) <= 1e-2
