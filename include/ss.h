@@ -265,6 +265,27 @@ ss_status ss_spgemm_tiled_ws(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_
                              const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
                              ss_dtype y_dt, void* Y, int64_t ldy, void* workspace, int64_t ws_bytes, void* stream);
 
+/* ss_spgemm_tiled_noalloc -- ss_spgemm_tiled_ws for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the split-K partial tiles go to the
+ * library's own static device array of SS_NOALLOC_SCRATCH_BYTES (8 MiB) on
+ * the current GPU instead of a caller workspace. The array is part of the
+ * library's code object: each GPU the library runs on holds its own copy
+ * until the process ends; its address is looked up (hipGetSymbolAddress) on
+ * the first call on each device and kept. The call allocates nothing (no
+ * hipMalloc / hipFree, no allocating library routine). No part of the array
+ * needs clearing: every split writes its whole partial tile before the
+ * reduction reads it. Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (different streams or threads) race: order them.
+ * A problem whose workspace (ss_spgemm_tiled_workspace_bytes) exceeds the
+ * array returns SS_ERR_UNSUPPORTED with nothing launched (the split-K plan
+ * needs at most 32 KiB per compute unit: 8 MiB on a 256-CU GPU). Arguments,
+ * results (bit for bit) and other errors as ss_spgemm_tiled_ws. */
+#define SS_NOALLOC_SCRATCH_BYTES (8 << 20)
+ss_status ss_spgemm_tiled_noalloc(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
+                                  const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx,
+                                  const float* sw, ss_dtype y_dt, void* Y, int64_t ldy, void* stream);
+
 /* ss_spgemm_tiled_batched -- `batch` independent ss_spgemm_tiled products of
  * one shape in one launch (the prefill kernel; problem b reads tvals + b *
  * tvals_stride and tmeta + b * tmeta_stride (bytes), dense + b * dense_stride,

@@ -21,6 +21,7 @@ Functions keep the names of the C entry points:
     spgemm_tiled(side, M, N, Kc, tvals, tmeta, dense, sx, sw, y_dtype) -> Y [M, N]
         (takes a workspace from torch when ss_spgemm_tiled_workspace_bytes asks for one)
     spgemm_tiled_workspace_bytes(side, M, N, Kc, dtype) -> int
+    spgemm_tiled_noalloc(side, M, N, Kc, tvals, tmeta, dense, sx, sw, y_dtype) -> Y  (static scratch, no workspace)
 """
 from __future__ import annotations
 
@@ -66,6 +67,8 @@ lib.ss_spgemm_tiled_workspace_bytes.argtypes = [_int, _i64, _i64, _i64, _int]
 lib.ss_spgemm_tiled_workspace_bytes.restype = _i64
 lib.ss_spgemm_tiled_ws.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp,
                                    _i64, _vp]
+lib.ss_spgemm_tiled_noalloc.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64,
+                                        _vp]
 lib.ss_prune24_block.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _fp, _vp]
 lib.ss_quant_group_act.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _fp, _vp]
 lib.ss_spgemm_tiled_block.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
@@ -75,7 +78,7 @@ lib.ss_quant_lift_spgemm_decode.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _
                                             _fp, _vp]
 for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm", "ss_pack_sparse",
            "ss_prune24_act_tiled", "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_ws",
-           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode",
+           "ss_spgemm_tiled_noalloc", "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode",
            "ss_spgemm_tiled_batched"):
     getattr(lib, _f).restype = _int
 
@@ -83,7 +86,7 @@ EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_er
            "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm",
            "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_prune24_act_tiled",
            "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_workspace_bytes", "ss_spgemm_tiled_ws",
-           "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode",
+           "ss_spgemm_tiled_noalloc", "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode",
            "ss_spgemm_tiled_batched")
 
 
@@ -250,6 +253,18 @@ def spgemm_tiled(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta:
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.ss_spgemm_tiled_ws(side, M, N, Kc, ab, _ptr(tvals), _ptr(tmeta), _ptr(dense), _ld(dense),
                                   _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _ptr(ws), nbytes, _stream(dense.device)))
+    return Y
+
+
+def spgemm_tiled_noalloc(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta: torch.Tensor,
+                         dense: torch.Tensor, sx=None, sw=None, y_dtype="bf16", out=None):
+    """spgemm_tiled for callers that cannot allocate: a few-token product that splits K keeps its partial
+    tiles in the library's static per-GPU scratch (no workspace argument). Pass ``out`` to allocate nothing
+    at all on the Python side either."""
+    y = dtype_code(y_dtype)
+    Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
+    _check(lib.ss_spgemm_tiled_noalloc(side, M, N, Kc, dtype_code(dense.dtype), _ptr(tvals), _ptr(tmeta), _ptr(dense),
+                                       _ld(dense), _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _stream(dense.device)))
     return Y
 
 

@@ -2,6 +2,8 @@
 // per call on the caller's stream. Nothing is enqueued when validation fails.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
+
+#include <atomic>
 #include <stdio.h>
 #include <string.h>
 
@@ -326,6 +328,47 @@ int64_t ss_spgemm_tiled_workspace_bytes(ss_side side, int64_t M, int64_t N, int6
   const bool sx_side = (side == SS_SPARSE_X);
   const int ab = ab_dt == SS_I8 ? 0 : ab_dt == SS_FP8E4M3 ? 1 : 2;
   return ss::spgemm_tiled_workspace_bytes(sx_side, ab, sx_side ? M : N, sx_side ? N : M, Kc);
+}
+
+// The allocation-free variant's split-K workspace: a static array in the code object (one copy per GPU), and
+// its device address per GPU, looked up once with that GPU current. Host code must use the looked-up
+// address: the array's name on the host is only a stand-in for the symbol.
+static __device__ __align__(256) uint8_t scratch[SS_NOALLOC_SCRATCH_BYTES];
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+ss_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SS_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                                                 kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(SS_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SS_OK;
+}
+}  // namespace
+
+ss_status ss_spgemm_tiled_noalloc(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
+                                  const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx,
+                                  const float* sw, ss_dtype y_dt, void* Y, int64_t ldy, void* stream) {
+  bool run = false;
+  ss_status s = check_spgemm_tiled(side, M, N, Kc, ab_dt, tvals, tmeta, dense, ldd, sx, sw, y_dt, Y, ldy, &run);
+  if (s != SS_OK) return s;
+  if (!run) return ok();
+  const int64_t need = ss_spgemm_tiled_workspace_bytes(side, M, N, Kc, ab_dt);
+  if (need > SS_NOALLOC_SCRATCH_BYTES)
+    return fail(SS_ERR_UNSUPPORTED, "workspace of %lld bytes exceeds the %d-byte static scratch", (long long)need,
+                SS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0 && (s = scratch_ptr(&ws)) != SS_OK) return s;
+  return run_spgemm_tiled(side, M, N, Kc, ab_dt, tvals, tmeta, dense, ldd, sx, sw, y_dt, Y, ldy, ws, stream);
 }
 
 ss_status ss_spgemm_tiled_ws(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
