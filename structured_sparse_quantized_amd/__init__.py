@@ -91,11 +91,54 @@ EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_er
 
 
 class SSError(RuntimeError):
-    def __init__(self, status: int):
+    def __init__(self, status: int, detail: str | None = None):
         self.status = status
         msg = lib.ss_status_string(status).decode()
-        detail = lib.ss_last_error().decode()
+        if detail is None:
+            detail = lib.ss_last_error().decode()
         super().__init__(f"{msg}: {detail}")
+
+
+# Size checks made before a call reaches the C ABI: the library validates sizes, strides and alignment, but
+# it cannot see how large a tensor behind a pointer is. A tensor smaller than the region a call reads or
+# writes raises SSError(SS_ERR_SHAPE), a host tensor SSError(SS_ERR_UNSUPPORTED), before anything launches.
+def _bytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need_bytes(t, nbytes: int, name: str) -> None:
+    if t is None:
+        return
+    if not t.is_contiguous() or _bytes(t) < nbytes:
+        raise SSError(SS_ERR_SHAPE, f"{name}: needs {nbytes} contiguous bytes, has {_bytes(t)}"
+                      f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _need_mat(t, rows: int, cols: int, name: str) -> None:
+    """A row-major matrix of at least rows x cols elements (rows may be padded: a larger leading dimension)."""
+    if t is None:
+        return
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols or (t.shape[0] > 0 and t.stride(1) != 1):
+        raise SSError(SS_ERR_SHAPE, f"{name}: needs a row-major [{rows}, >= {cols}] matrix, has "
+                      f"{list(t.shape)} with strides {list(t.stride())}")
+
+
+def _need_vec(t, n: int, name: str) -> None:
+    if t is None:
+        return
+    if t.numel() < n or (t.dim() == 1 and t.stride(0) != 1):
+        raise SSError(SS_ERR_SHAPE, f"{name}: needs {n} contiguous elements, has {t.numel()}")
+
+
+def _need_dtype(t, dt, name: str) -> None:
+    if t is not None and t.dtype != dt:
+        raise SSError(SS_ERR_DTYPE, f"{name}: needs {dt}, has {t.dtype}")
+
+
+def _on_gpu(*ts) -> None:
+    for t in ts:
+        if t is not None and t.device.type != "cuda":
+            raise SSError(SS_ERR_UNSUPPORTED, f"tensor on {t.device}: the library runs on the GPU only")
 
 
 def _check(status: int) -> None:
@@ -147,12 +190,23 @@ def _alloc_sparse(rows, Kc, out, device):
     return vals, meta, scale
 
 
+def _check_sparse_out(vals, meta, scale, rows, Kc, o):
+    _need_mat(vals, rows, Kc // 2, "vals")
+    _need_mat(meta, rows, Kc // 8, "meta")
+    _need_vec(scale, rows, "scale")
+    _need_dtype(vals, _TORCH[o], "vals")
+    _need_dtype(meta, torch.uint8, "meta")
+    _on_gpu(vals, meta, scale)
+
+
 def prune24(W: torch.Tensor, out_dtype="i8", out=None):
     """Offline 2:4 weight prune + per-channel quantisation + compression."""
     o = dtype_code(out_dtype)
     rows, K = W.shape
     Kc = lifted_k(K, 2)
     vals, meta, scale = out if out is not None else _alloc_sparse(rows, Kc, o, W.device)
+    _check_sparse_out(vals, meta, scale, rows, Kc, o)
+    _on_gpu(W)
     _check(lib.ss_prune24(_ptr(W), dtype_code(W.dtype), rows, K, _ld(W), o, _ptr(vals), _ld(vals), _ptr(meta),
                           _ld(meta), _ptr(scale), _stream(W.device)))
     return vals, meta, scale
@@ -164,6 +218,8 @@ def slide_decompose(W: torch.Tensor, n: int, out_dtype="i8", out=None):
     rows, K = W.shape
     Kc = lifted_k(K, n)
     vals, meta, scale = out if out is not None else _alloc_sparse(rows, Kc, o, W.device)
+    _check_sparse_out(vals, meta, scale, rows, Kc, o)
+    _on_gpu(W)
     _check(lib.ss_slide_decompose(_ptr(W), dtype_code(W.dtype), rows, K, _ld(W), n, o, _ptr(vals), _ld(vals),
                                   _ptr(meta), _ld(meta), _ptr(scale), _stream(W.device)))
     return vals, meta, scale
@@ -179,6 +235,10 @@ def quant_lift_act(X: torch.Tensor, n: int = 2, q_dtype="i8", out=None):
         sx = torch.empty(M, dtype=torch.float32, device=X.device)
     else:
         Xq, sx = out
+        _need_mat(Xq, M, Kc, "Xq")
+        _need_vec(sx, M, "sx")
+        _need_dtype(Xq, _TORCH[q], "Xq")
+    _on_gpu(X, Xq, sx)
     _check(lib.ss_quant_lift_act(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), n, q, _ptr(Xq), _ld(Xq), _ptr(sx),
                                  _stream(X.device)))
     return Xq, sx
@@ -190,6 +250,8 @@ def prune24_act(X: torch.Tensor, out_dtype="bf16", out=None):
     M, K = X.shape
     Kc = lifted_k(K, 2)
     vals, meta, sx = out if out is not None else _alloc_sparse(M, Kc, o, X.device)
+    _check_sparse_out(vals, meta, sx, M, Kc, o)
+    _on_gpu(X)
     _check(lib.ss_prune24_act(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), o, _ptr(vals), _ld(vals), _ptr(meta),
                               _ld(meta), _ptr(sx), _stream(X.device)))
     return vals, meta, sx
@@ -199,6 +261,16 @@ def spgemm(side: int, M: int, N: int, Kc: int, vals: torch.Tensor, meta: torch.T
            sx=None, sw=None, y_dtype="bf16", out=None):
     """Y [M, N] = sparse x dense product with the per-token x per-channel rescale."""
     y = dtype_code(y_dtype)
+    rows, dn = (M, N) if side == SS_SPARSE_X else (N, M)
+    _need_mat(vals, rows, Kc // 2, "vals")
+    _need_mat(meta, rows, Kc // 8, "meta")
+    _need_mat(dense, dn, Kc, "dense")
+    _need_vec(sx, M, "sx")
+    _need_vec(sw, N, "sw")
+    if out is not None:
+        _need_mat(out, M, N, "out")
+    _need_dtype(out, _TORCH[y], "out")
+    _on_gpu(vals, meta, dense, sx, sw, out)
     Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
     _check(lib.ss_spgemm(side, M, N, Kc, dtype_code(vals.dtype), _ptr(vals), _ld(vals), _ptr(meta), _ld(meta),
                          _ptr(dense), _ld(dense), _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _stream(dense.device)))
@@ -222,9 +294,30 @@ def pack_sparse(vals: torch.Tensor, meta: torch.Tensor, out=None):
         tm = torch.empty(nm, dtype=torch.uint8, device=vals.device)
     else:
         tv, tm = out
+        nv, nm = tiled_bytes(rows, Kc, vals.dtype)
+        _need_bytes(tv, nv, "tvals")
+        _need_bytes(tm, nm, "tmeta")
+    _on_gpu(vals, meta, tv, tm)
     _check(lib.ss_pack_sparse(rows, Kc, dtype_code(vals.dtype), _ptr(vals), _ld(vals), _ptr(meta), _ld(meta),
                               _ptr(tv), _ptr(tm), _stream(vals.device)))
     return tv, tm
+
+
+def _check_tiled_product(side, M, N, Kc, ab, tvals, tmeta, dense, sx, sw, out, y, batch=1):
+    rows, dn = (M, N) if side == SS_SPARSE_X else (N, M)  # sparse rows, dense rows
+    nv, nm = tiled_bytes(rows, Kc, ab)
+    _need_bytes(tvals, batch * nv if batch > 1 else nv, "tvals")
+    _need_bytes(tmeta, batch * nm if batch > 1 else nm, "tmeta")
+    if batch == 1:
+        _need_mat(dense, dn, Kc, "dense")
+        _need_vec(sx, M, "sx")
+        _need_vec(sw, N, "sw")
+        if out is not None:
+            _need_mat(out, M, N, "out")
+    _need_dtype(out, _TORCH[y], "out")
+    _need_dtype(sx, torch.float32, "sx")
+    _need_dtype(sw, torch.float32, "sw")
+    _on_gpu(tvals, tmeta, dense, sx, sw, out)
 
 
 def spgemm_tiled_workspace_bytes(side: int, M: int, N: int, Kc: int, dtype="i8") -> int:
@@ -239,6 +332,7 @@ def spgemm_tiled(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta:
     torch's allocator when the library asks for it (pass workspace=False to run without)."""
     y = dtype_code(y_dtype)
     ab = dtype_code(dense.dtype)
+    _check_tiled_product(side, M, N, Kc, ab, tvals, tmeta, dense, sx, sw, out, y)
     Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
     if workspace is False:
         _check(lib.ss_spgemm_tiled(side, M, N, Kc, ab, _ptr(tvals), _ptr(tmeta), _ptr(dense), _ld(dense), _ptr(sx),
@@ -250,6 +344,8 @@ def spgemm_tiled(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta:
             ws = torch.empty(max(need, 0), dtype=torch.uint8, device=dense.device) if need > 0 else None
         else:
             ws = workspace
+            _need_bytes(ws, int(lib.ss_spgemm_tiled_workspace_bytes(side, M, N, Kc, ab)), "workspace")
+            _on_gpu(ws)
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.ss_spgemm_tiled_ws(side, M, N, Kc, ab, _ptr(tvals), _ptr(tmeta), _ptr(dense), _ld(dense),
                                   _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _ptr(ws), nbytes, _stream(dense.device)))
@@ -262,6 +358,7 @@ def spgemm_tiled_noalloc(side: int, M: int, N: int, Kc: int, tvals: torch.Tensor
     tiles in the library's static per-GPU scratch (no workspace argument). Pass ``out`` to allocate nothing
     at all on the Python side either."""
     y = dtype_code(y_dtype)
+    _check_tiled_product(side, M, N, Kc, dtype_code(dense.dtype), tvals, tmeta, dense, sx, sw, out, y)
     Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
     _check(lib.ss_spgemm_tiled_noalloc(side, M, N, Kc, dtype_code(dense.dtype), _ptr(tvals), _ptr(tmeta), _ptr(dense),
                                        _ld(dense), _ptr(sx), _ptr(sw), y, _ptr(Y), _ld(Y), _stream(dense.device)))
@@ -281,7 +378,19 @@ def spgemm_tiled_batched(side: int, batch: int, M: int, N: int, Kc: int, tvals: 
     if strides is None:
         nv, nm = tiled_bytes(rows, Kc, ab)
         strides = (nv, nm)
-    assert dense.dim() == 3 and dense.stride(2) == 1 and Y.dim() == 3 and Y.stride(2) == 1
+    nv, nm = tiled_bytes(rows, Kc, ab)
+    dn = N if side == SS_SPARSE_X else M
+    _need_bytes(tvals, (batch - 1) * strides[0] + nv, "tvals")
+    _need_bytes(tmeta, (batch - 1) * strides[1] + nm, "tmeta")
+    if dense.dim() != 3 or dense.shape[0] < batch or dense.shape[1] < dn or dense.shape[2] < Kc or dense.stride(2) != 1:
+        raise SSError(SS_ERR_SHAPE, f"dense: needs [{batch}, {dn}, >= {Kc}] with unit stride, has {list(dense.shape)}")
+    if Y.dim() != 3 or Y.shape[0] < batch or Y.shape[1] < M or Y.shape[2] < N or Y.stride(2) != 1:
+        raise SSError(SS_ERR_SHAPE, f"out: needs [{batch}, {M}, {N}] with unit stride, has {list(Y.shape)}")
+    for t, n, name in ((sx, M, "sx"), (sw, N, "sw")):  # [batch, n] per problem, or [n] shared by all
+        if t is not None and not ((t.dim() == 2 and t.shape[0] >= batch and t.shape[1] >= n and t.stride(1) == 1)
+                                  or (t.dim() == 1 and t.numel() >= n and t.stride(0) == 1)):
+            raise SSError(SS_ERR_SHAPE, f"{name}: needs [{batch}, >= {n}] or [>= {n}], has {list(t.shape)}")
+    _on_gpu(tvals, tmeta, dense, sx, sw, Y)
     def _s(t):
         return 0 if t is None else (t.stride(0) if t.dim() == 2 else 0)
     _check(lib.ss_spgemm_tiled_batched(side, batch, M, N, Kc, ab, _ptr(tvals), strides[0], _ptr(tmeta), strides[1],
@@ -295,6 +404,17 @@ def quant_lift_spgemm_decode(X: torch.Tensor, n: int, tvals: torch.Tensor, tmeta
     """Few tokens (1..4): quant+lift and the weight-sparse product in one launch; Y [M, N]."""
     M, K = X.shape
     y = dtype_code(y_dtype)
+    q = dtype_code(q_dtype)
+    Kc = lifted_k(K, n) if n >= 2 else 0
+    nv, nm = tiled_bytes(N, Kc, q) if Kc > 0 else (0, 0)
+    _need_bytes(tvals, nv, "tvals")
+    _need_bytes(tmeta, nm, "tmeta")
+    _need_vec(sw, N, "sw")
+    _need_vec(sx_out, M, "sx_out")
+    if out is not None:
+        _need_mat(out, M, N, "out")
+    _need_dtype(out, _TORCH[y], "out")
+    _on_gpu(X, tvals, tmeta, sw, out, sx_out)
     Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=X.device)
     _check(lib.ss_quant_lift_spgemm_decode(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), n, dtype_code(q_dtype),
                                            _ptr(tvals), _ptr(tmeta), _ptr(sw), N, y, _ptr(Y), _ld(Y), _ptr(sx_out),
@@ -314,6 +434,11 @@ def prune24_act_tiled(X: torch.Tensor, out_dtype="fp8", out=None):
         sx = None if o == SS_BF16 else torch.empty(M, dtype=torch.float32, device=X.device)
     else:
         tv, tm, sx = out
+        nv, nm = tiled_bytes(M, Kc, o)
+        _need_bytes(tv, nv, "tvals")
+        _need_bytes(tm, nm, "tmeta")
+        _need_vec(sx, M, "sx")
+    _on_gpu(X, tv, tm, sx)
     _check(lib.ss_prune24_act_tiled(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), o, _ptr(tv), _ptr(tm), _ptr(sx),
                                     _stream(X.device)))
     return tv, tm, sx
@@ -331,6 +456,11 @@ def slide_decompose_tiled(W: torch.Tensor, n: int, out_dtype="i8", out=None):
         scale = None if o == SS_BF16 else torch.empty(rows, dtype=torch.float32, device=W.device)
     else:
         tv, tm, scale = out
+        nv, nm = tiled_bytes(rows, Kc, o)
+        _need_bytes(tv, nv, "tvals")
+        _need_bytes(tm, nm, "tmeta")
+        _need_vec(scale, rows, "scale")
+    _on_gpu(W, tv, tm, scale)
     _check(lib.ss_slide_decompose_tiled(_ptr(W), dtype_code(W.dtype), rows, K, _ld(W), n, o, _ptr(tv), _ptr(tm),
                                         _ptr(scale), _stream(W.device)))
     return tv, tm, scale
@@ -353,6 +483,11 @@ def prune24_block(W: torch.Tensor, out=None):
         sw = torch.empty(((rows + BLOCK - 1) // BLOCK, Kc // BLOCK), dtype=torch.float32, device=W.device)
     else:
         tv, tm, sw = out
+        nv, nm = tiled_bytes(rows, Kc, SS_FP8E4M3)
+        _need_bytes(tv, nv, "tvals")
+        _need_bytes(tm, nm, "tmeta")
+        _need_mat(sw, (rows + BLOCK - 1) // BLOCK, Kc // BLOCK, "sw")
+    _on_gpu(W, tv, tm, sw)
     _check(lib.ss_prune24_block(_ptr(W), dtype_code(W.dtype), rows, K, _ld(W), _ptr(tv), _ptr(tm), _ptr(sw),
                                 _stream(W.device)))
     return tv, tm, sw
@@ -368,6 +503,9 @@ def quant_group_act(X: torch.Tensor, out=None):
         sx = torch.empty((M, Kc // BLOCK), dtype=torch.float32, device=X.device)
     else:
         Xq, sx = out
+        _need_mat(Xq, M, Kc, "Xq")
+        _need_mat(sx, M, Kc // BLOCK, "sx")
+    _on_gpu(X, Xq, sx)
     _check(lib.ss_quant_group_act(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), _ptr(Xq), _ld(Xq), _ptr(sx),
                                   _stream(X.device)))
     return Xq, sx
@@ -377,6 +515,15 @@ def spgemm_tiled_block(M: int, N: int, Kc: int, tvals: torch.Tensor, tmeta: torc
                        sx: torch.Tensor, sw: torch.Tensor, y_dtype="bf16", out=None):
     """Y [M, N]: the weight-sparse block-scaled FP8 product."""
     y = dtype_code(y_dtype)
+    nv, nm = tiled_bytes(N, Kc, SS_FP8E4M3)
+    _need_bytes(tvals, nv, "tvals")
+    _need_bytes(tmeta, nm, "tmeta")
+    _need_mat(dense, M, Kc, "dense")
+    _need_mat(sx, M, Kc // BLOCK, "sx")
+    _need_mat(sw, (N + BLOCK - 1) // BLOCK, Kc // BLOCK, "sw")
+    if out is not None:
+        _need_mat(out, M, N, "out")
+    _on_gpu(tvals, tmeta, dense, sx, sw, out)
     Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=dense.device)
     _check(lib.ss_spgemm_tiled_block(M, N, Kc, _ptr(tvals), _ptr(tmeta), _ptr(dense), _ld(dense), _ptr(sx), _ptr(sw),
                                      y, _ptr(Y), _ld(Y), _stream(dense.device)))

@@ -5,9 +5,10 @@
 //
 // Persistent workgroups walk rows r, r + grid, ...; the next row is loaded
 // into registers before the current one is reduced and written, so HBM reads
-// and writes overlap. For n > 2 the codes of a row are staged in LDS and
-// gathered into 16-byte output chunks (the blog's output-oriented iteration:
-// one output window per index, base 2n*group + 2*offset).
+// and writes overlap. For n > 2 the codes of a row are staged in LDS (zero past
+// K) and each thread forms whole periods of the lift's byte pattern
+// (LiftPeriod): the period's source words read once, its 16-byte output chunks
+// built with constant shifts.
 #include "ss_device.h"
 #include "ss_kernels.h"
 
@@ -131,24 +132,23 @@ __global__ __launch_bounds__(kBlock, (PIPE || VPT > 4) ? 2 : (VPT > 2 ? 4 : 8)) 
         }
       }
       if (tail0 + tid < K) lds[tail0 + tid] = (uint8_t)code(ctail);
-      for (int c = K + tid; c < Kpad + 4; c += kBlock) lds[c] = 0;
+      // zero past K through the last period's source bytes: windows past the last group read zeros, so
+      // the output from the logical K' to Kc is zero
+      using LP = LiftPeriod<N>;
+      const int nchunk = Kc / 16, nper = (nchunk + LP::PC - 1) / LP::PC;
+      for (int c = K + tid; c < nper * LP::SB; c += kBlock) lds[c] = 0;
       lds_barrier();
       const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds);
-      for (int c = tid; c < Kc / 16; c += kBlock) {
-        uint32_t w4[4];
+      for (int p = tid; p < nper; p += kBlock) {
+        uint32_t s[LP::SW], o[4 * LP::PC];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = c * 4 + q;  // flat window index
-          if (4 * t < kl) {
-            const int g = t / (N - 1), w = t - g * (N - 1);
-            const int base = 2 * N * g + 2 * w;  // even
-            const uint32_t lo = l32[base >> 2], hi = l32[(base >> 2) + 1];
-            w4[q] = (base & 2) ? ((lo >> 16) | (hi << 16)) : lo;
-          } else {
-            w4[q] = 0;
-          }
-        }
-        *reinterpret_cast<uint4*>(qr + c * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        for (int i = 0; i < LP::SW; ++i) s[i] = l32[p * LP::SW + i];
+        LP::emit(s, o);
+#pragma unroll
+        for (int h = 0; h < LP::PC; ++h)
+          if (p * LP::PC + h < nchunk)
+            *reinterpret_cast<uint4*>(qr + (p * LP::PC + h) * 16) = make_uint4(o[4 * h], o[4 * h + 1], o[4 * h + 2],
+                                                                               o[4 * h + 3]);
       }
       lds_barrier();  // the LDS row is rewritten for the next row
     }
@@ -179,17 +179,12 @@ __global__ __launch_bounds__(kBlock) void quant_lift_long_kernel(const TIn* __re
   const bool zero_row = (amax == 0.0f);
   const float inv = zero_row ? 0.0f : Qz::Q / amax;
   if (threadIdx.x == 0) sx[row] = zero_row ? 0.0f : amax / Qz::Q;
-  const int64_t Kpad = (K + 2 * n - 1) / (2 * n) * (2 * n);
-  const int64_t kl = Kpad / (2 * n) * 4 * (n - 1);
+  // output position kp = 4(n-1) g + 4 w + j takes the code of X[2n g + 2w + j] (zero past K)
+  const int64_t gb = 4 * (n - 1);  // output bytes per group
   for (int64_t kp = threadIdx.x; kp < Kc; kp += kBlock) {
-    uint8_t q = 0;
-    if (kp < kl) {
-      const int64_t t = kp >> 2, j = kp & 3;
-      const int64_t g = t / (n - 1), w = t - g * (n - 1);
-      const int64_t src = 2 * n * g + 2 * w + j;
-      if (src < K && !zero_row) q = Qz::code(V::scalar(xr + src), inv);
-    }
-    qr[kp] = q;
+    const int64_t g = kp / gb, rem = kp - g * gb;
+    const int64_t src = 2 * n * g + 2 * (rem >> 2) + (rem & 3);
+    qr[kp] = (src < K && !zero_row) ? Qz::code(V::scalar(xr + src), inv) : 0;
   }
 }
 
@@ -201,7 +196,9 @@ hipError_t launch_n(const TIn* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq
   const int64_t kpad = (K + 2 * N - 1) / (2 * N) * (2 * N);
   // codes staged in LDS for the gather, except without a lift and for 6:8 from bf16 with whole 8-groups
   const bool reg_lift = N == 4 && E == 8 && K % 8 == 0;
-  const size_t lds = (N == 2 || reg_lift) ? 0 : (size_t)((kpad + 4 + 15) / 16 * 16);
+  using LP = LiftPeriod<N < 3 ? 3 : N>;
+  const int64_t nper = (Kc / 16 + LP::PC - 1) / LP::PC;  // periods of the lift pattern covering the row
+  const size_t lds = (N == 2 || reg_lift) ? 0 : (size_t)((std::max<int64_t>(nper * LP::SB, kpad) + 15) / 16 * 16);
   const bool fits = K < (1 << 30) && Kc < (1 << 30) && M < (1 << 30) && lds <= 64 * 1024 && vpt <= 12;
   if (!fits) {
     hipLaunchKernelGGL((quant_lift_long_kernel<TIn, FP8>), dim3((unsigned)M), dim3(kBlock), 0, st, X, ldx, K, N, Xq, ldq, Kc, sx);

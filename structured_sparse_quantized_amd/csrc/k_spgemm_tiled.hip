@@ -598,7 +598,31 @@ constexpr int FMAXM = 4;  // tokens
 // plus the word the last window's read reaches into, rounded to 16
 __host__ __device__ inline int fused_stage_bytes(int64_t K, int n) {
   const int64_t kpad = (K + 2 * n - 1) / (2 * n) * (2 * n);
-  return (int)((kpad + 4 + 15) / 16 * 16);
+  if (n < 3) return (int)((kpad + 15) / 16 * 16);
+  // the lift reads whole periods of its pattern: zeros past K through the last period's source bytes
+  const int64_t nchunk = (kpad / (2 * n) * (n - 1) + 3) / 4, pc = lift_period_chunks(n);
+  const int64_t need = (nchunk + pc - 1) / pc * lift_period_bytes(n);
+  return (int)(((need > kpad ? need : kpad) + 15) / 16 * 16);
+}
+// The lifted row from a staged row of plain codes (zero past K through the last period's source bytes):
+// nwin 4-byte windows, written as whole periods of 16-byte chunks.
+template <int N>
+__device__ __forceinline__ void lift_row(const uint8_t* st, uint8_t* row, int nwin, int tid) {
+  using LP = LiftPeriod<N>;
+  const int nchunk = (nwin + 3) / 4, nper = (nchunk + LP::PC - 1) / LP::PC;
+  const uint32_t* s32 = reinterpret_cast<const uint32_t*>(st);
+  for (int p = tid; p < nper; p += 64 * NW) {
+    uint32_t s[LP::SW], o[4 * LP::PC];
+#pragma unroll
+    for (int i = 0; i < LP::SW; ++i) s[i] = s32[p * LP::SW + i];
+    LP::emit(s, o);
+#pragma unroll
+    for (int h = 0; h < LP::PC; ++h) {
+      const int c = p * LP::PC + h;
+      if (c < nchunk)
+        *reinterpret_cast<uint4*>(row + 16 * c) = make_uint4(o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]);
+    }
+  }
 }
 // 16-byte vectors of a token row held per thread: K <= 20480 (bf16) / 16384 (f32)
 template <typename TIn> constexpr int fmaxv() { return sizeof(TIn) == 2 ? 5 : 8; }
@@ -707,14 +731,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fused_decode_kernel(int R, int M, 
     }
     if (gather) {
       __syncthreads();  // the staged codes are complete (the next token's first barrier guards their reuse)
-      // output-oriented iteration (SlideSparse blog section 3.2): window t = (n-1) g + w reads the 4 codes
-      // at 2n g + 2w, an even offset, from the two words around it
-      const uint32_t* s32 = reinterpret_cast<const uint32_t*>(st);
-      uint32_t* o32 = reinterpret_cast<uint32_t*>(row);
-      for (int t = tid; t < nwin; t += 64 * NW) {
-        const int g = t / (n - 1), w = t - g * (n - 1), base = 2 * n * g + 2 * w;
-        const uint32_t lo = s32[base >> 2], hi = s32[(base >> 2) + 1];
-        o32[t] = (base & 2) ? ((lo >> 16) | (hi << 16)) : lo;
+      // whole periods of the lift pattern per thread (LiftPeriod), written into the token's LDS row
+      switch (n) {
+        case 3: lift_row<3>(st, row, nwin, tid); break;
+        case 5: lift_row<5>(st, row, nwin, tid); break;
+        case 4: lift_row<4>(st, row, nwin, tid); break;
+        case 6: lift_row<6>(st, row, nwin, tid); break;
+        case 7: lift_row<7>(st, row, nwin, tid); break;
+        default: lift_row<8>(st, row, nwin, tid); break;
       }
     }
   }

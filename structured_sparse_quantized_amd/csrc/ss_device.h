@@ -75,6 +75,35 @@ __device__ __forceinline__ uint32_t top2_nibble(uint32_t k0, uint32_t k1, uint32
   return i0 | (i1 << 2);
 }
 
+// ---- activation lift by periods ---------------------------------------------------
+// The lift writes window w of 2n-group g as four codes, X'[4(n-1)g + 4w + j] = X[2n g + 2w + j] (SlideSparse
+// article, activation lifting; SlideSparse blog, section 3.2). Its byte pattern is periodic: PC output chunks
+// of 16 bytes (4 windows each) hold whole groups and come from SB consecutive source bytes (SB a multiple of
+// 4, so a period starts on a word). A thread that owns a period reads its SW source words once and forms the
+// 4 PC output words with shifts whose amounts are compile-time constants.
+// chunks per period for pattern n (n >= 3): the fewest whole groups that fill whole chunks from whole words
+__host__ __device__ constexpr int lift_period_chunks(int n) {
+  int p = 1;
+  while ((4 * p) % (n - 1) != 0 || (2 * n * (4 * p / (n - 1))) % 4 != 0) ++p;
+  return p;
+}
+__host__ __device__ constexpr int lift_period_bytes(int n) { return 2 * n * (4 * lift_period_chunks(n) / (n - 1)); }
+template <int N> struct LiftPeriod {
+  static constexpr int WPG = N - 1;                 // windows per group
+  static constexpr int PC = lift_period_chunks(N);  // output chunks per period
+  static constexpr int SB = lift_period_bytes(N);   // source bytes per period
+  static constexpr int SW = SB / 4;                // source words per period
+  // first source byte of output word u of the period: window u lies in group u / WPG at position u % WPG
+  static constexpr int src(int u) { return 2 * N * (u / WPG) + 2 * (u % WPG); }
+  __device__ __forceinline__ static void emit(const uint32_t* s, uint32_t* out) {
+#pragma unroll
+    for (int u = 0; u < 4 * PC; ++u) {
+      const int b = src(u);  // even: a window starts on a byte pair
+      out[u] = (b & 2) ? ((s[b >> 2] >> 16) | (s[(b >> 2) + 1] << 16)) : s[b >> 2];
+    }
+  }
+};
+
 // ---- tiled-layout row order ---------------------------------------------------
 // Workgroups are dealt to the 8 XCDs round-robin by index. Kernels that write
 // one row of the tiled operand per workgroup (or per persistent iteration i)

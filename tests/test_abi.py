@@ -237,3 +237,56 @@ def test_batched_validation_statuses():
     assert b(ys=4) == ss.SS_ERR_ALIGN and b(tvs=-16) == ss.SS_ERR_SHAPE
     assert b(Kc=100) == ss.SS_ERR_SHAPE and b(ab=ss.SS_F32) == ss.SS_ERR_DTYPE and b(sx=None) == ss.SS_ERR_NULL
     assert b(batch=0) == ss.SS_OK and b(M=0) == ss.SS_OK
+
+
+def test_binding_checks_tensor_sizes_before_the_call():
+    """The C ABI sees pointers only; the binding compares every tensor with the region the call would touch
+    and raises before anything is launched: too small -> SS_ERR_SHAPE, wrong dtype -> SS_ERR_DTYPE, a host
+    tensor of the right size -> SS_ERR_UNSUPPORTED (the library runs on the GPU only)."""
+    import torch
+    import structured_sparse_quantized_amd as ss
+    M, N, Kc = 20, 48, 512
+    nv, nm = ss.tiled_bytes(N, Kc, "i8")
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)  # noqa: E731
+    good = dict(tvals=u8(nv), tmeta=u8(nm), dense=torch.zeros((M, Kc), dtype=torch.int8),
+                sx=torch.ones(M), sw=torch.ones(N), out=torch.zeros((M, N), dtype=torch.bfloat16))
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, a["tvals"], a["tmeta"], a["dense"], a["sx"], a["sw"], "bf16",
+                               out=a["out"], workspace=False)
+
+    def status(fn):
+        with pytest.raises(ss.SSError) as e:
+            fn()
+        return e.value.status
+
+    assert status(lambda: call(tvals=u8(nv - 1))) == ss.SS_ERR_SHAPE
+    assert status(lambda: call(tmeta=u8(nm - 16))) == ss.SS_ERR_SHAPE
+    assert status(lambda: call(dense=torch.zeros((M - 1, Kc), dtype=torch.int8))) == ss.SS_ERR_SHAPE
+    assert status(lambda: call(dense=torch.zeros((M, Kc - 16), dtype=torch.int8))) == ss.SS_ERR_SHAPE
+    assert status(lambda: call(sx=torch.ones(M - 1))) == ss.SS_ERR_SHAPE
+    assert status(lambda: call(sw=torch.ones(N - 1))) == ss.SS_ERR_SHAPE
+    assert status(lambda: call(out=torch.zeros((M, N - 1), dtype=torch.bfloat16))) == ss.SS_ERR_SHAPE
+    assert status(lambda: call(out=torch.zeros((M, N), dtype=torch.float32))) == ss.SS_ERR_DTYPE
+    assert status(lambda: call(sx=torch.ones(M, dtype=torch.float64))) == ss.SS_ERR_DTYPE
+    assert status(lambda: call()) == ss.SS_ERR_UNSUPPORTED  # right sizes, host memory
+    # the other entry points that take caller buffers
+    X = torch.zeros((M, 100), dtype=torch.bfloat16)
+    Kq = ss.lifted_k(100, 4)
+    assert status(lambda: ss.quant_lift_act(X, 4, "i8", out=(torch.zeros((M, Kq - 16), dtype=torch.int8),
+                                                                torch.ones(M)))) == ss.SS_ERR_SHAPE
+    assert status(lambda: ss.quant_lift_act(X, 4, "i8", out=(torch.zeros((M, Kq), dtype=torch.int8),
+                                                                torch.ones(M - 1)))) == ss.SS_ERR_SHAPE
+    W = torch.zeros((N, 256))
+    assert status(lambda: ss.slide_decompose_tiled(W, 2, "i8", out=(u8(nv // 2), u8(nm // 2), torch.ones(N)))) == \
+        ss.SS_ERR_SHAPE
+    assert status(lambda: ss.prune24(W, "i8", out=(torch.zeros((N, 100), dtype=torch.int8),
+                                                   torch.zeros((N, 32), dtype=torch.uint8), torch.ones(N)))) == \
+        ss.SS_ERR_SHAPE
+    Xd = torch.zeros((4, 3584), dtype=torch.bfloat16)
+    assert status(lambda: ss.quant_lift_spgemm_decode(Xd, 3, u8(16), u8(16), torch.ones(N), N)) == ss.SS_ERR_SHAPE
+    B = 2
+    assert status(lambda: ss.spgemm_tiled_batched(ss.SS_SPARSE_W, B, M, N, Kc, u8(nv), u8(2 * nm),
+                                                  torch.zeros((B, M, Kc), dtype=torch.int8), None, None,
+                                                  "i32")) == ss.SS_ERR_SHAPE
