@@ -655,6 +655,37 @@ def suite(ss, torch, dev, gen, detail):
         torch.cuda.empty_cache()
     detail["block_fp8"] = blk
 
+    # quant+product A/B: the per-token quantisation inside the product's prologue (ss_quant_spgemm_prefill, one
+    # absmax pass + the product coding bf16 rows into its LDS stages + scales) against ss_quant_lift_act +
+    # ss_spgemm_tiled, Llama-shaped 2:4 FP8 layers
+    fused = []
+    for M in (4096, 16384):
+        tot_f, tot_2 = 0.0, 0.0
+        for name, (K, Nout) in synth.LLAMA31_8B_LINEARS.items():
+            W = randn((Nout, K), 0.02)
+            tv, tm, sw = ss.slide_decompose_tiled(W, 2, "fp8")
+            del W
+            X = randn((M, K), 1.0, torch.bfloat16)
+            xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
+            sx = torch.empty(M, dtype=torch.float32, device=dev)
+            sxf = torch.empty(M, dtype=torch.float32, device=dev)
+            Y = torch.empty((M, Nout), dtype=torch.bfloat16, device=dev)
+            t_f = median_us(torch, [lambda: ss.quant_spgemm_prefill(X, tv, tm, sw, Nout, "fp8", "bf16", out=Y, sx_out=sxf)])
+
+            def two():
+                ss.quant_lift_act(X, 2, "fp8", out=(xq, sx))
+                ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, K, tv, tm, xq, sx, sw, "bf16", out=Y, workspace=False)
+            t_2 = median_us(torch, [two])
+            tot_f += t_f
+            tot_2 += t_2
+            fused.append(row("quant_in_product", layer=name, M=M, K=K, N=Nout, fused_us=t_f, two_calls_us=t_2,
+                             fused_vs_two_calls=t_2 / t_f))
+            del tv, tm, sw, X, xq, sx, sxf, Y
+        fused.append(row("quant_in_product_layer", M=M, fused_us=tot_f, two_calls_us=tot_2,
+                         fused_vs_two_calls=tot_2 / tot_f))
+        torch.cuda.empty_cache()
+    detail["quant_in_product"] = fused
+
     # online 2:4 on the attention operand roles (bf16), 32 heads x 4096 tokens x 128, one batched launch
     H, L, d = 32, 4096, 128
     Kq = ss.lifted_k(d, 2)
@@ -670,7 +701,14 @@ def suite(ss, torch, dev, gen, detail):
                                                              "bf16", out=S)])
     Qh, Kt = Q.view(H, L, d), Kp[:, :, :d].transpose(1, 2).contiguous()
     t_qk_dn = median_us(torch, [lambda: torch.bmm(Qh, Kt)])
-    del Q, Kp, tvq, tmq, Qh, Kt, S
+    # K pruned along the head dimension: the keys are the sparse operand (side W), Q the dense one
+    Qp = torch.zeros((H, L, Kq), dtype=torch.bfloat16, device=dev)
+    Qp[:, :, :d] = Q.view(H, L, d)
+    Kr = Kp[:, :, :d].reshape(H * L, d).contiguous()
+    t_pk = median_us(torch, [lambda: ss.prune24_act_tiled(Kr, "bf16", out=(tvq, tmq, None))])
+    t_qk2 = median_us(torch, [lambda: ss.spgemm_tiled_batched(ss.SS_SPARSE_W, H, L, L, Kq, tvq, tmq, Qp, None, None,
+                                                              "bf16", out=S)])
+    del Q, Kp, tvq, tmq, Qh, Kt, S, Qp, Kr
     P = torch.softmax(randn((H * L, L), 2.0), dim=1).to(torch.bfloat16)
     Vt = randn((H, d, L), 1.0, torch.bfloat16)
     nv, nm = ss.tiled_bytes(H * L, L, "bf16")
@@ -682,10 +720,23 @@ def suite(ss, torch, dev, gen, detail):
                                                              "bf16", out=O)])
     Ph, V = P.view(H, L, L), Vt.transpose(1, 2).contiguous()
     t_pv_dn = median_us(torch, [lambda: torch.bmm(Ph, V)])
+    # V pruned along the keys: V^T [d, L] per head is the sparse operand (side W), P the dense one
+    nv, nm = ss.tiled_bytes(H * d, L, "bf16")
+    tvv = torch.empty(nv, dtype=torch.uint8, device=dev)
+    tmv = torch.empty(nm, dtype=torch.uint8, device=dev)
+    Vt2 = Vt.reshape(H * d, L)
+    t_pvv = median_us(torch, [lambda: ss.prune24_act_tiled(Vt2, "bf16", out=(tvv, tmv, None))])
+    P3 = P.view(H, L, L)
+    t_pv2 = median_us(torch, [lambda: ss.spgemm_tiled_batched(ss.SS_SPARSE_W, H, L, d, L, tvv, tmv, P3, None, None,
+                                                              "bf16", out=O)])
+    del tvv, tmv
     detail["attention_roles_bf16"] = row(
         "attention_roles_bf16", heads=H, tokens=L, head_dim=d,
         qk={"prune_q_us": t_pq, "sparse_batched_us": t_qk, "dense_bmm_us": t_qk_dn,
             "vs_dense": t_qk_dn / (t_pq + t_qk)},
+        qk_k_pruned={"prune_k_us": t_pk, "sparse_batched_us": t_qk2, "vs_dense": t_qk_dn / (t_pk + t_qk2)},
+        pv_v_pruned={"prune_v_us": t_pvv, "sparse_batched_us": t_pv2, "vs_dense": t_pv_dn / (t_pvv + t_pv2),
+                     "product_vs_dense": t_pv_dn / t_pv2},
         pv={"prune_p_us": t_pp, "sparse_batched_us": t_pv, "dense_bmm_us": t_pv_dn,
             "gemm_frac": 2.0 * H * L * L * d / 2 / t_pv / 1e6 / DENSE_PEAK_T["bf16"],
             "vs_dense": t_pv_dn / (t_pp + t_pv), "product_vs_dense": t_pv_dn / t_pv})

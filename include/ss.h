@@ -286,6 +286,22 @@ ss_status ss_spgemm_tiled_noalloc(ss_side side, int64_t M, int64_t N, int64_t Kc
                                   const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx,
                                   const float* sw, ss_dtype y_dt, void* Y, int64_t ldy, void* stream);
 
+/* ss_quant_spgemm_prefill -- a prefill layer with the per-token quantisation
+ * inside the sparse product (the SlideSparse blog, section 3.2, fuses the
+ * activation lift into the per-token quantisation kernel; here both move into
+ * the product's prologue, so the coded activations never go through HBM):
+ * Y [M, N] = X W'^T with X [M, K] bf16 (ldx elements, rows 16-byte aligned),
+ * K % 128 == 0 (SS_ERR_SHAPE otherwise), q_dt I8 or FP8E4M3, the 2:4 weights
+ * as ss_slide_decompose_tiled(W, 2, q_dt) writes them (tvals, tmeta, sw [N]),
+ * y_dt BF16 or F32. sx [M] (float) receives the per-token scales. Three
+ * launches: per-token absmax into sx, the product (which codes X with
+ * fl32(Q / absmax) into its LDS stages), then sx = absmax / Q. Codes, scales
+ * and outputs equal ss_quant_lift_act(X, n = 2) followed by
+ * ss_spgemm_tiled bit for bit. No scratch memory. */
+ss_status ss_quant_spgemm_prefill(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, ss_dtype q_dt,
+                                  const void* tvals, const uint8_t* tmeta, const float* sw, int64_t N, ss_dtype y_dt,
+                                  void* Y, int64_t ldy, float* sx, void* stream);
+
 /* ss_spgemm_tiled_batched -- `batch` independent ss_spgemm_tiled products of
  * one shape in one launch (the prefill kernel; problem b reads tvals + b *
  * tvals_stride and tmeta + b * tmeta_stride (bytes), dense + b * dense_stride,

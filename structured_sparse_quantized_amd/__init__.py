@@ -69,6 +69,8 @@ lib.ss_spgemm_tiled_ws.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, 
                                    _i64, _vp]
 lib.ss_spgemm_tiled_noalloc.argtypes = [_int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64,
                                         _vp]
+lib.ss_quant_spgemm_prefill.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _fp, _i64, _int, _vp, _i64, _fp,
+                                        _vp]
 lib.ss_prune24_block.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _fp, _vp]
 lib.ss_quant_group_act.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _i64, _fp, _vp]
 lib.ss_spgemm_tiled_block.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _fp, _fp, _int, _vp, _i64, _vp]
@@ -78,16 +80,16 @@ lib.ss_quant_lift_spgemm_decode.argtypes = [_vp, _int, _i64, _i64, _i64, _int, _
                                             _fp, _vp]
 for _f in ("ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm", "ss_pack_sparse",
            "ss_prune24_act_tiled", "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_ws",
-           "ss_spgemm_tiled_noalloc", "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode",
-           "ss_spgemm_tiled_batched"):
+           "ss_spgemm_tiled_noalloc", "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block",
+           "ss_quant_lift_spgemm_decode", "ss_spgemm_tiled_batched", "ss_quant_spgemm_prefill"):
     getattr(lib, _f).restype = _int
 
 EXPORTS = ("ss_lifted_k", "ss_lifted_k_logical", "ss_status_string", "ss_last_error", "ss_version",
            "ss_prune24", "ss_slide_decompose", "ss_quant_lift_act", "ss_prune24_act", "ss_spgemm",
            "ss_tiled_vals_bytes", "ss_tiled_meta_bytes", "ss_pack_sparse", "ss_prune24_act_tiled",
            "ss_slide_decompose_tiled", "ss_spgemm_tiled", "ss_spgemm_tiled_workspace_bytes", "ss_spgemm_tiled_ws",
-           "ss_spgemm_tiled_noalloc", "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block", "ss_quant_lift_spgemm_decode",
-           "ss_spgemm_tiled_batched")
+           "ss_spgemm_tiled_noalloc", "ss_prune24_block", "ss_quant_group_act", "ss_spgemm_tiled_block",
+           "ss_quant_lift_spgemm_decode", "ss_spgemm_tiled_batched", "ss_quant_spgemm_prefill")
 
 
 class SSError(RuntimeError):
@@ -397,6 +399,29 @@ def spgemm_tiled_batched(side: int, batch: int, M: int, N: int, Kc: int, tvals: 
                                        _ptr(dense), dense.stride(1), dense.stride(0), _ptr(sx), _s(sx), _ptr(sw),
                                        _s(sw), y, _ptr(Y), Y.stride(1), Y.stride(0), _stream(dense.device)))
     return Y
+
+
+def quant_spgemm_prefill(X: torch.Tensor, tvals: torch.Tensor, tmeta: torch.Tensor, sw: torch.Tensor, N: int,
+                         q_dtype="fp8", y_dtype="bf16", out=None, sx_out=None):
+    """Prefill layer with the per-token quantisation inside the product (2:4 weights, K % 128 == 0): returns
+    (Y [M, N], sx [M]); equal bit for bit to quant_lift_act(X, 2, q) followed by spgemm_tiled."""
+    M, K = X.shape
+    y, q = dtype_code(y_dtype), dtype_code(q_dtype)
+    Kc = lifted_k(K, 2)
+    nv, nm = tiled_bytes(N, Kc, q)
+    _need_bytes(tvals, nv, "tvals")
+    _need_bytes(tmeta, nm, "tmeta")
+    _need_vec(sw, N, "sw")
+    _need_vec(sx_out, M, "sx_out")
+    if out is not None:
+        _need_mat(out, M, N, "out")
+    _need_dtype(out, _TORCH[y], "out")
+    _on_gpu(X, tvals, tmeta, sw, out, sx_out)
+    Y = out if out is not None else torch.empty((M, N), dtype=_TORCH[y], device=X.device)
+    sx = sx_out if sx_out is not None else torch.empty(M, dtype=torch.float32, device=X.device)
+    _check(lib.ss_quant_spgemm_prefill(_ptr(X), dtype_code(X.dtype), M, K, _ld(X), q, _ptr(tvals), _ptr(tmeta),
+                                       _ptr(sw), N, y, _ptr(Y), _ld(Y), _ptr(sx), _stream(X.device)))
+    return Y, sx
 
 
 def quant_lift_spgemm_decode(X: torch.Tensor, n: int, tvals: torch.Tensor, tmeta: torch.Tensor, sw: torch.Tensor,

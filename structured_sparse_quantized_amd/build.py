@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libss.so")
 SOURCES = ["ss_api.hip", "k_quant_lift.hip", "k_prune.hip", "k_slide.hip", "k_spgemm.hip", "k_spgemm_tiled.hip",
-           "k_spgemm_wide.hip"]
+           "k_spgemm_wide.hip", "k_quant_spgemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -371,6 +371,31 @@ ss_status ss_spgemm_tiled_noalloc(ss_side side, int64_t M, int64_t N, int64_t Kc
   return run_spgemm_tiled(side, M, N, Kc, ab_dt, tvals, tmeta, dense, ldd, sx, sw, y_dt, Y, ldy, ws, stream);
 }
 
+ss_status ss_quant_spgemm_prefill(const void* X, ss_dtype x_dt, int64_t M, int64_t K, int64_t ldx, ss_dtype q_dt,
+                                  const void* tvals, const uint8_t* tmeta, const float* sw, int64_t N, ss_dtype y_dt,
+                                  void* Y, int64_t ldy, float* sx, void* stream) {
+  if (x_dt != SS_BF16) return fail(SS_ERR_DTYPE, "X must be BF16");
+  if (q_dt != SS_I8 && q_dt != SS_FP8E4M3) return fail(SS_ERR_DTYPE, "codes must be I8 or FP8E4M3");
+  if (y_dt != SS_BF16 && y_dt != SS_F32) return fail(SS_ERR_DTYPE, "output must be BF16 or F32");
+  if (M < 0 || N < 0 || K < 0) return fail(SS_ERR_SHAPE, "negative size");
+  if (K % 128 != 0) return fail(SS_ERR_SHAPE, "K=%lld is not a multiple of 128", (long long)K);
+  if (M == 0 || N == 0) return ok();
+  if (K == 0) return fail(SS_ERR_SHAPE, "K must be positive");
+  if (M > 0x7FFFFFF0LL || N > 0x7FFFFFF0LL || K > 0x7FFFFF00LL || ldy > 0x7FFFFFFFLL || ldx > 0x7FFFFFFFLL)
+    return fail(SS_ERR_SHAPE, "too large");
+  ss_status s;
+  if ((s = check_mat("X", X, M, K, ldx, 2)) != SS_OK) return s;
+  // (output rows need no 16-byte alignment: the stores fall back to single elements)
+  if ((s = check_mat("Y", Y, 1, N, ldy, esize(y_dt))) != SS_OK) return s;
+  if (!tvals || !tmeta || !sw || !sx) return fail(SS_ERR_NULL, "tvals, tmeta, sw and sx are required");
+  if (!aligned16(tvals) || !aligned16(tmeta)) return fail(SS_ERR_ALIGN, "tiled operand is not 16-byte aligned");
+  return hip_status(ss::launch_quant_spgemm_prefill(q_dt == SS_I8 ? 0 : 1, y_dt == SS_BF16 ? 0 : 1,
+                                                    static_cast<const uint16_t*>(X), ldx, M, K,
+                                                    static_cast<const uint8_t*>(tvals), tmeta, sw, N, Y, ldy, sx,
+                                                    (hipStream_t)stream),
+                    "ss_quant_spgemm_prefill launch");
+}
+
 ss_status ss_spgemm_tiled_ws(ss_side side, int64_t M, int64_t N, int64_t Kc, ss_dtype ab_dt, const void* tvals,
                              const uint8_t* tmeta, const void* dense, int64_t ldd, const float* sx, const float* sw,
                              ss_dtype y_dt, void* Y, int64_t ldy, void* workspace, int64_t ws_bytes, void* stream) {

@@ -67,6 +67,13 @@ hipError_t launch_quant_lift_spgemm(bool x_bf16, int ab, int yt, const void* X, 
                                     int64_t N, int64_t Kc, const uint8_t* tv, const uint8_t* tm, const float* sw,
                                     void* Y, int64_t ldy, float* sx_out, hipStream_t st);
 
+// Prefill with the per-token quantisation inside the product (2:4 weights, K % 128 == 0, bf16 X): absmax
+// into sx, the product coding X into its LDS stages, then sx = a / Q. ab: 0 = int8, 1 = fp8; yt: 0 = bf16,
+// 1 = f32.
+hipError_t launch_quant_spgemm_prefill(int ab, int yt, const uint16_t* X, int64_t ldx, int64_t M, int64_t K,
+                                       const uint8_t* tv, const uint8_t* tm, const float* sw, int64_t N, void* Y,
+                                       int64_t ldy, float* sx, hipStream_t st);
+
 // Block-scaled FP8 (128 x 128 weight blocks, per-token groups of 128; 2:4 weights, K' = K = Kc):
 // weight prep into the tiled operand with scales [ceil(rows / 128)][Kc / 128], activation codes [M][Kc] with
 // scales [M][Kc / 128], and the weight-sparse product (yt: 0 = bf16, 1 = f32).
