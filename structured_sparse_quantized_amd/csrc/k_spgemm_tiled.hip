@@ -1068,13 +1068,14 @@ static bool few_tokens(bool side_x, int64_t R, int64_t C) {
   const int64_t tiles = ((R + tiled::BM - 1) / tiled::BM) * ((C + tiled::BN - 1) / tiled::BN);
   return !side_x && C <= 64 && (C <= 8 || tiles < 128);
 }
-// The wide-tile prefill kernel (k_spgemm_wide.hip) on the weight-sparse side: large problems only, where
-// its 256 x 256 tiles still give every CU four or more tiles and the sparse operand is tall (N >= 16384) or
-// the reduction long (K' >= 8192 positions of 8-bit codes). Measured 1.1-1.25x the 256 x 128 kernel on
-// Llama-shaped gate_up (4096 and 16384 tokens) and down (16384 tokens); slower on the smaller layers.
+// The wide-tile prefill kernel (k_spgemm_wide.hip) on the weight-sparse side, wherever its 256 x 256 tiles
+// still give every CU four or more: measured 1.07-1.3x the 256 x 128 kernel on the Llama-shaped layers at
+// 16384 tokens (qkv, o, gate_up, down) and on gate_up at 4096 tokens; with fewer tiles per CU the 256 x 128
+// kernel's finer grid wins.
 static bool use_wide(bool side_x, int64_t R, int64_t C, int64_t KS) {
+  (void)KS;
   const int64_t tiles = ((R + 255) / 256) * ((C + 255) / 256);
-  return !side_x && tiles >= 4 * (int64_t)num_cus_p() && (R >= 16384 || KS >= 64);
+  return !side_x && tiles >= 4 * (int64_t)num_cus_p();
 }
 // The split-K path (with a workspace) serves the few-token products with more than 16 tokens.
 static bool use_splitk(bool side_x, int64_t R, int64_t C) { return few_tokens(side_x, R, C) && C > 16; }
