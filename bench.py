@@ -272,6 +272,57 @@ def time_steps(torch, layer_calls, steps, warmup, mark=None):
     return ms, mk
 
 
+def read_sclk_mhz():
+    """Current engine clock from the amdgpu sysfs DPM table (the level marked '*'), or None."""
+    import glob
+    import re
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path).read().splitlines():
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    if m:
+                        return int(m.group(1))
+        except OSError:
+            continue
+    return None
+
+
+def sample_sclk(fns, torch, seconds=0.3, period=0.002):
+    """Run the callables ``fns`` round robin, back to back, for ``seconds`` while a thread samples the engine
+    clock; the median, range and sample count of the DPM level (None where the table is not readable)."""
+    import threading
+    if read_sclk_mhz() is None:
+        return {"error": "no readable pp_dpm_sclk"}
+    samples, stop = [], threading.Event()
+
+    def run():
+        while not stop.is_set():
+            v = read_sclk_mhz()
+            if v is not None:
+                samples.append(v)
+            time.sleep(period)
+
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=run)
+    th.start()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fns[i % len(fns)]()
+            i += 1
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return {"error": "no samples"}
+    return {"samples": len(samples), "median": statistics.median(samples), "min": min(samples),
+            "max": max(samples), "idle_after": read_sclk_mhz()}
+
+
 def per_call(torch, layer_calls):
     """Median per-call us of every call of the step, each over the rotating buffer sets."""
     names = [n for n, _ in layer_calls[0]]
@@ -334,6 +385,9 @@ def main(argv=None):
         calls[name] = {"quant_us": tq, "quant_GBs": qb / tq / 1e3, "quant_frac": qb / tq / 1e3 / HBM_PEAK_GBS,
                        "gemm_us": tg, "gemm_TFLOPs": ops / tg / 1e6, "gemm_frac": ops / tg / 1e6 / DENSE_PEAK_T["fp8"]}
     detail["headline_per_call"] = row("headline_per_call", tokens=M, rotating_sets=NBUF, calls=calls)
+    # engine clock while the dominant product runs back to back
+    sclk = sample_sclk([dict(c)["gemm_gate_up"] for c in steps_calls], torch)
+    detail["sclk_gate_up"] = row("sclk_gate_up", **sclk)
     # dense FP8 comparator on the same buffers
     dense_calls = [lay.dense_calls(b) for b in range(NBUF)]
     try:
@@ -363,6 +417,7 @@ def main(argv=None):
         "vs_dense": None if ms_dense is None else ms_dense / ms_step,
         "gemm_frac": {k: round(v["gemm_frac"], 3) for k, v in calls.items()},
         "quant_GBs": round(calls["qkv"]["quant_GBs"], 1),
+        "sclk_MHz_gate_up": sclk.get("median"),
         "weight_prep_us": round(sum(v["us"] for v in prep.values()), 1),
     })
     del lay, steps_calls, dense_calls
