@@ -117,7 +117,7 @@ def test_one_launch_decode_many_row_blocks(ss, n, M):
 
 @pytest.mark.parametrize("q", ["i8", "fp8", "bf16"])
 def test_wide_kernel_ragged(ss, q):
-    """A product large enough for the 256 x 256 kernel (N >= 16384 with >= 4 tiles per CU) with ragged
+    """A product large enough for the 256 x 256 kernel (four or more 256 x 256 tiles per CU) with ragged
     tiles on both sides and a reduction that ends inside a 4-step index group: N = 16484 channels, 4000
     tokens, K = 1280 (INT8 / FP8: 10 steps of 128; bf16: 20 steps of 64)."""
     import torch
