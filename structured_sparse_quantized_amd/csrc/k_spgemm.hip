@@ -198,9 +198,8 @@ __global__ __launch_bounds__(256, 2) void spgemm_kernel(int64_t R, int64_t C, in
         // Y[bc][ar .. ar+3]: 4 consecutive outputs of one token row
         if (yvec && ar + 3 < R) {
           if constexpr (YT == 0) {
-            const uint32_t lo = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + bc * ldy + ar) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + bc * ldy + ar) =
+                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
           } else if constexpr (YT == 1) {
             *reinterpret_cast<float4*>(static_cast<float*>(Y) + bc * ldy + ar) = make_float4(y[0], y[1], y[2], y[3]);
           } else {
@@ -390,12 +389,9 @@ __global__ __launch_bounds__(64 * NW, 1) void spgemm8_kernel(int R, int C, int K
         if constexpr (YT == 2) {
           yi[q] = (int32_t)acc[i][u][q];
         } else {
-          float f = (float)acc[i][u][q];
-          // the token scale is applied first, then the channel scale
+          // the token scale is applied first, then the channel scale (an absent scale is 1: exact)
           const float s1 = SIDE_X ? s_a[i][q] : s_b[u], s2 = SIDE_X ? s_b[u] : s_a[i][q];
-          if (sx) f = __fmul_rn(f, s1);
-          if (sw) f = __fmul_rn(f, s2);
-          y[q] = f;
+          y[q] = __fmul_rn(__fmul_rn((float)acc[i][u][q], s1), s2);
         }
       }
       store_out<YT, SIDE_X>(Y, ldy, ar, bc, R, y, yi);

@@ -415,15 +415,21 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // no load may outlive the workgroup
 
   // Epilogue: y = fl32(fl32(float(acc) * sx[m]) * sw[n]), the scales from LDS (staged in the prologue;
-  // out-of-range results are never stored).
+  // out-of-range results are never stored). An absent scale vector reads as 1, and a multiply by 1 is exact,
+  // so every result takes the same two multiplies with no branch per value.
   float s_a[TI][4], s_b[TJ];
   const float* scl = reinterpret_cast<const float*>(smem + LDS);
+  const bool has_a = sa != nullptr && !BS, has_b = sb != nullptr && !BS;
 #pragma unroll
-  for (int t = 0; t < TI; ++t)
+  for (int t = 0; t < TI; ++t) {
+    const float4 v = *reinterpret_cast<const float4*>(scl + (wm * TI + t) * 16 + 4 * jj);
+    s_a[t][0] = has_a ? v.x : 1.0f;
+    s_a[t][1] = has_a ? v.y : 1.0f;
+    s_a[t][2] = has_a ? v.z : 1.0f;
+    s_a[t][3] = has_a ? v.w : 1.0f;
+  }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_a[t][q] = (sa && !BS) ? scl[(wm * TI + t) * 16 + 4 * jj + q] : 1.0f;
-#pragma unroll
-  for (int u = 0; u < TJ; ++u) s_b[u] = (sb && !BS) ? scl[BM + (wn * TJ + u) * 16 + r16] : 1.0f;
+  for (int u = 0; u < TJ; ++u) s_b[u] = has_b ? scl[BM + (wn * TJ + u) * 16 + r16] : 1.0f;
 #pragma unroll
   for (int t = 0; t < TI; ++t) {
 #pragma unroll
@@ -440,12 +446,9 @@ __device__ __forceinline__ void spgemm_body(int R, int C, int KS, const uint8_t*
         } else if constexpr (YT == 2) {
           yi[q] = (int32_t)acc[t][u][q];
         } else {
-          float f = (float)acc[t][u][q];
           // the token scale first, then the channel scale
           const float s1 = SIDE_X ? s_a[t][q] : s_b[u], s2 = SIDE_X ? s_b[u] : s_a[t][q];
-          if (sx) f = __fmul_rn(f, s1);
-          if (sw) f = __fmul_rn(f, s2);
-          y[q] = f;
+          y[q] = __fmul_rn(__fmul_rn((float)acc[t][u][q], s1), s2);
         }
       }
       store_out<YT, SIDE_X>(Y, ldy, ar, bc, R, y, yi);

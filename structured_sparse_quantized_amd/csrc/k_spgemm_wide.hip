@@ -322,10 +322,22 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
     const int lane = etid & 63, wave = __builtin_amdgcn_readfirstlane(etid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
     const int r16 = lane & 15, jj = lane >> 4;
+    // This lane's scales, read once: A rows (wm TI + t) 16 + 4 jj + q and B row (wn TJ + u) 16 + r16. An absent
+    // scale vector reads as 1 (its slot holds junk, never used), and a multiply by 1 is exact, so every result
+    // takes the same two multiplies with no branch per value.
     const float* scl = reinterpret_cast<const float*>(smem + META);
-    float s_b[TJ];
+    const bool has_a = sa != nullptr, has_b = sb != nullptr;
+    float s_a[TI][4], s_b[TJ];
   #pragma unroll
-    for (int u = 0; u < TJ; ++u) s_b[u] = sb ? scl[256 + (wn * TJ + u) * 16 + r16] : 1.0f;
+    for (int t = 0; t < TI; ++t) {
+      const float4 v = *reinterpret_cast<const float4*>(scl + (wm * TI + t) * 16 + 4 * jj);
+      s_a[t][0] = has_a ? v.x : 1.0f;
+      s_a[t][1] = has_a ? v.y : 1.0f;
+      s_a[t][2] = has_a ? v.z : 1.0f;
+      s_a[t][3] = has_a ? v.w : 1.0f;
+    }
+  #pragma unroll
+    for (int u = 0; u < TJ; ++u) s_b[u] = has_b ? scl[256 + (wn * TJ + u) * 16 + r16] : 1.0f;
     // lane's 4 results of instruction tile (t, u): A rows 16 t + 4 jj + q, B row 16 u + r16 (wave-local)
     auto result = [&](int t, int u, float* y, int32_t* yi) {
   #pragma unroll
@@ -333,13 +345,9 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
         if constexpr (YT == 2) {
           yi[q] = (int32_t)acc[t][u][q];
         } else {
-          const float s_a = sa ? scl[(wm * TI + t) * 16 + 4 * jj + q] : 1.0f;
-          float f = (float)acc[t][u][q];
           // the token scale first, then the channel scale
-          const float s1 = SIDE_X ? s_a : s_b[u], s2 = SIDE_X ? s_b[u] : s_a;
-          if (sx) f = __fmul_rn(f, s1);
-          if (sw) f = __fmul_rn(f, s2);
-          y[q] = f;
+          const float s1 = SIDE_X ? s_a[t][q] : s_b[u], s2 = SIDE_X ? s_b[u] : s_a[t][q];
+          y[q] = __fmul_rn(__fmul_rn((float)acc[t][u][q], s1), s2);
         }
       }
     };
@@ -380,9 +388,7 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
             result(t, p * UP + uu, y, yi);
             SS_LDS uint8_t* d = stg + (uu * 16 + r16) * STRIDE + (t * 16 + 4 * jj) * EB;
             if constexpr (YT == 0) {
-              const uint32_t lo = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-              const uint32_t hi = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
-              *reinterpret_cast<SS_LDS tiled::v2i*>(d) = tiled::v2i{(int)lo, (int)hi};
+              *reinterpret_cast<SS_LDS tiled::v2i*>(d) = tiled::v2i{(int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
             } else if constexpr (YT == 1) {
               *reinterpret_cast<SS_LDS v4i*>(d) = v4i{__float_as_int(y[0]), __float_as_int(y[1]), __float_as_int(y[2]),
                                                       __float_as_int(y[3])};

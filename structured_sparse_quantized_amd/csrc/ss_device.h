@@ -18,6 +18,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two float32 -> two bfloat16 in one word (lo in the low half) by gfx950's packed conversion instruction:
+// nearest with ties to even, equal to f32_to_bf16 on every non-NaN input (denormals included); a NaN leaves
+// as a quiet NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
 // Magnitude key: for finite floats the unsigned order of the bits without the
 // sign is the order of |v|, and +0 / -0 share key 0.
 __device__ __forceinline__ uint32_t mag_key_f32(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }

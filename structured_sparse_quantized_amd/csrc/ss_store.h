@@ -10,9 +10,8 @@ __device__ __forceinline__ void store_out(void* Y, int64_t ldy, int64_t ar, int6
                                           const int32_t* yi) {
   if (!SIDE_X && (ldy & 3) == 0 && ar + 3 < R) {  // Y[bc][ar .. ar+3] is one aligned vector
     if constexpr (YT == 0) {
-      const uint32_t lo = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + bc * ldy + ar) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + bc * ldy + ar) =
+          make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
     } else if constexpr (YT == 1) {
       *reinterpret_cast<float4*>(static_cast<float*>(Y) + bc * ldy + ar) = make_float4(y[0], y[1], y[2], y[3]);
     } else {
