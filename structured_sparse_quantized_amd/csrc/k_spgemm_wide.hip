@@ -15,7 +15,7 @@
 // per step; the 256 accumulator registers per lane sit in the accumulation registers, and the A and B
 // fragments are double-buffered in ordinary registers (the fragments of step j+1 are read from LDS while
 // the instructions of step j run), column by column of B.
-// LDS: a ring of three stages (48 KB each) filled by LDS DMA (global_load_lds, 1 KB per wave instruction;
+// LDS: a ring of three stages (48 KB each) filled by LDS DMA (buffer loads into LDS, 1 KB per wave instruction;
 // B rows swizzled so fragment reads are conflict-free), and one 16 KB slot holding the index words of the
 // current 4-step group (the tiled layout's metadata block of each of the 16 row blocks, brought in by DMA
 // one group ahead and read into registers after the last instruction of the group before). The slot takes the
@@ -58,6 +58,11 @@ static_assert((BM + BN) * 4 <= 8 * 1024, "the epilogue scales fit the index-word
 
 constexpr int vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }  // s_waitcnt vmcnt(n)
 
+// raw buffer resource over [p, p + bytes): base and size in scalar registers, 32-bit untyped data
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
 template <int AB, int YT, bool SIDE_X, int GR>
 __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, const uint8_t* __restrict__ tv,
                                                           const uint8_t* __restrict__ tm,
@@ -85,11 +90,17 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
 
   // Per-lane DMA sources. Rows past the end are clamped to the last row (block); their results are never
   // stored. Sparse rows past R inside the last row block are zero in the tiled layout.
-  // (uniform bases in scalar registers, one 32-bit lane offset)
+  // The loads are buffer loads: a resource (base and size) in scalar registers, a 32-bit lane offset that stays
+  // constant through the loop and a uniform offset that carries the step, so no vector instruction computes
+  // an address (the 64-bit address arithmetic of global loads cost 2-6%). The launcher keeps every operand
+  // below 2 GB.
   const uint32_t l16 = lane * 16;
-  const uint8_t* pa[PA];
+  const uint32_t nA = (uint32_t)nrb * (uint32_t)KSP * 1024u, nB = (uint32_t)C * (uint32_t)ldb,
+                 nM = (uint32_t)nrb * (uint32_t)KS4 * (uint32_t)MT::BLOCK;
+  uint32_t sA[PA];  // uniform: byte offset of A row block q of this wave
 #pragma unroll
-  for (int q = 0; q < PA; ++q) pa[q] = tv + (int64_t)min(r0 / 16 + wave + q * NW, nrb - 1) * KSP * 1024;
+  for (int q = 0; q < PA; ++q)
+    sA[q] = __builtin_amdgcn_readfirstlane((uint32_t)min(r0 / 16 + wave + q * NW, nrb - 1) * (uint32_t)KSP * 1024u);
   uint32_t offb[PB];
 #pragma unroll
   for (int q = 0; q < PB; ++q) {
@@ -99,12 +110,15 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
   // index-word DMA: instruction i of this wave brings bytes 1024 (wave + NW i) + 16 lane of the slot, i.e.
   // row block rb of the tile at offset off of its group block
   // (8-bit: one row block per instruction; bf16: two 512-byte blocks, the upper half of the wave the second)
-  const uint8_t* pm[MPW];
+  constexpr uint32_t MBLK = MT::BLOCK;
+  uint32_t om[4];  // MPW of them (a length that depends on a template parameter in these calls drops the
+                   // kernel's host launch stub without a diagnostic)
+  static_assert(MPW <= 4, "index-word loads per wave");
   const uint32_t moff = MT::BLOCK == 1024 ? l16 : (lane & 31) * 16;
 #pragma unroll
   for (int i = 0; i < MPW; ++i) {
     const int rb = (wave + NW * i) * (1024 / MT::BLOCK) + (MT::BLOCK == 1024 ? 0 : (lane >> 5));
-    pm[i] = tm + (int64_t)min(r0 / 16 + rb, nrb - 1) * KS4 * MT::BLOCK;
+    om[i] = (uint32_t)min(r0 / 16 + rb, nrb - 1) * (uint32_t)KS4 * (uint32_t)MT::BLOCK + moff;
   }
   const float* sa = SIDE_X ? sx : sw;  // scale indexed by A row
   const float* sb = SIDE_X ? sw : sx;  // scale indexed by B row
@@ -113,23 +127,21 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
   // uniform too.
   auto issue = [&](int k, uint32_t so) {  // stage k into the slot at LDS offset so
     SS_LDS uint8_t* base = (SS_LDS uint8_t*)smem + so;
-    const int kb = min(k, KS - 1);  // padding steps re-read the dense operand's last step (the sparse one is zero)
-    const uint8_t* bk = bd + (uint32_t)kb * 128;
+    const uint32_t kb = (uint32_t)min(k, KS - 1) * 128u;  // padding steps re-read the dense operand's last step
 #pragma unroll
-    for (int q = 0; q < PA; ++q) {
-      const uint8_t* ak = pa[q] + (int64_t)k * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)(ak + l16), (SS_LDS void*)(base + (wave + q * NW) * 1024), 16, 0, 0);
-    }
+    for (int q = 0; q < PA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(tv, nA), (SS_LDS void*)(base + (wave + q * NW) * 1024), 16, l16,
+                                               sA[q] + (uint32_t)k * 1024u, 0, 0);
 #pragma unroll
     for (int q = 0; q < PB; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(bk + offb[q]),
-                                       (SS_LDS void*)(base + A_BYTES + (wave + q * NW) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(bd, nB), (SS_LDS void*)(base + A_BYTES + (wave + q * NW) * 1024), 16,
+                                               offb[q], kb, 0, 0);
   };
   auto issue_meta = [&](int g) {  // the index words of 4-step group g into the slot
 #pragma unroll
     for (int i = 0; i < MPW; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(pm[i] + (int64_t)g * MT::BLOCK + moff),
-                                       (SS_LDS void*)((SS_LDS uint8_t*)smem + META + (wave + NW * i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(tm, nM), (SS_LDS void*)((SS_LDS uint8_t*)smem + META + (wave + NW * i) * 1024),
+                                               16, om[i], g * MBLK, 0, 0);
   };
 
   // single loads, so a step can spread them among its instructions: load i of stage k (i < PA: an A row
@@ -137,18 +149,17 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
   auto issue_one = [&](int i, int k, uint32_t so) {
     SS_LDS uint8_t* base = (SS_LDS uint8_t*)smem + so;
     if (i < PA) {
-      __builtin_amdgcn_global_load_lds((const void*)(pa[i] + (int64_t)k * 1024 + l16),
-                                       (SS_LDS void*)(base + (wave + i * NW) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(tv, nA), (SS_LDS void*)(base + (wave + i * NW) * 1024), 16, l16,
+                                               sA[i] + (uint32_t)k * 1024u, 0, 0);
     } else {
       const int q = i - PA;
-      const uint8_t* bk = bd + (uint32_t)min(k, KS - 1) * 128;
-      __builtin_amdgcn_global_load_lds((const void*)(bk + offb[q]),
-                                       (SS_LDS void*)(base + A_BYTES + (wave + q * NW) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(bd, nB), (SS_LDS void*)(base + A_BYTES + (wave + q * NW) * 1024), 16,
+                                               offb[q], (uint32_t)min(k, KS - 1) * 128u, 0, 0);
     }
   };
   auto meta_one = [&](int i, int g) {
-    __builtin_amdgcn_global_load_lds((const void*)(pm[i] + (int64_t)g * MT::BLOCK + moff),
-                                     (SS_LDS void*)((SS_LDS uint8_t*)smem + META + (wave + NW * i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(tm, nM), (SS_LDS void*)((SS_LDS uint8_t*)smem + META + (wave + NW * i) * 1024),
+                                             16, om[i], g * MBLK, 0, 0);
   };
   auto scale_one = [&](int i) {
     // a missing scale vector loads junk from a valid address (never used), so the count stays fixed
