@@ -86,6 +86,17 @@ def _round(x):
     return float(x)
 
 
+def _sig6(o):
+    """The final line's numbers to 6 significant digits (it stays one short line)."""
+    if isinstance(o, float):
+        return float(f"{o:.6g}")
+    if isinstance(o, dict):
+        return {k: _sig6(v) for k, v in o.items()}
+    if isinstance(o, (list, tuple)):
+        return [_sig6(v) for v in o]
+    return o
+
+
 def traffic_record(kernel):
     """HBM bytes per launch measured with rocprofv3 counters, if they were taken
     on the current source of the kernel (else None)."""
@@ -442,7 +453,7 @@ def main(argv=None):
             pass
     if args.calib_copy:
         calib_copy(torch, dev)
-    print(json.dumps(out, default=_round, separators=(",", ":")))
+    print(json.dumps(_sig6(out), default=_round, separators=(",", ":")))
 
 
 def calib_copy(torch, dev):
@@ -550,10 +561,9 @@ def cpu_leg(torch, lay, M, n_tok, n_ch, seed=7):
               "sample": f"{len(toks)} tokens x >= {n_ch} channels per linear, set 0 of the timed steps"}
     cpu = {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
            "cpu": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
-           "sample": f"{len(toks)} tokens through the four linears: per-token FP8 quant of all K and the product "
-                     f"over >= {n_ch} of each linear's channels, scaled to all channels; float64 BLAS "
-                     f"({threads} threads), element-wise steps single-threaded NumPy; weight prep "
-                     f"({prep_s:.1f} s, offline) not counted"}
+           "sample": f"{len(toks)} tokens, four linears: FP8 quant of all K, product over >= {n_ch} channels "
+                     f"of each (scaled to all); float64 BLAS on {threads} threads; weight prep ({prep_s:.1f} s) "
+                     f"not counted"}
     log(f"[bench] CPU oracle: {cpu['value']:.1f} tokens/s; parity {parity}")
     return parity, cpu
 

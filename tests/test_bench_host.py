@@ -59,38 +59,39 @@ def test_rotation_covers_twice_the_infinity_cache():
 
 def test_last_line_is_compact():
     """The driver keeps a bounded tail of stdout: the final JSON line must stay well under 2,000 characters with
-    every field filled (a synthetic line of the same shape as main() prints)."""
+    every field filled (a synthetic line of the same shape and precision as main() prints, rounded the same
+    way to 6 significant digits)."""
     b = _bench()
     out = {
-        "metric": b.METRIC, "value": 1.2345678e6, "unit": "tokens/s", "n_gpus": 1, "steps": 20, "warmup": 5,
-        "ms_per_step": 12.345678, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "metric": b.METRIC, "value": 8024332.757171267, "unit": "tokens/s", "n_gpus": 1, "steps": 20, "warmup": 5,
+        "ms_per_step": 2.041789703369141, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
         "data": "synthetic",
         "config": {"workload": "Llama-3.1-8B-shaped layer linears qkv+o+gate_up+down, 2:4 FP8-e4m3 W per-channel, "
                                "dynamic per-token FP8 X, bf16 out, 16384 tokens (online quant + sparse GEMM)",
                    "tokens": 16384, "global_batch": 16384, "parallelism": "none (1 GPU)"},
-        "model_tokens_per_s": 38580.2345, "roofline": {"bound": "mfma", "achieved": 1234.5678, "peak": 5000.0,
-                                                     "unit": "TFLOP/s", "frac": 0.2469, "traffic": 1.23456789e9,
-                                                     "kernel": "spgemm_tiled gate_up 16384x28672x4096 (2:4 fp8)"},
-        "vs_dense": 1.0234567, "gemm_frac": {"qkv": 0.3, "o": 0.3, "gate_up": 0.3, "down": 0.3},
-        "quant_GBs": 6123.4, "weight_prep_us": 1234.5,
+        "model_tokens_per_s": 250760.39866160208,
+        "roofline": {"bound": "mfma", "achieved": 1924.1565513970645, "peak": 5000.0, "unit": "TFLOP/s",
+                     "frac": 0.3848313102794129, "traffic": 3101175136.8254504,
+                     "kernel": "gate_up product 16384x28672x4096, 2:4 FP8 (256x256 wide kernel)"},
+        "vs_dense": 1.4618011575005978, "gemm_frac": {"qkv": 0.383, "o": 0.377, "gate_up": 0.392, "down": 0.434},
+        "quant_GBs": 5232.1, "sclk_MHz_gate_up": 1832.5, "weight_prep_us": 214.0,
         "l24_fp8_4096": {"tps": 12345678, "vs_dense": 1.234, "gemm_frac_max": 0.345},
         "l68_i8_4096": {"tps": 12345678, "vs_dense": 1.234, "gemm_frac_max": 0.345},
         "l68_fp8_4096": {"tps": 12345678, "vs_dense": 1.234, "gemm_frac_max": 0.345},
         "l68_i8_16384": {"tps": 12345678, "vs_dense": 1.234, "gemm_frac_max": 0.345},
         "l68_fp8_16384": {"tps": 12345678, "vs_dense": 1.234, "gemm_frac_max": 0.345},
-        "cpu_baseline": {"value": 123.456789, "unit": "tokens/s", "cores": 16, "kind": "oracle",
+        "cpu_baseline": {"value": 147.89924188351085, "unit": "tokens/s", "cores": 16, "kind": "oracle",
                          "cpu": "AMD EPYC 9575F 64-Core Processor", "host_cpus": 16,
-                         "sample": "256 tokens through the four linears: per-token FP8 quant of all K and the product "
-                                   "over >= 768 of each linear's channels, scaled to all channels; float64 BLAS "
-                                   "(16 threads), element-wise steps single-threaded NumPy; weight prep (12.3 s, "
-                                   "offline) not counted"},
-        "parity_vs_oracle": {"ok": True, "codes_bit_exact": True, "max_rel_fro": 1.234567e-06,
-                             "max_elem_over_bound": 0.01234567,
+                         "sample": "256 tokens, four linears: FP8 quant of all K, product over >= 768 channels of each "
+                                   "(scaled to all); float64 BLAS on 16 threads; weight prep (12.3 s) not counted"},
+        "parity_vs_oracle": {"ok": True, "codes_bit_exact": True, "max_rel_fro": 0.00016947884109797242,
+                             "max_elem_over_bound": 0.8965563788201644,
                              "sample": "256 tokens x >= 768 channels per linear, set 0 of the timed steps"},
         "detail": "gpurun_out/bench_detail.json",
     }
-    line = json.dumps(out, default=b._round, separators=(",", ":"))
-    assert len(line) < 2000, len(line)
+    line = json.dumps(b._sig6(out), default=b._round, separators=(",", ":"))
+    assert len(line) < 1900, len(line)
+    assert json.loads(line)["value"] == 8024330.0 and json.loads(line)["roofline"]["frac"] == 0.384831
 
 
 def _fake_layer(plant):
