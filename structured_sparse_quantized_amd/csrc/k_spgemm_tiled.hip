@@ -1096,15 +1096,19 @@ static bool few_tokens(bool side_x, int64_t R, int64_t C) {
   const int64_t tiles = ((R + tiled::BM - 1) / tiled::BM) * ((C + tiled::BN - 1) / tiled::BN);
   return !side_x && C <= 64 && (C <= 8 || tiles < 128);
 }
-// The wide-tile prefill kernel (k_spgemm_wide.hip) on the weight-sparse side, wherever its 256 x 256 tiles
-// still give every CU four or more: measured 1.07-1.3x the 256 x 128 kernel on the Llama-shaped layers at
-// 16384 tokens (qkv, o, gate_up, down) and on gate_up at 4096 tokens; with fewer tiles per CU the 256 x 128
-// kernel's finer grid wins. Its buffer loads take 32-bit offsets, so each operand stays below 2 GB.
-static bool use_wide(bool side_x, int64_t R, int64_t C, int64_t KS, int64_t ldb_bytes) {
-  const int64_t tiles = ((R + 255) / 256) * ((C + 255) / 256);
+// The wide-wave prefill kernel (k_spgemm_wide.hip) on the weight-sparse side: 256 x 256 tiles wherever they
+// still give every CU four or more (measured 1.07-1.3x this file's 256 x 128 kernel on the Llama-shaped layers
+// at 16384 tokens and on gate_up at 4096), else its 256 x 128 form with two workgroups per CU wherever that
+// gives a CU more than one tile (1.06-1.34x this file's kernel from 384 to 900 tiles on those layers at 512-8192
+// tokens; with one tile per CU or fewer, this file's eight waves per tile win). Its buffer loads take 32-bit
+// offsets, so each operand stays below 2 GB. Returns the tile width, or 0 for this file's kernel.
+static int wide_bn(bool side_x, int64_t R, int64_t C, int64_t KS, int64_t ldb_bytes) {
   const int64_t sparse_bytes = (R + 15) / 16 * ((KS + 3) / 4 * 4) * 1024, dense_bytes = C * ldb_bytes;
-  return !side_x && tiles >= 4 * (int64_t)num_cus_p() && sparse_bytes < (INT64_C(1) << 31) &&
-         dense_bytes < (INT64_C(1) << 31);
+  if (side_x || sparse_bytes >= (INT64_C(1) << 31) || dense_bytes >= (INT64_C(1) << 31)) return 0;
+  const int64_t cus = num_cus_p();
+  if (((R + 255) / 256) * ((C + 255) / 256) >= 4 * cus) return 256;
+  if (((R + 255) / 256) * ((C + 127) / 128) > cus) return 128;
+  return 0;
 }
 // The split-K path (with a workspace) serves the few-token products with more than 16 tokens.
 static bool use_splitk(bool side_x, int64_t R, int64_t C) { return few_tokens(side_x, R, C) && C > 16; }
@@ -1194,8 +1198,8 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
   // few tokens: split-K when a workspace is given and the problem uses one, else the row-block decode kernel
   const bool dec = few_tokens(side_x, R, C);
   const bool spk = ws != nullptr && use_splitk(side_x, R, C);
-  if (!spk && !dec && use_wide(side_x, R, C, ks, ldb_bytes))
-    return launch_spgemm_wide(ab, yt, r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st);
+  const int bn = spk || dec ? 0 : wide_bn(side_x, R, C, ks, ldb_bytes);
+  if (bn) return launch_spgemm_wide(bn, ab, yt, r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st);
 #define SS_TL(AB_, YT_)                                                                                   \
   return spk      ? splitk::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, ws, st)               \
          : dec    ? decode::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)                   \

@@ -5,27 +5,30 @@
 // C[r][c] = sum_k A[r][k] B[c][k]; A = the tiled compressed operand (rows r), B = the dense operand (rows c),
 // as in the 256 x 128 product of k_spgemm_tiled.hip, whose tiled layout this kernel reads unchanged.
 //
-// Why a wider tile: a 16x16x128 sparse instruction does the work of a dense 16x16x128 one in half the
-// matrix-core cycles, so per cycle it needs twice the operand bytes. A 256 x 256 tile moves 48 KB of
-// operands (16 KB of compressed A values, 32 KB of dense B rows) into LDS per 128-position step for
-// 16.8 M dense-equivalent operations -- 25% fewer L2 -> LDS bytes per operation than 256 x 128 -- and
-// waves of 128 x 128 read 25% fewer LDS bytes per operation than waves of 64 x 64.
-//
-// Workgroup: four waves (one per SIMD) in a 2 x 2 grid, each 128 A rows x 128 B rows = 8 x 8 instructions
-// per step; the 256 accumulator registers per lane sit in the accumulation registers, and the A and B
-// fragments are double-buffered in ordinary registers (the fragments of step j+1 are read from LDS while
-// the instructions of step j run), column by column of B.
-// LDS: a ring of three stages (48 KB each) filled by LDS DMA (buffer loads into LDS, 1 KB per wave instruction;
-// B rows swizzled so fragment reads are conflict-free), and one 16 KB slot holding the index words of the
-// current 4-step group (the tiled layout's metadata block of each of the 16 row blocks, brought in by DMA
-// one group ahead and read into registers after the last instruction of the group before). The slot takes the
-// tile's epilogue scales during the last group.
+// Why wide waves: a 16x16x128 sparse instruction does the work of a dense 16x16x128 one in half the
+// matrix-core cycles, so per cycle it needs twice the operand bytes; waves of 128 A rows read fewer LDS bytes
+// per operation than waves of 64. Two tile shapes, one workgroup of four waves (one per SIMD, 2 x 2) each:
+//  * BN = 256: 256 x 256 tiles, waves of 128 x 128 = 8 x 8 instructions per step, the 256 accumulators per
+//    lane in the accumulation registers. A 256 x 256 tile moves 48 KB of operands (16 KB of compressed A
+//    values, 32 KB of dense B rows) into LDS per 128-position step for 16.8 M dense-equivalent operations, 25%
+//    fewer L2 -> LDS bytes per operation than 256 x 128. LDS: a ring of three 48 KB stages and the 16 KB
+//    index-word slot (160 KB), so one workgroup per CU; A fragments double-buffered in registers.
+//  * BN = 128: 256 x 128 tiles, waves of 128 x 64 = 8 x 4 instructions per step (128 accumulators per lane,
+//    245 registers in all); a ring of two 32 KB stages and the index-word slot (80 KB), so two workgroups
+//    share a CU and the prologue and epilogue of one overlap the other's instructions. A fragments refilled
+//    right after their last use (the step's last column). For problems with more than one such tile per CU
+//    but too few 256 x 256 tiles to keep every CU busy.
+// LDS stages are filled by LDS DMA (buffer loads into LDS, 1 KB per wave instruction; B rows swizzled so
+// fragment reads are conflict-free); the index-word slot holds the current 4-step group's index words (the
+// tiled layout's metadata block of each of the 16 row blocks, brought in by DMA one group ahead and read into
+// registers after the last instruction of the group before) and takes the tile's epilogue scales during the
+// last group. B fragments are refilled column by column of B.
 // Synchronisation: one barrier per step. At the top of step j every wave waits until its own loads of
 // stage j+1 have landed (loads complete in issue order, so this is a wait for a fixed count of later
 // loads) and its own LDS reads are done, then the barrier makes stage j+1 visible and frees the slot of
-// stage j (read during step j-1), into which stage j+3 is loaded during step j, two loads per column of
-// instructions (with one wave per SIMD, a run of loads would leave the matrix core idle while it issues:
-// spreading them was 6-13% faster than issuing the stage at the top of the step).
+// stage j (read during step j-1), into which stage j+S (S stages in the ring) is loaded during step j, spread
+// over the step's columns (with one wave per SIMD, a run of loads would leave the matrix core idle while it
+// issues: spreading them was 6-13% faster than issuing the stage at the top of the step).
 #include <algorithm>
 
 #include "ss_device.h"
@@ -42,19 +45,30 @@ using tiled::swz;
 using tiled::v4i;
 #define SS_LDS __attribute__((address_space(3)))
 
-constexpr int BM = 256, BN = 256, NW = 4, WGN = 2, S = 3;
-constexpr int TI = 8, TJ = 8;                         // 8 x 8 instructions per wave per step
-constexpr int RBT = BM / 16;                          // row blocks of the sparse operand per tile
-constexpr int PA = RBT / NW, PB = BN / 8 / NW;        // LDS DMA loads per wave per step (1 KB each): 4 + 8
-constexpr int LPW = PA + PB;
-constexpr int A_BYTES = BM * 64, STAGE = A_BYTES + BN * 128;  // 16 KB + 32 KB
-constexpr int META = S * STAGE;                               // index-word slot (then the epilogue scales)
-constexpr int NSC = 2;                                        // scale loads per wave (A rows, B rows)
-template <int AB> constexpr int meta_slot() { return RBT * Meta<AB>::BLOCK; }           // 16 KB / 8 KB
-template <int AB> constexpr int mpw() { return meta_slot<AB>() / 1024 / NW; }          // meta loads per wave
-template <int AB> constexpr int lds_bytes() { return META + meta_slot<AB>(); }
-static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN, "load split");
-static_assert((BM + BN) * 4 <= 8 * 1024, "the epilogue scales fit the index-word slot");
+constexpr int BM = 256, NW = 4, WGN = 2, TI = 8;  // A rows per tile, waves, waves along B, A blocks per wave
+constexpr int RBT = BM / 16;                      // row blocks of the sparse operand per tile
+constexpr int PA = RBT / NW;                      // A loads per wave per step (1 KB each)
+constexpr int A_BYTES = BM * 64;                  // 16 KB of compressed A values per step
+constexpr int NSC = 2;                            // scale loads per wave (A rows, B rows)
+constexpr int TJMAX = 8;
+
+template <int BN> struct Shape {
+  static constexpr int TJ = BN / 32;              // B blocks per wave: 8 x TJ instructions per step
+  static constexpr int PB = BN / 8 / NW;          // B loads per wave per step (8 rows x 128 bytes each)
+  static constexpr int LPW = PA + PB;
+  static constexpr int STAGE = A_BYTES + BN * 128;
+  static constexpr int S = BN == 256 ? 3 : 2;     // stages in the ring
+  static constexpr int META = S * STAGE;          // index-word slot (then the epilogue scales)
+  static constexpr int OCC = BN == 256 ? 1 : 2;   // workgroups per CU
+  static constexpr bool ADB = BN == 256;          // A fragments double-buffered
+  static constexpr int SLOTS = BN == 256 ? 2 : 3; // loads per column
+  static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN && TJ <= TJMAX, "load split");
+  static_assert((BM + BN) * 4 <= 8 * 1024, "the epilogue scales fit the index-word slot");
+};
+template <int AB> constexpr int meta_slot() { return RBT * Meta<AB>::BLOCK; }    // 16 KB / 8 KB
+template <int AB> constexpr int mpw() { return meta_slot<AB>() / 1024 / NW; }   // meta loads per wave
+template <int BN, int AB> constexpr int lds_bytes() { return Shape<BN>::META + meta_slot<AB>(); }
+constexpr int up_rows(int tj, int cap) { return tj > cap && tj > 1 ? up_rows(tj / 2, cap) : tj; }
 
 constexpr int vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }  // s_waitcnt vmcnt(n)
 
@@ -63,12 +77,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
 
-template <int AB, int YT, bool SIDE_X, int GR>
-__global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, const uint8_t* __restrict__ tv,
-                                                          const uint8_t* __restrict__ tm,
-                                                          const uint8_t* __restrict__ bd, int ldb,
-                                                          const float* __restrict__ sx, const float* __restrict__ sw,
-                                                          void* __restrict__ Y, int ldy, int tiles_r, int tiles_c) {
+// (arrays that the loads index have fixed lengths: a length that depends on a template parameter in these
+// calls drops the kernel's host launch stub without a diagnostic)
+template <int BN, int AB, int YT, int GR>
+__global__ __launch_bounds__(64 * NW, Shape<BN>::OCC) void wide_kernel(
+    int R, int C, int KS, const uint8_t* __restrict__ tv, const uint8_t* __restrict__ tm, const uint8_t* __restrict__ bd,
+    int ldb, const float* __restrict__ sx, const float* __restrict__ sw, void* __restrict__ Y, int ldy, int tiles_r,
+    int tiles_c) {
+  using SH = Shape<BN>;
+  constexpr int TJ = SH::TJ, PB = SH::PB, LPW = SH::LPW, STAGE = SH::STAGE, S = SH::S, META = SH::META;
   using Acc = typename Mma<AB>::Acc;
   using MT = Meta<AB>;
   using MV = typename MT::V;
@@ -101,7 +118,7 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
 #pragma unroll
   for (int q = 0; q < PA; ++q)
     sA[q] = __builtin_amdgcn_readfirstlane((uint32_t)min(r0 / 16 + wave + q * NW, nrb - 1) * (uint32_t)KSP * 1024u);
-  uint32_t offb[PB];
+  uint32_t offb[TJMAX];  // PB of them
 #pragma unroll
   for (int q = 0; q < PB; ++q) {
     const int b = (wave + q * NW) * 8 + (lane >> 3);
@@ -111,8 +128,7 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
   // row block rb of the tile at offset off of its group block
   // (8-bit: one row block per instruction; bf16: two 512-byte blocks, the upper half of the wave the second)
   constexpr uint32_t MBLK = MT::BLOCK;
-  uint32_t om[4];  // MPW of them (a length that depends on a template parameter in these calls drops the
-                   // kernel's host launch stub without a diagnostic)
+  uint32_t om[4];  // MPW of them
   static_assert(MPW <= 4, "index-word loads per wave");
   const uint32_t moff = MT::BLOCK == 1024 ? l16 : (lane & 31) * 16;
 #pragma unroll
@@ -120,8 +136,8 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
     const int rb = (wave + NW * i) * (1024 / MT::BLOCK) + (MT::BLOCK == 1024 ? 0 : (lane >> 5));
     om[i] = (uint32_t)min(r0 / 16 + rb, nrb - 1) * (uint32_t)KS4 * (uint32_t)MT::BLOCK + moff;
   }
-  const float* sa = SIDE_X ? sx : sw;  // scale indexed by A row
-  const float* sb = SIDE_X ? sw : sx;  // scale indexed by B row
+  const float* sa = sw;  // scale indexed by A row (channels)
+  const float* sb = sx;  // scale indexed by B row (tokens)
 
   // Sources are a uniform base (scalar registers) plus a 32-bit lane offset; the stage's LDS offset is
   // uniform too.
@@ -161,23 +177,27 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(tm, nM), (SS_LDS void*)((SS_LDS uint8_t*)smem + META + (wave + NW * i) * 1024),
                                              16, om[i], g * MBLK, 0, 0);
   };
+  // A rows r0 + 64 wave + lane; B rows c0 + 64 (wave % (BN / 64)) + lane (with BN = 128, waves 2 and 3 bring the
+  // same bytes as waves 0 and 1)
   auto scale_one = [&](int i) {
     // a missing scale vector loads junk from a valid address (never used), so the count stays fixed
-    const int e = wave * 64 + lane;
+    const int wb = i == 0 ? wave : wave % (BN / 64);
+    const int e = wb * 64 + lane;
     const float* s = i == 0 ? (sa ? sa + min(r0 + e, R - 1) : reinterpret_cast<const float*>(tm) + lane)
                             : (sb ? sb + min(c0 + e, C - 1) : reinterpret_cast<const float*>(tm) + lane);
-    __builtin_amdgcn_global_load_lds((const void*)s, (SS_LDS void*)((SS_LDS uint8_t*)smem + META + i * 1024 + wave * 256), 4,
+    __builtin_amdgcn_global_load_lds((const void*)s, (SS_LDS void*)((SS_LDS uint8_t*)smem + META + i * 1024 + wb * 256), 4,
                                      0, 0);
   };
 
-  Acc acc[TI][TJ];
+  Acc acc[TI][TJMAX];
 #pragma unroll
   for (int t = 0; t < TI; ++t)
 #pragma unroll
     for (int u = 0; u < TJ; ++u) acc[t][u] = Acc{0, 0, 0, 0};
 
-  // fragments: A double-buffered (a[2]), B single-buffered (each column refilled right after its use)
-  v4i a0[TI], a1[TI], b[TJ][2];
+  // fragments: A double-buffered (a0 / a1) or refilled after its last use (a0 only), B single-buffered (each
+  // column refilled right after its use)
+  v4i a0[TI], a1[TI], b[TJMAX][2];
   MV mcur[TI];
   // LDS addresses: one per-lane base per operand (constant across steps) plus the stage's offset, so every
   // fragment read is that sum plus an immediate (all fragment offsets of a stage are below 48 KB).
@@ -203,19 +223,22 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
   };
   auto read_meta = [&](MV* m, int t) { m[t] = *reinterpret_cast<const SS_LDS MV*>(lds(lm) + t * MT::BLOCK); };
 
-  // Step j = 4g + Q: wait for stage j+1, barrier, issue stage j+3 (and the next group's index words, or at
-  // the last group the epilogue scales), then the 64 instructions of step j on (acur, b, mcur) column by
-  // column, each column followed by the reads of stage j+1's B column and one A fragment into anxt; at
-  // Q = 3 the next group's index words replace mcur after the last column.
-  // sl = slot of stage j (= slot of stage j + 3), sl1 = slot of stage j + 1 (LDS offsets)
+  // Step j = 4g + Q: wait for stage j+1, barrier, issue stage j+S (and the next group's index words, or at
+  // the last group the epilogue scales), then the 8 x TJ instructions of step j on (acur, b, mcur) column by
+  // column, each column followed by the reads of stage j+1's B column; stage j+1's A fragments go to anxt
+  // (one per column, BN = 256) or back into acur right after their last use (BN = 128); at Q = 3 the next
+  // group's index words replace mcur after the last column.
+  // sl = slot of stage j (= slot of stage j + S), sl1 = slot of stage j + 1 (LDS offsets)
   auto step = [&](int j, auto qc, auto lastc, v4i* acur, v4i* anxt, uint32_t sl, uint32_t sl1) {
     constexpr int Q = decltype(qc)::value;
     constexpr bool LAST = decltype(lastc)::value;
-    // loads issued after this wave's stage j+1: stage j+2 (if it exists) and the index words or scales
-    // issued at steps j-2 / j-1 after their stage
-    constexpr bool NEXT = !(LAST && Q == 3);                  // stage j+1 exists
-    constexpr bool S2 = !LAST || Q < 2;                        // stage j+2 exists
-    constexpr int N = (S2 ? LPW : 0) + (!LAST ? ((Q == 1 || Q == 2) ? MPW : 0) : (Q == 1 || Q == 2 ? NSC : 0));
+    constexpr bool NEXT = !(LAST && Q == 3);  // stage j+1 exists
+    constexpr bool SJ = !LAST || Q + S <= 3;   // stage j+S exists
+    // loads issued after this wave's stage j+1 (issued at step j+1-S): with three stages, stage j+2 (if it
+    // exists); the index words or scales issued right after a group's first stage load (at steps j-2 / j-1
+    // with three stages, at step j-1 with two)
+    constexpr int N = (S == 3 && (!LAST || Q < 2) ? LPW : 0) +
+                      ((Q == 1 || (S == 3 && Q == 2)) ? (LAST ? NSC : MPW) : 0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NEXT) {
       __builtin_amdgcn_s_waitcnt(vm(N));
@@ -223,20 +246,20 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
       __builtin_amdgcn_s_barrier();
     }
     __builtin_amdgcn_sched_barrier(0);
-    // The step's loads (stage j+3, then the next group's index words or the epilogue scales) are spread over
-    // its 64 instructions, two per column: one wave per SIMD has no other wave to issue instructions while it
-    // sends a run of loads, so the matrix core would idle behind it. Load slot s goes after instruction
-    // t = 0 (s even) or t = 4 (s odd) of column s / 2, the A fragment of stage j+1 after t = 1, and the two
-    // B fragment halves after the column's last instruction (their registers are free from then on).
-    constexpr bool ISSUE = !LAST || Q == 0;
-    constexpr int NL = ISSUE ? LPW + (!LAST ? (Q == 0 ? MPW : 0) : NSC) : 0;
+    // The step's loads (stage j+S, then the next group's index words or the epilogue scales) are spread over
+    // its instructions, SLOTS per column: one wave per SIMD has no other wave to issue instructions while it
+    // sends a run of loads, so the matrix core would idle behind it. BN = 256: load slot s goes after
+    // instruction t = 0 (s even) or t = 4 (s odd) of column s / 2, the A fragment of stage j+1 after t = 1;
+    // BN = 128: slots after t = 1, 4, 7. The two B fragment halves follow the column's last instruction (their
+    // registers are free from then on).
+    constexpr int NL = (SJ ? LPW : 0) + (Q == 0 ? (LAST ? NSC : MPW) : 0);
     auto load_slot = [&](int s) {
       if (s >= NL) return;
-      if (s < LPW) issue_one(s, j + 3, sl);
-      else if (!LAST) meta_one(s - LPW, j / 4 + 1);
-      else scale_one(s - LPW);
+      if (SJ && s < LPW) issue_one(s, j + S, sl);
+      else if (!LAST) meta_one(s - (SJ ? LPW : 0), j / 4 + 1);
+      else scale_one(s - (SJ ? LPW : 0));
     };
-    static_assert(LPW + MPW <= 2 * TJ && LPW + NSC <= 2 * TJ, "two load slots per column");
+    static_assert(LPW + MPW <= SH::SLOTS * TJ && LPW + NSC <= SH::SLOTS * TJ, "load slots per column");
     const Addr st = addr(sl1);
 #pragma unroll
     for (int u = 0; u < TJ; ++u) {
@@ -244,17 +267,28 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
       for (int t = 0; t < TI; ++t) {
         acc[t][u] = tiled::mma_step<AB, Q>(acur[t], b[u][0], b[u][1], acc[t][u], mcur[t]);
         __builtin_amdgcn_sched_barrier(0);
-        if (t == 0) {
-          load_slot(2 * u);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (t == 1 && NEXT) {
-          read_a(anxt, u, st);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (t == 4) {
-          load_slot(2 * u + 1);
-          __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SH::ADB) {
+          if (t == 0) {
+            load_slot(2 * u);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (t == 1 && NEXT) {
+            read_a(anxt, u, st);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (t == 4) {
+            load_slot(2 * u + 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          if (u == TJ - 1 && NEXT) {
+            read_a(anxt, t, st);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (t == 1 || t == 4 || t == 7) {
+            load_slot(3 * u + (t == 1 ? 0 : t == 4 ? 1 : 2));
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
       if constexpr (NEXT) {
@@ -275,12 +309,11 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
   using NotLast = std::false_type;
   using Last = std::true_type;
 
-  // prologue: group 0's index words, stages 0..2; wait for stage 0
+  // prologue: group 0's index words, stages 0 .. S-1; wait for stage 0
   issue_meta(0);
-  issue(0, 0);
-  issue(1, STAGE);
-  issue(2, 2 * STAGE);
-  __builtin_amdgcn_s_waitcnt(vm(2 * LPW));
+#pragma unroll
+  for (int k = 0; k < S; ++k) issue(k, k * STAGE);
+  __builtin_amdgcn_s_waitcnt(vm((S - 1) * LPW));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   {
@@ -292,34 +325,39 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
 #pragma unroll
     for (int t = 0; t < TI; ++t) read_meta(mcur, t);
   }
-  // slot offsets of stages j, j+1, j+2 (uniform), rotated every step
+  // slot offsets of stages j, j+1 (and j+2) (uniform), rotated every step
   uint32_t s0 = 0, s1 = STAGE, s2 = 2 * STAGE;
   auto rot = [&]() {
     const uint32_t t = s0;
     s0 = __builtin_amdgcn_readfirstlane(s1);
-    s1 = __builtin_amdgcn_readfirstlane(s2);
-    s2 = __builtin_amdgcn_readfirstlane(t);
+    if constexpr (S == 3) {
+      s1 = __builtin_amdgcn_readfirstlane(s2);
+      s2 = __builtin_amdgcn_readfirstlane(t);
+    } else {
+      s1 = __builtin_amdgcn_readfirstlane(t);
+    }
   };
+  v4i* const ax = SH::ADB ? a1 : a0;  // the second A buffer (the first again when single-buffered)
   for (int g = 0; g + 1 < G; ++g) {
     const int j = 4 * g;
-    step(j, Q0{}, NotLast{}, a0, a1, s0, s1);
+    step(j, Q0{}, NotLast{}, a0, ax, s0, s1);
     rot();
-    step(j + 1, Q1{}, NotLast{}, a1, a0, s0, s1);
+    step(j + 1, Q1{}, NotLast{}, ax, a0, s0, s1);
     rot();
-    step(j + 2, Q2{}, NotLast{}, a0, a1, s0, s1);
+    step(j + 2, Q2{}, NotLast{}, a0, ax, s0, s1);
     rot();
-    step(j + 3, Q3{}, NotLast{}, a1, a0, s0, s1);
+    step(j + 3, Q3{}, NotLast{}, ax, a0, s0, s1);
     rot();
   }
   {
     const int j = KSP - 4;
-    step(j, Q0{}, Last{}, a0, a1, s0, s1);
+    step(j, Q0{}, Last{}, a0, ax, s0, s1);
     rot();
-    step(j + 1, Q1{}, Last{}, a1, a0, s0, s1);
+    step(j + 1, Q1{}, Last{}, ax, a0, s0, s1);
     rot();
-    step(j + 2, Q2{}, Last{}, a0, a1, s0, s1);
+    step(j + 2, Q2{}, Last{}, a0, ax, s0, s1);
     rot();
-    step(j + 3, Q3{}, Last{}, a1, a0, s0, s1);
+    step(j + 3, Q3{}, Last{}, ax, a0, s0, s1);
   }
   __builtin_amdgcn_s_waitcnt(vm(0));  // the scales (and no load may outlive the workgroup)
   __builtin_amdgcn_s_barrier();
@@ -338,7 +376,7 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
     // takes the same two multiplies with no branch per value.
     const float* scl = reinterpret_cast<const float*>(smem + META);
     const bool has_a = sa != nullptr, has_b = sb != nullptr;
-    float s_a[TI][4], s_b[TJ];
+    float s_a[TI][4], s_b[TJMAX];
   #pragma unroll
     for (int t = 0; t < TI; ++t) {
       const float4 v = *reinterpret_cast<const float4*>(scl + (wm * TI + t) * 16 + 4 * jj);
@@ -349,97 +387,78 @@ __global__ __launch_bounds__(64 * NW, 1) void wide_kernel(int R, int C, int KS, 
     }
   #pragma unroll
     for (int u = 0; u < TJ; ++u) s_b[u] = has_b ? scl[256 + (wn * TJ + u) * 16 + r16] : 1.0f;
-    // lane's 4 results of instruction tile (t, u): A rows 16 t + 4 jj + q, B row 16 u + r16 (wave-local)
+    // lane's 4 results of instruction tile (t, u): A rows 16 t + 4 jj + q, B row 16 u + r16 (wave-local);
+    // the token scale first, then the channel scale
     auto result = [&](int t, int u, float* y, int32_t* yi) {
   #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if constexpr (YT == 2) {
-          yi[q] = (int32_t)acc[t][u][q];
-        } else {
-          // the token scale first, then the channel scale
-          const float s1 = SIDE_X ? s_a[t][q] : s_b[u], s2 = SIDE_X ? s_b[u] : s_a[t][q];
-          y[q] = __fmul_rn(__fmul_rn((float)acc[t][u][q], s1), s2);
-        }
+        if constexpr (YT == 2) yi[q] = (int32_t)acc[t][u][q];
+        else y[q] = __fmul_rn(__fmul_rn((float)acc[t][u][q], s_b[u]), s_a[t][q]);
       }
     };
-    if constexpr (SIDE_X) {
+    // Y[B row][A row]: each lane holds 4 consecutive A rows of one B row (8 or 16 bytes). The wave's 128 x 16 TJ
+    // results go through its own part of the (now idle) stage ring, 16 UP B rows per pass, rows padded by 16
+    // bytes so both the writes and the reads are free of bank conflicts, and leave as 16-byte pieces that
+    // cover whole output rows.
+    constexpr int EB = YT == 0 ? 2 : 4;                                        // output element bytes
+    constexpr int STRIDE = 128 * EB + 16, CPR = 128 * EB / 16;                 // row bytes, 16-byte chunks
+    constexpr int UP = up_rows(TJ, META / NW / (16 * STRIDE)), NP = TJ / UP;  // B fragments per pass; passes
+    constexpr int RP = 16 * UP;                                                // rows per pass
+    static_assert(NW * RP * STRIDE <= META, "staging fits the stage ring");
+    SS_LDS uint8_t* stg = (SS_LDS uint8_t*)smem + wave * RP * STRIDE;
+    const bool vec = ((int64_t)ldy * EB) % 16 == 0;
+    uint8_t* Yb = static_cast<uint8_t*>(Y);
   #pragma unroll
-      for (int t = 0; t < TI; ++t) {
-        const int ar = r0 + (wm * TI + t) * 16 + 4 * jj;  // 4 consecutive A rows
+    for (int p = 0; p < NP; ++p) {
   #pragma unroll
-        for (int u = 0; u < TJ; ++u) {
-          const int bc = c0 + (wn * TJ + u) * 16 + r16;  // one B row
-          if (bc >= C) continue;
+      for (int uu = 0; uu < UP; ++uu) {
+  #pragma unroll
+        for (int t = 0; t < TI; ++t) {
           float y[4];
           int32_t yi[4];
-          result(t, u, y, yi);
-          store_out<YT, SIDE_X>(Y, ldy, ar, bc, R, y, yi);
-        }
-      }
-    } else {
-      // Side W writes Y[B row][A row]: each lane holds 4 consecutive A rows of one B row (8 or 16 bytes). The
-      // wave's 128 x 128 results go through its own part of the (now idle) stage ring, rows padded by 16 bytes
-      // so both the writes and the reads are free of bank conflicts, and leave as 16-byte pieces that cover
-      // whole output rows (4-byte results in two passes of 64 rows).
-      constexpr int EB = YT == 0 ? 2 : 4;             // output element bytes
-      constexpr int NP = EB == 2 ? 1 : 2, UP = TJ / NP;  // passes; B fragments per pass
-      constexpr int RP = 16 * UP, STRIDE = 128 * EB + 16, CPR = 128 * EB / 16;  // rows, row bytes, 16-byte chunks
-      static_assert(NW * RP * STRIDE <= META, "staging fits the stage ring");
-      SS_LDS uint8_t* stg = (SS_LDS uint8_t*)smem + wave * RP * STRIDE;
-      const bool vec = ((int64_t)ldy * EB) % 16 == 0;
-      uint8_t* Yb = static_cast<uint8_t*>(Y);
-  #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-  #pragma unroll
-        for (int uu = 0; uu < UP; ++uu) {
-  #pragma unroll
-          for (int t = 0; t < TI; ++t) {
-            float y[4];
-            int32_t yi[4];
-            result(t, p * UP + uu, y, yi);
-            SS_LDS uint8_t* d = stg + (uu * 16 + r16) * STRIDE + (t * 16 + 4 * jj) * EB;
-            if constexpr (YT == 0) {
-              *reinterpret_cast<SS_LDS tiled::v2i*>(d) = tiled::v2i{(int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
-            } else if constexpr (YT == 1) {
-              *reinterpret_cast<SS_LDS v4i*>(d) = v4i{__float_as_int(y[0]), __float_as_int(y[1]), __float_as_int(y[2]),
-                                                      __float_as_int(y[3])};
-            } else {
-              *reinterpret_cast<SS_LDS v4i*>(d) = v4i{yi[0], yi[1], yi[2], yi[3]};
-            }
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-  #pragma unroll 4
-        for (int i = lane; i < RP * CPR; i += 64) {
-          const int row = i / CPR, ch = i % CPR;
-          const v4i v = *reinterpret_cast<const SS_LDS v4i*>(stg + row * STRIDE + ch * 16);
-          const int bc = c0 + (wn * TJ + p * UP) * 16 + row;
-          const int ar = r0 + wm * TI * 16 + ch * (16 / EB);
-          if (bc >= C) continue;
-          uint8_t* dst = Yb + ((int64_t)bc * ldy + ar) * EB;
-          if (vec && ar + 16 / EB <= R) {
-            __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));  // whole rows: no line left to merge in L2
+          result(t, p * UP + uu, y, yi);
+          SS_LDS uint8_t* d = stg + (uu * 16 + r16) * STRIDE + (t * 16 + 4 * jj) * EB;
+          if constexpr (YT == 0) {
+            *reinterpret_cast<SS_LDS tiled::v2i*>(d) = tiled::v2i{(int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
+          } else if constexpr (YT == 1) {
+            *reinterpret_cast<SS_LDS v4i*>(d) = v4i{__float_as_int(y[0]), __float_as_int(y[1]), __float_as_int(y[2]),
+                                                    __float_as_int(y[3])};
           } else {
-            const uint32_t w[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
-  #pragma unroll
-            for (int e = 0; e < 16 / EB; ++e) {
-              if (ar + e >= R) break;
-              if constexpr (EB == 2) reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-              else reinterpret_cast<uint32_t*>(dst)[e] = w[e];
-            }
+            *reinterpret_cast<SS_LDS v4i*>(d) = v4i{yi[0], yi[1], yi[2], yi[3]};
           }
         }
-        __builtin_amdgcn_wave_barrier();
       }
+      __builtin_amdgcn_wave_barrier();
+  #pragma unroll 4
+      for (int i = lane; i < RP * CPR; i += 64) {
+        const int row = i / CPR, ch = i % CPR;
+        const v4i v = *reinterpret_cast<const SS_LDS v4i*>(stg + row * STRIDE + ch * 16);
+        const int bc = c0 + (wn * TJ + p * UP) * 16 + row;
+        const int ar = r0 + wm * TI * 16 + ch * (16 / EB);
+        if (bc >= C) continue;
+        uint8_t* dst = Yb + ((int64_t)bc * ldy + ar) * EB;
+        if (vec && ar + 16 / EB <= R) {
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));  // whole rows: no line left to merge in L2
+        } else {
+          const uint32_t w[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+  #pragma unroll
+          for (int e = 0; e < 16 / EB; ++e) {
+            if (ar + e >= R) break;
+            if constexpr (EB == 2) reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+            else reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
 
-template <int AB, int YT, bool SIDE_X, int GR = 8>
+template <int BN, int AB, int YT, int GR = 8>
 hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb, const float* sx,
                   const float* sw, void* Y, int ldy, hipStream_t st) {
-  auto kern = wide_kernel<AB, YT, SIDE_X, GR>;
-  constexpr int lds = lds_bytes<AB>();
+  auto kern = wide_kernel<BN, AB, YT, GR>;
+  constexpr int lds = lds_bytes<BN, AB>();
   const hipError_t e = lds_limit((const void*)kern, lds);
   if (e != hipSuccess) return e;
   const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
@@ -447,21 +466,29 @@ hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, co
   return hipGetLastError();
 }
 
-}  // namespace wide
-
-hipError_t launch_spgemm_wide(int ab, int yt, int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd,
-                              int ldb, const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
+template <int BN>
+hipError_t launch_bn(int ab, int yt, int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb,
+                     const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
   if (ab == 0) {
-    if (yt == 0) return wide::launch<0, 0, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-    if (yt == 1) return wide::launch<0, 1, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-    return wide::launch<0, 2, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 0) return launch<BN, 0, 0>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 1) return launch<BN, 0, 1>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    return launch<BN, 0, 2>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
   }
   if (ab == 1) {
-    if (yt == 0) return wide::launch<1, 0, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-    return wide::launch<1, 1, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 0) return launch<BN, 1, 0>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    return launch<BN, 1, 1>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
   }
-  if (yt == 0) return wide::launch<2, 0, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-  return wide::launch<2, 1, false>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  if (yt == 0) return launch<BN, 2, 0>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  return launch<BN, 2, 1>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+}
+
+}  // namespace wide
+
+hipError_t launch_spgemm_wide(int bn, int ab, int yt, int R, int C, int KS, const uint8_t* tv, const uint8_t* tm,
+                              const uint8_t* bd, int ldb, const float* sx, const float* sw, void* Y, int ldy,
+                              hipStream_t st) {
+  return bn == 256 ? wide::launch_bn<256>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st)
+                   : wide::launch_bn<128>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
 }
 
 }  // namespace ss

@@ -115,13 +115,15 @@ def test_one_launch_decode_many_row_blocks(ss, n, M):
     _layer(ss, n, "i8", M, K, N, seed=7 * n + M, fused=True)
 
 
+@pytest.mark.parametrize("shape", [(4000, 1280, 16484), (1500, 1280, 6000)], ids=["256x256", "256x128"])
 @pytest.mark.parametrize("q", ["i8", "fp8", "bf16"])
-def test_wide_kernel_ragged(ss, q):
-    """A product large enough for the 256 x 256 kernel (four or more 256 x 256 tiles per CU) with ragged
-    tiles on both sides and a reduction that ends inside a 4-step index group: N = 16484 channels, 4000
-    tokens, K = 1280 (INT8 / FP8: 10 steps of 128; bf16: 20 steps of 64)."""
+def test_wide_kernel_ragged(ss, q, shape):
+    """Products routed to the wide-wave kernel, with ragged tiles on both sides and a reduction that ends inside
+    a 4-step index group (K = 1280: INT8 / FP8 10 steps of 128, bf16 20 steps of 64): N = 16484 channels and
+    4000 tokens take its 256 x 256 tiles (four or more per CU), N = 6000 and 1500 tokens its 256 x 128 tiles
+    with two workgroups per CU (288 such tiles, 144 of 256 x 256)."""
     import torch
-    M, K, N = 4000, 1280, 16484
+    M, K, N = shape
     gen = torch.Generator(device="cuda")
     gen.manual_seed(99)
     W = torch.randn((N, K), generator=gen, device="cuda") * 0.02
