@@ -1101,12 +1101,14 @@ static bool few_tokens(bool side_x, int64_t R, int64_t C) {
 // at 16384 tokens and on gate_up at 4096), else its 256 x 128 form with two workgroups per CU wherever that
 // gives a CU more than one tile (1.06-1.34x this file's kernel from 384 to 900 tiles on those layers at 512-8192
 // tokens; with one tile per CU or fewer, this file's eight waves per tile win). Its buffer loads take 32-bit
-// offsets, so each operand stays below 2 GB. Returns the tile width, or 0 for this file's kernel.
+// offsets, so each operand stays below 2 GB. The sparse-activation side takes the 256 x 128 form under the
+// same rule (1.2x this file's kernel on an 8192 x 4096 x 4096 product). Returns the tile width, or 0 for this
+// file's kernel.
 static int wide_bn(bool side_x, int64_t R, int64_t C, int64_t KS, int64_t ldb_bytes) {
   const int64_t sparse_bytes = (R + 15) / 16 * ((KS + 3) / 4 * 4) * 1024, dense_bytes = C * ldb_bytes;
-  if (side_x || sparse_bytes >= (INT64_C(1) << 31) || dense_bytes >= (INT64_C(1) << 31)) return 0;
+  if (sparse_bytes >= (INT64_C(1) << 31) || dense_bytes >= (INT64_C(1) << 31)) return 0;
   const int64_t cus = num_cus_p();
-  if (((R + 255) / 256) * ((C + 255) / 256) >= 4 * cus) return 256;
+  if (!side_x && ((R + 255) / 256) * ((C + 255) / 256) >= 4 * cus) return 256;
   if (((R + 255) / 256) * ((C + 127) / 128) > cus) return 128;
   return 0;
 }
@@ -1199,7 +1201,7 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
   const bool dec = few_tokens(side_x, R, C);
   const bool spk = ws != nullptr && use_splitk(side_x, R, C);
   const int bn = spk || dec ? 0 : wide_bn(side_x, R, C, ks, ldb_bytes);
-  if (bn) return launch_spgemm_wide(bn, ab, yt, r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st);
+  if (bn) return launch_spgemm_wide(bn, side_x, ab, yt, r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st);
 #define SS_TL(AB_, YT_)                                                                                   \
   return spk      ? splitk::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, ws, st)               \
          : dec    ? decode::launch<AB_, YT_>(r, c, ks, tv, tm, b, lb, sx, sw, Y, ly, st)                   \

@@ -79,7 +79,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 
 // (arrays that the loads index have fixed lengths: a length that depends on a template parameter in these
 // calls drops the kernel's host launch stub without a diagnostic)
-template <int BN, int AB, int YT, int GR>
+template <int BN, int AB, int YT, bool SX, int GR>
 __global__ __launch_bounds__(64 * NW, Shape<BN>::OCC) void wide_kernel(
     int R, int C, int KS, const uint8_t* __restrict__ tv, const uint8_t* __restrict__ tm, const uint8_t* __restrict__ bd,
     int ldb, const float* __restrict__ sx, const float* __restrict__ sw, void* __restrict__ Y, int ldy, int tiles_r,
@@ -136,8 +136,8 @@ __global__ __launch_bounds__(64 * NW, Shape<BN>::OCC) void wide_kernel(
     const int rb = (wave + NW * i) * (1024 / MT::BLOCK) + (MT::BLOCK == 1024 ? 0 : (lane >> 5));
     om[i] = (uint32_t)min(r0 / 16 + rb, nrb - 1) * (uint32_t)KS4 * (uint32_t)MT::BLOCK + moff;
   }
-  const float* sa = sw;  // scale indexed by A row (channels)
-  const float* sb = sx;  // scale indexed by B row (tokens)
+  const float* sa = SX ? sx : sw;  // scale indexed by A row
+  const float* sb = SX ? sw : sx;  // scale indexed by B row
 
   // Sources are a uniform base (scalar registers) plus a 32-bit lane offset; the stage's LDS offset is
   // uniform too.
@@ -392,22 +392,82 @@ __global__ __launch_bounds__(64 * NW, Shape<BN>::OCC) void wide_kernel(
     auto result = [&](int t, int u, float* y, int32_t* yi) {
   #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if constexpr (YT == 2) yi[q] = (int32_t)acc[t][u][q];
-        else y[q] = __fmul_rn(__fmul_rn((float)acc[t][u][q], s_b[u]), s_a[t][q]);
+        if constexpr (YT == 2) {
+          yi[q] = (int32_t)acc[t][u][q];
+        } else {
+          const float s1 = SX ? s_a[t][q] : s_b[u], s2 = SX ? s_b[u] : s_a[t][q];
+          y[q] = __fmul_rn(__fmul_rn((float)acc[t][u][q], s1), s2);
+        }
       }
     };
+    constexpr int EB = YT == 0 ? 2 : 4;  // output element bytes
+    const bool vec = ((int64_t)ldy * EB) % 16 == 0;
+    uint8_t* Yb = static_cast<uint8_t*>(Y);
+    // one 16-byte piece of staged results: whole when it lies inside Y and rows are 16-byte aligned, else
+    // element by element (row: the output row; col: its first column; n: columns in Y)
+    auto put = [&](const v4i& v, int row, int col, int ncol) {
+      uint8_t* dst = Yb + ((int64_t)row * ldy + col) * EB;
+      if (vec && col + 16 / EB <= ncol) {
+        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));  // whole rows: no line left to merge in L2
+      } else {
+        const uint32_t w[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+  #pragma unroll
+        for (int e = 0; e < 16 / EB; ++e) {
+          if (col + e >= ncol) break;
+          if constexpr (EB == 2) reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          else reinterpret_cast<uint32_t*>(dst)[e] = w[e];
+        }
+      }
+    };
+    if constexpr (SX) {
+      // Y[A row][B row]: a lane's 4 results of a tile lie in 4 output rows. The wave's 128 x 16 TJ results go
+      // through its part of the idle ring as [A row][B row] (16 RX A rows per pass, rows padded by 16 bytes: the
+      // 2- or 4-byte writes of a tile and the 16-byte reads are free of bank conflicts) and leave as 16-byte
+      // pieces of output rows.
+      constexpr int STRIDE = 16 * TJ * EB + 16, CPR = TJ * EB;                  // row bytes, 16-byte chunks
+      constexpr int RX = up_rows(TI, META / NW / (16 * STRIDE)), NP = TI / RX;  // A blocks per pass; passes
+      static_assert(NW * 16 * RX * STRIDE <= META, "staging fits the stage ring");
+      SS_LDS uint8_t* stg = (SS_LDS uint8_t*)smem + wave * 16 * RX * STRIDE;
+  #pragma unroll
+      for (int p = 0; p < NP; ++p) {
+  #pragma unroll
+        for (int tt = 0; tt < RX; ++tt) {
+  #pragma unroll
+          for (int u = 0; u < TJ; ++u) {
+            float y[4];
+            int32_t yi[4];
+            result(p * RX + tt, u, y, yi);
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              SS_LDS uint8_t* d = stg + (tt * 16 + 4 * jj + q) * STRIDE + (u * 16 + r16) * EB;
+              if constexpr (YT == 0) *reinterpret_cast<SS_LDS uint16_t*>(d) = (uint16_t)pack_bf16x2(y[q], 0.0f);
+              else if constexpr (YT == 1) *reinterpret_cast<SS_LDS float*>(d) = y[q];
+              else *reinterpret_cast<SS_LDS int32_t*>(d) = yi[q];
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+  #pragma unroll 4
+        for (int i = lane; i < 16 * RX * CPR; i += 64) {
+          const int row = i / CPR, ch = i % CPR;
+          const v4i v = *reinterpret_cast<const SS_LDS v4i*>(stg + row * STRIDE + ch * 16);
+          const int ar = r0 + (wm * TI + p * RX) * 16 + row;
+          if (ar >= R) continue;
+          put(v, ar, c0 + wn * TJ * 16 + ch * (16 / EB), C);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      return;
+    }
     // Y[B row][A row]: each lane holds 4 consecutive A rows of one B row (8 or 16 bytes). The wave's 128 x 16 TJ
     // results go through its own part of the (now idle) stage ring, 16 UP B rows per pass, rows padded by 16
     // bytes so both the writes and the reads are free of bank conflicts, and leave as 16-byte pieces that
     // cover whole output rows.
-    constexpr int EB = YT == 0 ? 2 : 4;                                        // output element bytes
     constexpr int STRIDE = 128 * EB + 16, CPR = 128 * EB / 16;                 // row bytes, 16-byte chunks
     constexpr int UP = up_rows(TJ, META / NW / (16 * STRIDE)), NP = TJ / UP;  // B fragments per pass; passes
     constexpr int RP = 16 * UP;                                                // rows per pass
     static_assert(NW * RP * STRIDE <= META, "staging fits the stage ring");
     SS_LDS uint8_t* stg = (SS_LDS uint8_t*)smem + wave * RP * STRIDE;
-    const bool vec = ((int64_t)ldy * EB) % 16 == 0;
-    uint8_t* Yb = static_cast<uint8_t*>(Y);
   #pragma unroll
     for (int p = 0; p < NP; ++p) {
   #pragma unroll
@@ -434,30 +494,18 @@ __global__ __launch_bounds__(64 * NW, Shape<BN>::OCC) void wide_kernel(
         const int row = i / CPR, ch = i % CPR;
         const v4i v = *reinterpret_cast<const SS_LDS v4i*>(stg + row * STRIDE + ch * 16);
         const int bc = c0 + (wn * TJ + p * UP) * 16 + row;
-        const int ar = r0 + wm * TI * 16 + ch * (16 / EB);
         if (bc >= C) continue;
-        uint8_t* dst = Yb + ((int64_t)bc * ldy + ar) * EB;
-        if (vec && ar + 16 / EB <= R) {
-          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));  // whole rows: no line left to merge in L2
-        } else {
-          const uint32_t w[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
-  #pragma unroll
-          for (int e = 0; e < 16 / EB; ++e) {
-            if (ar + e >= R) break;
-            if constexpr (EB == 2) reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-            else reinterpret_cast<uint32_t*>(dst)[e] = w[e];
-          }
-        }
+        put(v, bc, r0 + wm * TI * 16 + ch * (16 / EB), R);
       }
       __builtin_amdgcn_wave_barrier();
     }
   }
 }
 
-template <int BN, int AB, int YT, int GR = 8>
+template <int BN, int AB, int YT, bool SX, int GR = 8>
 hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb, const float* sx,
                   const float* sw, void* Y, int ldy, hipStream_t st) {
-  auto kern = wide_kernel<BN, AB, YT, GR>;
+  auto kern = wide_kernel<BN, AB, YT, SX, GR>;
   constexpr int lds = lds_bytes<BN, AB>();
   const hipError_t e = lds_limit((const void*)kern, lds);
   if (e != hipSuccess) return e;
@@ -466,29 +514,30 @@ hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, co
   return hipGetLastError();
 }
 
-template <int BN>
+template <int BN, bool SX>
 hipError_t launch_bn(int ab, int yt, int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb,
                      const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
   if (ab == 0) {
-    if (yt == 0) return launch<BN, 0, 0>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-    if (yt == 1) return launch<BN, 0, 1>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-    return launch<BN, 0, 2>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 0) return launch<BN, 0, 0, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 1) return launch<BN, 0, 1, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    return launch<BN, 0, 2, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
   }
   if (ab == 1) {
-    if (yt == 0) return launch<BN, 1, 0>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-    return launch<BN, 1, 1>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 0) return launch<BN, 1, 0, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    return launch<BN, 1, 1, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
   }
-  if (yt == 0) return launch<BN, 2, 0>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-  return launch<BN, 2, 1>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  if (yt == 0) return launch<BN, 2, 0, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  return launch<BN, 2, 1, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
 }
 
 }  // namespace wide
 
-hipError_t launch_spgemm_wide(int bn, int ab, int yt, int R, int C, int KS, const uint8_t* tv, const uint8_t* tm,
-                              const uint8_t* bd, int ldb, const float* sx, const float* sw, void* Y, int ldy,
-                              hipStream_t st) {
-  return bn == 256 ? wide::launch_bn<256>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st)
-                   : wide::launch_bn<128>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+hipError_t launch_spgemm_wide(int bn, bool side_x, int ab, int yt, int R, int C, int KS, const uint8_t* tv,
+                              const uint8_t* tm, const uint8_t* bd, int ldb, const float* sx, const float* sw, void* Y,
+                              int ldy, hipStream_t st) {
+  if (side_x) return wide::launch_bn<128, true>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  return bn == 256 ? wide::launch_bn<256, false>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st)
+                   : wide::launch_bn<128, false>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
 }
 
 }  // namespace ss

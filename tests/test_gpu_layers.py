@@ -115,6 +115,43 @@ def test_one_launch_decode_many_row_blocks(ss, n, M):
     _layer(ss, n, "i8", M, K, N, seed=7 * n + M, fused=True)
 
 
+@pytest.mark.parametrize("q,y", [("i8", "i32"), ("i8", "bf16"), ("fp8", "f32"), ("fp8", "bf16"), ("bf16", "f32")])
+def test_wide_kernel_sparse_activations_ragged(ss, q, y):
+    """The sparse-activation side on the wide-wave kernel's 256 x 128 form (6000 tokens pruned 2:4 online into
+    the tiled layout x 1500 dense channels: 288 tiles), ragged on both sides, K = 1280 ending inside a 4-step
+    index group; outputs Y[token][channel] staged as whole 16-byte row pieces."""
+    import torch
+    M, K, N = 6000, 1280, 1500
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(123)
+    X = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+    W = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+    tv, tm, sx = ss.prune24_act_tiled(X, q)
+    if q == "bf16":
+        wd, sw = W.to(torch.bfloat16), None
+    else:
+        wd, sw = ss.quant_lift_act(W, 2, q)
+    Y = ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, K, tv, tm, wd, sx, sw, y)
+    rng = np.random.default_rng(9)
+    toks = _sample(M, 48, rng, edge=128)
+    chans = _sample(N, 96, rng, edge=128)
+    Xh = X.index_select(0, torch.from_numpy(toks).cuda()).view(torch.int16).cpu().numpy().view(np.uint16)
+    Wc = W.index_select(0, torch.from_numpy(chans).cuda())
+    got = host(Y)[np.ix_(toks, chans)]
+    ov, om, osx = oracle.prune24_act(Xh, q)
+    if q == "bf16":
+        ow, osw = Wc.to(torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16), None
+    else:
+        ow, osw = oracle.quant_lift_act(Wc.cpu().numpy(), 2, q)
+    exp = oracle.spgemm("X", ov, om, ow, K, q, osx, osw, y)
+    if q == "i8":
+        assert np.array_equal(got, exp)
+        return
+    g, e = (bf16_to_f64(got), bf16_to_f64(exp)) if y == "bf16" else (got, exp)
+    assert rel_fro(g, e) <= 1e-2
+    assert_elementwise(g, e, sum_abs_terms(ov, om, ow, K, q, osw, osx).T, out=y)
+
+
 @pytest.mark.parametrize("shape", [(4000, 1280, 16484), (1500, 1280, 6000)], ids=["256x256", "256x128"])
 @pytest.mark.parametrize("q", ["i8", "fp8", "bf16"])
 def test_wide_kernel_ragged(ss, q, shape):
