@@ -1,7 +1,7 @@
 """The online half of the path (quant+lift, then the sparse product) captured in a HIP graph: the calls
 are stateless, allocate nothing and record no memset, so a graph replays them. Each replay runs on new
 input contents written between replays, with eager work and synchronisations in between, and must equal
-eager calls on the same inputs bit for bit. Covers the prefill kernel, the few-token row-block kernel,
+eager calls on the same inputs bit for bit. Covers the prefill kernels, the few-token row-block kernel,
 the split-K kernel with a caller-owned workspace, the block-scaled FP8 pair and the one-launch few-token
 entry."""
 import numpy as np
@@ -18,8 +18,11 @@ def ss():
     return m
 
 
-# (tokens, channels, K, n): prefill 6:8; decode 4:6 at 1 token (row-block kernel) and 48 tokens (split-K)
-CASES = [(2048, 4096, 4096, 4), (1, 3584, 18944, 3), (48, 3584, 18944, 3), (40, 4608, 3584, 5)]
+# (tokens, channels, K, n): prefill 6:8 (8-wave kernel); 2:4 prefill on the wide-wave kernel's 256 x 128
+# (4096 x 6144) and 256 x 256 (16384 x 4096) forms; decode 4:6 at 1 token (row-block kernel) and 48 tokens
+# (split-K)
+CASES = [(2048, 4096, 4096, 4), (4096, 6144, 4096, 2), (16384, 4096, 4096, 2), (1, 3584, 18944, 3),
+         (48, 3584, 18944, 3), (40, 4608, 3584, 5)]
 
 
 @pytest.mark.parametrize("case", CASES)
