@@ -7,17 +7,22 @@
 //
 // Why wide waves: a 16x16x128 sparse instruction does the work of a dense 16x16x128 one in half the
 // matrix-core cycles, so per cycle it needs twice the operand bytes; waves of 128 A rows read fewer LDS bytes
-// per operation than waves of 64. Two tile shapes, one workgroup of four waves (one per SIMD, 2 x 2) each:
-//  * BN = 256: 256 x 256 tiles, waves of 128 x 128 = 8 x 8 instructions per step, the 256 accumulators per
-//    lane in the accumulation registers. A 256 x 256 tile moves 48 KB of operands (16 KB of compressed A
-//    values, 32 KB of dense B rows) into LDS per 128-position step for 16.8 M dense-equivalent operations, 25%
-//    fewer L2 -> LDS bytes per operation than 256 x 128. LDS: a ring of three 48 KB stages and the 16 KB
-//    index-word slot (160 KB), so one workgroup per CU; A fragments double-buffered in registers.
-//  * BN = 128: 256 x 128 tiles, waves of 128 x 64 = 8 x 4 instructions per step (128 accumulators per lane,
-//    245 registers in all); a ring of two 32 KB stages and the index-word slot (80 KB), so two workgroups
-//    share a CU and the prologue and epilogue of one overlap the other's instructions. A fragments refilled
-//    right after their last use (the step's last column). For problems with more than one such tile per CU
+// per operation than waves of 64. Waves are 128 A rows tall, two along A and W / 2 along B; three forms:
+//  * BN = 256 (256 x 256 tiles): a 256 x 256 tile moves 48 KB of operands (16 KB of compressed A values,
+//    32 KB of dense B rows) into LDS per 128-position step for 16.8 M dense-equivalent operations, 25% fewer
+//    L2 -> LDS bytes per operation than 256 x 128. LDS: a ring of three 48 KB stages and the 16 KB
+//    index-word slot (160 KB), so one workgroup per CU. Two wave layouts:
+//    - W = 4 (one wave per SIMD): waves of 128 x 128 = 8 x 8 instructions per step, the 256 accumulators
+//      per lane in the accumulation registers, A fragments double-buffered in registers. The fewest LDS
+//      bytes read per operation; taken for long reductions.
+//    - W = 8 (two waves per SIMD): waves of 128 x 64 = 8 x 4 instructions per step (243 registers). A third
+//      more LDS bytes read per step, but one wave's waits in the prologue and epilogue overlap the other's
+//      work, which pays where those are a large share of a tile (short reductions).
+//  * BN = 128, W = 4: 256 x 128 tiles, waves of 128 x 64 (128 accumulators per lane, 245 registers in all); a
+//    ring of two 32 KB stages and the index-word slot (80 KB), so two workgroups share a CU and the prologue
+//    and epilogue of one overlap the other's instructions. For problems with more than one such tile per CU
 //    but too few 256 x 256 tiles to keep every CU busy.
+// Waves of 128 x 64 refill their A fragments right after their last use (the step's last column).
 // LDS stages are filled by LDS DMA (buffer loads into LDS, 1 KB per wave instruction; B rows swizzled so
 // fragment reads are conflict-free); the index-word slot holds the current 4-step group's index words (the
 // tiled layout's metadata block of each of the 16 row blocks, brought in by DMA one group ahead and read into
@@ -45,29 +50,31 @@ using tiled::swz;
 using tiled::v4i;
 #define SS_LDS __attribute__((address_space(3)))
 
-constexpr int BM = 256, NW = 4, WGN = 2, TI = 8;  // A rows per tile, waves, waves along B, A blocks per wave
-constexpr int RBT = BM / 16;                      // row blocks of the sparse operand per tile
-constexpr int PA = RBT / NW;                      // A loads per wave per step (1 KB each)
-constexpr int A_BYTES = BM * 64;                  // 16 KB of compressed A values per step
-constexpr int NSC = 2;                            // scale loads per wave (A rows, B rows)
-constexpr int TJMAX = 8;
+constexpr int BM = 256, TI = 8;  // A rows per tile, A blocks per wave (waves are 128 A rows tall, two along A)
+constexpr int RBT = BM / 16;     // row blocks of the sparse operand per tile
+constexpr int A_BYTES = BM * 64; // 16 KB of compressed A values per step
+constexpr int NSC = 2;           // scale loads per wave (A rows, B rows)
+constexpr int TJMAX = 8, PAMAX = 4;
 
-template <int BN> struct Shape {
-  static constexpr int TJ = BN / 32;              // B blocks per wave: 8 x TJ instructions per step
+// BN: tile width along B; W: waves per workgroup (2 along A, W / 2 along B)
+template <int BN, int W> struct Shape {
+  static constexpr int NW = W, WGN = W / 2;
+  static constexpr int TJ = BN / 16 / WGN;        // B blocks per wave: 8 x TJ instructions per step
+  static constexpr int PA = RBT / NW;             // A loads per wave per step (1 KB each)
   static constexpr int PB = BN / 8 / NW;          // B loads per wave per step (8 rows x 128 bytes each)
   static constexpr int LPW = PA + PB;
   static constexpr int STAGE = A_BYTES + BN * 128;
   static constexpr int S = BN == 256 ? 3 : 2;     // stages in the ring
   static constexpr int META = S * STAGE;          // index-word slot (then the epilogue scales)
-  static constexpr int OCC = BN == 256 ? 1 : 2;   // workgroups per CU
-  static constexpr bool ADB = BN == 256;          // A fragments double-buffered
-  static constexpr int SLOTS = BN == 256 ? 2 : 3; // loads per column
-  static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN && TJ <= TJMAX, "load split");
+  static constexpr bool ADB = TJ == 8;            // A fragments double-buffered
+  static constexpr int SLOTS = ADB ? 2 : 3;       // loads per column
+  static_assert(PA * NW * 16 == BM && PB * NW * 8 == BN && TJ <= TJMAX && PA <= PAMAX, "load split");
   static_assert((BM + BN) * 4 <= 8 * 1024, "the epilogue scales fit the index-word slot");
 };
+template <int BN> constexpr int occupancy() { return BN == 256 ? 1 : 2; }  // workgroups per CU
 template <int AB> constexpr int meta_slot() { return RBT * Meta<AB>::BLOCK; }    // 16 KB / 8 KB
-template <int AB> constexpr int mpw() { return meta_slot<AB>() / 1024 / NW; }   // meta loads per wave
-template <int BN, int AB> constexpr int lds_bytes() { return Shape<BN>::META + meta_slot<AB>(); }
+template <int AB, int NW> constexpr int mpw() { return meta_slot<AB>() / 1024 / NW; }   // meta loads per wave
+template <int BN, int W, int AB> constexpr int lds_bytes() { return Shape<BN, W>::META + meta_slot<AB>(); }
 constexpr int up_rows(int tj, int cap) { return tj > cap && tj > 1 ? up_rows(tj / 2, cap) : tj; }
 
 constexpr int vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }  // s_waitcnt vmcnt(n)
@@ -79,17 +86,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 
 // (arrays that the loads index have fixed lengths: a length that depends on a template parameter in these
 // calls drops the kernel's host launch stub without a diagnostic)
-template <int BN, int AB, int YT, bool SX, int GR>
-__global__ __launch_bounds__(64 * NW, Shape<BN>::OCC) void wide_kernel(
+template <int BN, int W, int AB, int YT, bool SX, int GR>
+__global__ __launch_bounds__(64 * W, occupancy<BN>()) void wide_kernel(
     int R, int C, int KS, const uint8_t* __restrict__ tv, const uint8_t* __restrict__ tm, const uint8_t* __restrict__ bd,
     int ldb, const float* __restrict__ sx, const float* __restrict__ sw, void* __restrict__ Y, int ldy, int tiles_r,
     int tiles_c) {
-  using SH = Shape<BN>;
-  constexpr int TJ = SH::TJ, PB = SH::PB, LPW = SH::LPW, STAGE = SH::STAGE, S = SH::S, META = SH::META;
+  using SH = Shape<BN, W>;
+  constexpr int TJ = SH::TJ, PA = SH::PA, PB = SH::PB, LPW = SH::LPW, STAGE = SH::STAGE, S = SH::S, META = SH::META;
+  constexpr int NW = SH::NW, WGN = SH::WGN;
   using Acc = typename Mma<AB>::Acc;
   using MT = Meta<AB>;
   using MV = typename MT::V;
-  constexpr int MPW = mpw<AB>();
+  constexpr int MPW = mpw<AB, NW>();
   extern __shared__ __align__(16) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(64 * NW, Shape<BN>::OCC) void wide_kernel(
   const uint32_t l16 = lane * 16;
   const uint32_t nA = (uint32_t)nrb * (uint32_t)KSP * 1024u, nB = (uint32_t)C * (uint32_t)ldb,
                  nM = (uint32_t)nrb * (uint32_t)KS4 * (uint32_t)MT::BLOCK;
-  uint32_t sA[PA];  // uniform: byte offset of A row block q of this wave
+  uint32_t sA[PAMAX];  // PA of them, uniform: byte offset of A row block q of this wave
 #pragma unroll
   for (int q = 0; q < PA; ++q)
     sA[q] = __builtin_amdgcn_readfirstlane((uint32_t)min(r0 / 16 + wave + q * NW, nrb - 1) * (uint32_t)KSP * 1024u);
@@ -177,11 +185,11 @@ __global__ __launch_bounds__(64 * NW, Shape<BN>::OCC) void wide_kernel(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(tm, nM), (SS_LDS void*)((SS_LDS uint8_t*)smem + META + (wave + NW * i) * 1024),
                                              16, om[i], g * MBLK, 0, 0);
   };
-  // A rows r0 + 64 wave + lane; B rows c0 + 64 (wave % (BN / 64)) + lane (with BN = 128, waves 2 and 3 bring the
-  // same bytes as waves 0 and 1)
+  // A rows r0 + 64 (wave % 4) + lane; B rows c0 + 64 (wave % (BN / 64)) + lane (waves past the rows' count
+  // bring the same bytes as the first ones)
   auto scale_one = [&](int i) {
     // a missing scale vector loads junk from a valid address (never used), so the count stays fixed
-    const int wb = i == 0 ? wave : wave % (BN / 64);
+    const int wb = i == 0 ? wave % (BM / 64) : wave % (BN / 64);
     const int e = wb * 64 + lane;
     const float* s = i == 0 ? (sa ? sa + min(r0 + e, R - 1) : reinterpret_cast<const float*>(tm) + lane)
                             : (sb ? sb + min(c0 + e, C - 1) : reinterpret_cast<const float*>(tm) + lane);
@@ -504,42 +512,48 @@ __global__ __launch_bounds__(64 * NW, Shape<BN>::OCC) void wide_kernel(
   }
 }
 
-template <int BN, int AB, int YT, bool SX, int GR = 8>
+template <int BN, int W, int AB, int YT, bool SX, int GR = 8>
 hipError_t launch(int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb, const float* sx,
                   const float* sw, void* Y, int ldy, hipStream_t st) {
-  auto kern = wide_kernel<BN, AB, YT, SX, GR>;
-  constexpr int lds = lds_bytes<BN, AB>();
+  auto kern = wide_kernel<BN, W, AB, YT, SX, GR>;
+  constexpr int lds = lds_bytes<BN, W, AB>();
   const hipError_t e = lds_limit((const void*)kern, lds);
   if (e != hipSuccess) return e;
   const int tr = (R + BM - 1) / BM, tc = (C + BN - 1) / BN;
-  hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * NW), lds, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, tr, tc);
+  hipLaunchKernelGGL(kern, dim3(tr * tc), dim3(64 * W), lds, st, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, tr, tc);
   return hipGetLastError();
 }
 
-template <int BN, bool SX>
+template <int BN, int W, bool SX>
 hipError_t launch_bn(int ab, int yt, int R, int C, int KS, const uint8_t* tv, const uint8_t* tm, const uint8_t* bd, int ldb,
                      const float* sx, const float* sw, void* Y, int ldy, hipStream_t st) {
   if (ab == 0) {
-    if (yt == 0) return launch<BN, 0, 0, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-    if (yt == 1) return launch<BN, 0, 1, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-    return launch<BN, 0, 2, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 0) return launch<BN, W, 0, 0, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 1) return launch<BN, W, 0, 1, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    return launch<BN, W, 0, 2, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
   }
   if (ab == 1) {
-    if (yt == 0) return launch<BN, 1, 0, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-    return launch<BN, 1, 1, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    if (yt == 0) return launch<BN, W, 1, 0, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+    return launch<BN, W, 1, 1, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
   }
-  if (yt == 0) return launch<BN, 2, 0, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-  return launch<BN, 2, 1, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  if (yt == 0) return launch<BN, W, 2, 0, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  return launch<BN, W, 2, 1, SX>(R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
 }
 
 }  // namespace wide
 
+// 256 x 256 tiles take eight waves up to this many steps of the reduction, four beyond: on Llama-shaped FP8
+// layers at 16384 tokens eight waves were 1.02x on qkv and o and 1.005-1.02x on gate_up (32 steps), 0.97x on
+// down (112 steps).
+constexpr int kWide8MaxSteps = 64;
+
 hipError_t launch_spgemm_wide(int bn, bool side_x, int ab, int yt, int R, int C, int KS, const uint8_t* tv,
                               const uint8_t* tm, const uint8_t* bd, int ldb, const float* sx, const float* sw, void* Y,
                               int ldy, hipStream_t st) {
-  if (side_x) return wide::launch_bn<128, true>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
-  return bn == 256 ? wide::launch_bn<256, false>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st)
-                   : wide::launch_bn<128, false>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  if (side_x) return wide::launch_bn<128, 4, true>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  if (bn != 256) return wide::launch_bn<128, 4, false>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
+  return KS <= kWide8MaxSteps ? wide::launch_bn<256, 8, false>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st)
+                              : wide::launch_bn<256, 4, false>(ab, yt, R, C, KS, tv, tm, bd, ldb, sx, sw, Y, ldy, st);
 }
 
 }  // namespace ss

@@ -50,8 +50,9 @@ hipError_t launch_spgemm_tiled(bool side_x, int ab, int yt, int64_t R, int64_t C
                                void* Y, int64_t ldy, void* ws, hipStream_t st);
 int64_t spgemm_tiled_workspace_bytes(bool side_x, int ab, int64_t R, int64_t C, int64_t Kc);
 // The prefill kernel of k_spgemm_wide.hip with 256 x bn tiles (bn = 256: one workgroup per CU, weight-sparse
-// side only; bn = 128: two); R = rows of the sparse operand, C = rows of the dense one, KS = steps of 64 value
-// bytes, ldb in bytes; launch_spgemm_tiled routes the larger prefill problems to it.
+// side only, eight waves for reductions of at most 64 steps and four beyond; bn = 128: two workgroups of four
+// waves); R = rows of the sparse operand, C = rows of the dense one, KS = steps of 64 value bytes, ldb in
+// bytes; launch_spgemm_tiled routes the larger prefill problems to it.
 hipError_t launch_spgemm_wide(int bn, bool side_x, int ab, int yt, int R, int C, int KS, const uint8_t* tv,
                               const uint8_t* tm, const uint8_t* bd, int ldb, const float* sx, const float* sw, void* Y,
                               int ldy, hipStream_t st);
