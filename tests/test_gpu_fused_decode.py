@@ -58,6 +58,47 @@ def test_fused_matches_two_calls_and_oracle(ss, case, q):
         assert rel_fro(bf16_to_f64(host(Yf)), bf16_to_f64(exp)) <= 1e-2
 
 
+# (M, N, K, n, q): more row blocks than twice the CUs, so the persistent kernel hands every workgroup two or
+# more of them whatever its per-CU count: Qwen2.5-7B gate_up with a ragged last block (small LDS, two
+# workgroups a CU, 2368 blocks), four tokens at K = 12000 (about 80 KB of LDS, one workgroup a CU, 563 blocks),
+# 6:8 from bf16 (no staging row, 1250 blocks)
+MANY_BLOCKS = [(1, 37885, 3584, 3, "i8"), (4, 9000, 12000, 3, "fp8"), (3, 20000, 4096, 4, "i8")]
+
+
+@pytest.mark.parametrize("case", MANY_BLOCKS)
+def test_fused_row_blocks_past_the_grid(ss, case):
+    """Workgroups that run a second and later row block reuse their LDS codes, reduction slots and scale
+    registers: the whole output equals the two calls bit for bit (the row-block kernel there runs one block a
+    workgroup), and sampled channels, including row blocks past the first pass of the grid and the ragged
+    last block, equal the oracle (INT8 bit-exact, FP8 within 1e-2)."""
+    import torch
+    M, N, K, n, q = case
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nrb = -(-N // 16)
+    assert nrb > 2 * cus, "the case must give every workgroup more than one row block"
+    X, W, _ = synth.workload(M * 7 + N + K + n, M, N, K)
+    xd = _dev_rows(X, "bf16")
+    tv, tm, sw = ss.slide_decompose_tiled(_dev_rows(W, "f32"), n, q)
+    Kc = ss.lifted_k(K, n)
+    Yf = ss.quant_lift_spgemm_decode(xd, n, tv, tm, sw, N, q, "bf16")
+    xq, sx = ss.quant_lift_act(xd, n, q)
+    Y2 = ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, xq, sx, sw, "bf16")
+    assert torch.equal(Yf.view(torch.int16), Y2.view(torch.int16))
+    rng = np.random.default_rng(N)
+    later = [g * 16 + r for g in (cus, 2 * cus, 2 * cus + 1, nrb - 2) for r in (0, 7, 15)]
+    chans = np.unique(np.concatenate([np.arange(16), np.arange(N - 48, N), np.asarray(later),
+                                      rng.choice(N, 160, replace=False)]))
+    chans = chans[chans < N]
+    ov, om, osw = oracle.slide_decompose(np.ascontiguousarray(W[chans]), n, q)
+    oq, osx = oracle.quant_lift_act(X, n, q)
+    exp = oracle.spgemm("W", ov, om, oq, Kc, q, osx, osw, "bf16")
+    got = host(Yf)[:, chans]
+    if q == "i8":
+        assert np.array_equal(got, exp)
+    else:
+        assert rel_fro(bf16_to_f64(got), bf16_to_f64(exp)) <= 1e-2
+
+
 @pytest.mark.parametrize("y", ["f32", "i32"])
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 def test_fused_output_types_and_f32_input(ss, kind, y):
