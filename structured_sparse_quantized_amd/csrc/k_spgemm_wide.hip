@@ -457,13 +457,31 @@ __global__ __launch_bounds__(64 * W, occupancy<BN>()) void wide_kernel(
           }
         }
         __builtin_amdgcn_wave_barrier();
+        const int ar0 = r0 + (wm * TI + p * RX) * 16, bc0 = c0 + wn * TJ * 16;
+        if (vec && ar0 + 16 * RX <= R && bc0 + 16 * TJ <= C) {
+          // the pass's rows lie inside Y: every LDS read first, then every store
+          constexpr int IT = 16 * RX * CPR / 64;
+          v4i v[IT];
+  #pragma unroll
+          for (int k = 0; k < IT; ++k) {
+            const int i = lane + 64 * k;
+            v[k] = *reinterpret_cast<const SS_LDS v4i*>(stg + (i / CPR) * STRIDE + (i % CPR) * 16);
+          }
+  #pragma unroll
+          for (int k = 0; k < IT; ++k) {
+            const int i = lane + 64 * k;
+            __builtin_nontemporal_store(
+                v[k], reinterpret_cast<v4i*>(Yb + ((int64_t)(ar0 + i / CPR) * ldy + bc0 + (i % CPR) * (16 / EB)) * EB));
+          }
+        } else {
   #pragma unroll 4
-        for (int i = lane; i < 16 * RX * CPR; i += 64) {
-          const int row = i / CPR, ch = i % CPR;
-          const v4i v = *reinterpret_cast<const SS_LDS v4i*>(stg + row * STRIDE + ch * 16);
-          const int ar = r0 + (wm * TI + p * RX) * 16 + row;
-          if (ar >= R) continue;
-          put(v, ar, c0 + wn * TJ * 16 + ch * (16 / EB), C);
+          for (int i = lane; i < 16 * RX * CPR; i += 64) {
+            const int row = i / CPR, ch = i % CPR;
+            const v4i v = *reinterpret_cast<const SS_LDS v4i*>(stg + row * STRIDE + ch * 16);
+            const int ar = ar0 + row;
+            if (ar >= R) continue;
+            put(v, ar, bc0 + ch * (16 / EB), C);
+          }
         }
         __builtin_amdgcn_wave_barrier();
       }
@@ -499,13 +517,32 @@ __global__ __launch_bounds__(64 * W, occupancy<BN>()) void wide_kernel(
         }
       }
       __builtin_amdgcn_wave_barrier();
+      const int bc0 = c0 + (wn * TJ + p * UP) * 16, ar0 = r0 + wm * TI * 16;
+      if (vec && bc0 + RP <= C && ar0 + 128 <= R) {
+        // the pass's rows lie inside Y: every LDS read first, then every store (one read in flight at a time
+        // would leave each wave waiting out the LDS latency once per 16-byte piece)
+        constexpr int IT = RP * CPR / 64;
+        v4i v[IT];
+  #pragma unroll
+        for (int k = 0; k < IT; ++k) {
+          const int i = lane + 64 * k;
+          v[k] = *reinterpret_cast<const SS_LDS v4i*>(stg + (i / CPR) * STRIDE + (i % CPR) * 16);
+        }
+  #pragma unroll
+        for (int k = 0; k < IT; ++k) {
+          const int i = lane + 64 * k;
+          __builtin_nontemporal_store(
+              v[k], reinterpret_cast<v4i*>(Yb + ((int64_t)(bc0 + i / CPR) * ldy + ar0 + (i % CPR) * (16 / EB)) * EB));
+        }
+      } else {
   #pragma unroll 4
-      for (int i = lane; i < RP * CPR; i += 64) {
-        const int row = i / CPR, ch = i % CPR;
-        const v4i v = *reinterpret_cast<const SS_LDS v4i*>(stg + row * STRIDE + ch * 16);
-        const int bc = c0 + (wn * TJ + p * UP) * 16 + row;
-        if (bc >= C) continue;
-        put(v, bc, r0 + wm * TI * 16 + ch * (16 / EB), R);
+        for (int i = lane; i < RP * CPR; i += 64) {
+          const int row = i / CPR, ch = i % CPR;
+          const v4i v = *reinterpret_cast<const SS_LDS v4i*>(stg + row * STRIDE + ch * 16);
+          const int bc = bc0 + row;
+          if (bc >= C) continue;
+          put(v, bc, ar0 + ch * (16 / EB), R);
+        }
       }
       __builtin_amdgcn_wave_barrier();
     }
