@@ -1097,7 +1097,8 @@ static bool few_tokens(bool side_x, int64_t R, int64_t C) {
 }
 // The wide-wave prefill kernel (k_spgemm_wide.hip) on the weight-sparse side: 256 x 256 tiles wherever they
 // still give every CU four or more (measured 1.07-1.3x this file's 256 x 128 kernel on the Llama-shaped layers
-// at 16384 tokens and on gate_up at 4096), else its 256 x 128 form with two workgroups per CU wherever that
+// at 16384 tokens and on gate_up at 4096) or, for reductions longer than 64 steps, 0.6 of one or more (below),
+// else its 256 x 128 form with two workgroups per CU wherever that
 // gives a CU more than one tile (1.06-1.34x this file's kernel from 384 to 900 tiles on those layers at 512-8192
 // tokens; with one tile per CU or fewer, this file's eight waves per tile win). Its buffer loads take 32-bit
 // offsets, so each operand stays below 2 GB. The sparse-activation side takes the 256 x 128 form under the
@@ -1106,8 +1107,13 @@ static bool few_tokens(bool side_x, int64_t R, int64_t C) {
 static int wide_bn(bool side_x, int64_t R, int64_t C, int64_t KS, int64_t ldb_bytes) {
   const int64_t sparse_bytes = (R + 15) / 16 * ((KS + 3) / 4 * 4) * 1024, dense_bytes = C * ldb_bytes;
   if (sparse_bytes >= (INT64_C(1) << 31) || dense_bytes >= (INT64_C(1) << 31)) return 0;
-  const int64_t cus = num_cus_p();
-  if (!side_x && ((R + 255) / 256) * ((C + 255) / 256) >= 4 * cus) return 256;
+  const int64_t cus = num_cus_p(), t256 = ((R + 255) / 256) * ((C + 255) / 256);
+  if (!side_x && t256 >= 4 * cus) return 256;
+  // Reductions longer than 64 steps amortise a tile's prologue and epilogue, so 256 x 256 tiles pay from
+  // 0.6 of a tile per CU on: against the 256 x 128 form, Llama-shaped down (K = 14336, 2:4 and 6:8) measured
+  // 1.07-1.09x at 2560-3072 tokens, 1.07-1.27x at 4096, 1.19-1.26x at 6144-12288, the Qwen-shaped 4:6 and
+  // 8:10 down at 4096 tokens 1.10-1.12x; at half a tile per CU (2048 tokens) 0.88x.
+  if (!side_x && KS > 64 && 5 * t256 >= 3 * cus) return 256;
   if (((R + 255) / 256) * ((C + 127) / 128) > cus) return 128;
   return 0;
 }

@@ -152,15 +152,18 @@ def test_wide_kernel_sparse_activations_ragged(ss, q, y):
     assert_elementwise(g, e, sum_abs_terms(ov, om, ow, K, q, osw, osx).T, out=y)
 
 
-@pytest.mark.parametrize("shape", [(4000, 1280, 16484), (4000, 8960, 16484), (1500, 1280, 6000)],
-                         ids=["256x256-8waves", "256x256-4waves", "256x128"])
+@pytest.mark.parametrize("shape", [(4000, 1280, 16484), (4000, 8960, 16484), (1500, 1280, 6000), (3000, 8960, 4000),
+                                   (2300, 8960, 4000)],
+                         ids=["256x256-8waves", "256x256-4waves", "256x128", "256x256-4waves-long-k", "256x128-long-k"])
 @pytest.mark.parametrize("q", ["i8", "fp8", "bf16"])
 def test_wide_kernel_ragged(ss, q, shape):
     """Products routed to the wide-wave kernel, with ragged tiles on both sides and a reduction that ends inside
     a 4-step index group: N = 16484 channels and 4000 tokens take its 256 x 256 tiles (four or more per CU), with
     eight waves at K = 1280 (INT8 / FP8 10 steps of 128, bf16 20 steps of 64) and four at K = 8960 (70 and 140
     steps); N = 6000 and 1500 tokens at K = 1280 its 256 x 128 tiles with two workgroups per CU (288 such
-    tiles, 144 of 256 x 256)."""
+    tiles, 144 of 256 x 256). With a reduction over 64 steps (K = 8960) 256 x 256 tiles are taken from 0.6 of
+    one per CU: N = 4000 and 3000 tokens (192 of them, four waves); N = 4000 and 2300 tokens (144, below that)
+    take the 256 x 128 form (288 tiles)."""
     import torch
     M, K, N = shape
     gen = torch.Generator(device="cuda")
