@@ -1097,9 +1097,9 @@ static bool few_tokens(bool side_x, int64_t R, int64_t C) {
 }
 // The wide-wave prefill kernel (k_spgemm_wide.hip) on the weight-sparse side: 256 x 256 tiles wherever they
 // still give every CU four or more (measured 1.07-1.3x this file's 256 x 128 kernel on the Llama-shaped layers
-// at 16384 tokens and on gate_up at 4096) or, for reductions longer than 64 steps, 0.6 of one or more (below),
-// else its 256 x 128 form with two workgroups per CU wherever that
-// gives a CU more than one tile (1.06-1.34x this file's kernel from 384 to 900 tiles on those layers at 512-8192
+// at 16384 tokens and on gate_up at 4096), for reductions longer than 64 steps from 0.6 of one per CU, and
+// from two per CU when they fill whole rounds of CUs (below), else its 256 x 128 form with two workgroups per
+// CU wherever that gives a CU more than one tile (1.06-1.34x this file's kernel from 384 to 900 tiles on those layers at 512-8192
 // tokens; with one tile per CU or fewer, this file's eight waves per tile win). Its buffer loads take 32-bit
 // offsets, so each operand stays below 2 GB. The sparse-activation side takes the 256 x 128 form under the
 // same rule (1.2x this file's kernel on an 8192 x 4096 x 4096 product). Returns the tile width, or 0 for this
@@ -1114,6 +1114,10 @@ static int wide_bn(bool side_x, int64_t R, int64_t C, int64_t KS, int64_t ldb_by
   // 1.07-1.09x at 2560-3072 tokens, 1.07-1.27x at 4096, 1.19-1.26x at 6144-12288, the Qwen-shaped 4:6 and
   // 8:10 down at 4096 tokens 1.10-1.12x; at half a tile per CU (2048 tokens) 0.88x.
   if (!side_x && KS > 64 && 5 * t256 >= 3 * cus) return 256;
+  // Shorter reductions: from two tiles per CU when the last round of tiles fills 90% of the CUs or more
+  // (o and qkv at 8192 and 12288 tokens, 512-768 tiles: 1.017-1.037x the 256 x 128 form, the 6:8 o at 8192
+  // tokens 1.03x; gate_up at 2048 tokens, 896 tiles, 0.98x).
+  if (!side_x && t256 >= 2 * cus && 10 * t256 >= 9 * ((t256 + cus - 1) / cus) * cus) return 256;
   if (((R + 255) / 256) * ((C + 127) / 128) > cus) return 128;
   return 0;
 }
