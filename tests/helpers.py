@@ -80,3 +80,22 @@ def assert_elementwise(got, exp, terms, out="bf16", c=4e-5):
     bad = np.abs(got - exp) > bound
     assert not bad.any(), (f"{int(bad.sum())} of {bad.size} elements outside c*sum|terms| + rounding; worst ratio "
                            f"{float(np.max(np.abs(got - exp) / bound)):.3g}")
+
+
+def assert_product(got, exp, side, sp_vals, sp_meta, dense_codes, Kc, ab, sx, sw, out, tol=1e-2):
+    """A sparse product against the oracle's: INT8 bit for bit; FP8 / bf16 within `tol` relative Frobenius
+    error and element by element within assert_elementwise's bound (side "W": the sparse operand holds the
+    N weight rows and the dense one the M tokens; side "X" the other way round)."""
+    if ab == "i8":
+        assert np.array_equal(got, exp), out
+        return
+    if out == "bf16":
+        g, e = bf16_to_f64(got), bf16_to_f64(exp)
+    else:
+        g, e = np.asarray(got, np.float64), np.asarray(exp, np.float64)
+    assert rel_fro(g, e) <= tol
+    if side == "W":
+        terms = sum_abs_terms(sp_vals, sp_meta, dense_codes, Kc, ab, sx, sw)
+    else:
+        terms = sum_abs_terms(sp_vals, sp_meta, dense_codes, Kc, ab, sw, sx).T
+    assert_elementwise(g, e, terms, out=out)

@@ -7,13 +7,15 @@ attention it serves (deep reading of arXiv 2610.28947, introduction: either oper
   operand's rows run along the reduction).
 
 Batched results equal one ss_spgemm_tiled call per problem bit for bit; the attention roles match the CPU
-oracle (its 2:4 prune and product applied per head) within 1e-2 relative Frobenius error for bf16."""
+oracle (its 2:4 prune and product applied per head) within 1e-2 relative Frobenius error for bf16 and,
+element by element, within 4e-5 sum|terms| plus one output rounding."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from helpers import bf16_to_f64, dev_bf16, dev_codes, dev_f32, dev_u8, have_gpu, host, rel_fro
+from helpers import (assert_elementwise, bf16_to_f64, dev_bf16, dev_codes, dev_f32, dev_u8, have_gpu, host, rel_fro,
+                     sum_abs_terms)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
 
@@ -75,6 +77,7 @@ def test_qk_with_q_pruned_along_head_dim(ss, shape):
         vals, meta, _ = oracle.prune24_act(q[h], "bf16")
         exp = oracle.spgemm_acc("X", vals, meta, kd[h], Kc, "bf16")
         assert rel_fro(got[h], exp) <= 1e-2
+        assert_elementwise(got[h], exp, sum_abs_terms(vals, meta, kd[h], Kc, "bf16").T, out="f32")
 
 
 @pytest.mark.parametrize("shape", [(2, 256, 128), (3, 512, 128), (2, 1000, 64)])
@@ -102,6 +105,7 @@ def test_pv_with_probabilities_pruned_along_keys(ss, shape):
         vals, meta, _ = oracle.prune24_act(p[h], "bf16")
         exp = oracle.spgemm("X", vals, meta, vt[h], Kc, "bf16", None, None, "bf16")
         assert rel_fro(got[h], bf16_to_f64(exp)) <= 1e-2
+        assert_elementwise(got[h], bf16_to_f64(exp), sum_abs_terms(vals, meta, vt[h], Kc, "bf16").T, out="bf16")
 
 
 @pytest.mark.parametrize("shape", [(2, 256, 128), (3, 512, 64), (2, 1000, 128)])
@@ -127,6 +131,7 @@ def test_qk_with_k_pruned_along_head_dim(ss, shape):
         vals, meta, _ = oracle.prune24_act(k[h], "bf16")
         exp = oracle.spgemm_acc("W", vals, meta, qd[h], Kc, "bf16")
         assert rel_fro(got[h], exp) <= 1e-2
+        assert_elementwise(got[h], exp, sum_abs_terms(vals, meta, qd[h], Kc, "bf16"), out="f32")
 
 
 @pytest.mark.parametrize("shape", [(2, 256, 128), (3, 512, 64), (2, 768, 128)])
@@ -146,3 +151,4 @@ def test_pv_with_v_pruned_along_keys(ss, shape):
         vals, meta, _ = oracle.prune24_act(vt[h], "bf16")
         exp = oracle.spgemm("W", vals, meta, pd[h], Kc, "bf16", None, None, "bf16")
         assert rel_fro(got[h], bf16_to_f64(exp)) <= 1e-2
+        assert_elementwise(got[h], bf16_to_f64(exp), sum_abs_terms(vals, meta, pd[h], Kc, "bf16"), out="bf16")

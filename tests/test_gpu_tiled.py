@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import bf16_to_f64, dev_bf16, dev_codes, dev_f32, dev_u8, have_gpu, host, rel_fro
+from helpers import assert_product, dev_bf16, dev_codes, dev_f32, dev_u8, have_gpu, host
 from tiled_ref import tile_ref
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
@@ -107,12 +107,7 @@ def test_spgemm_tiled_against_oracle_operands(ss, side, ab, shape):
     for y in (["i32", "f32", "bf16"] if ab == "i8" else ["f32", "bf16"]):
         Y = host(ss.spgemm_tiled(s, M, N, Kc, tv, tm, d, dsx, dsw, y_dtype=y))
         exp = oracle.spgemm(side, vals, meta, dense, Kc, ab, sx, sw, y)
-        if ab == "i8":
-            assert np.array_equal(Y, exp), y
-        elif y == "bf16":
-            assert rel_fro(bf16_to_f64(Y), bf16_to_f64(exp)) <= TOL
-        else:
-            assert rel_fro(Y, exp) <= TOL
+        assert_product(Y, exp, side, vals, meta, dense, Kc, ab, sx, sw, y, TOL)
 
 
 def test_spgemm_tiled_output_leading_dim(ss):
@@ -144,10 +139,7 @@ def test_weight_sparse_path_tiled(ss, n, q):
     ov, om, osw = oracle.slide_decompose(W, n, q) if n > 2 else oracle.prune24(W, q)
     oxq, osx = oracle.quant_lift_act(X, n, q)
     exp = oracle.spgemm("W", ov, om, oxq, Kc, q, osx, osw, "bf16")
-    if q == "i8":
-        assert np.array_equal(Y, exp)
-    else:
-        assert rel_fro(bf16_to_f64(Y), bf16_to_f64(exp)) <= TOL
+    assert_product(Y, exp, "W", ov, om, oxq, Kc, q, osx, osw, "bf16", TOL)
 
 
 @pytest.mark.parametrize("out", ["i8", "fp8"])
@@ -161,10 +153,7 @@ def test_activation_sparse_path_tiled(ss, out):
     ov, om, osx = oracle.prune24_act(X, out)
     ow, osw = oracle.quant_lift_act(W, 2, out)
     exp = oracle.spgemm("X", ov, om, ow, K, out, osx, osw, "f32")
-    if out == "i8":
-        assert np.array_equal(Y, exp)
-    else:
-        assert rel_fro(Y, exp) <= TOL
+    assert_product(Y, exp, "X", ov, om, ow, K, out, osx, osw, "f32", TOL)
 
 
 def test_repeated_calls_and_streams(ss):
@@ -207,12 +196,7 @@ def test_spgemm_tiled_decode_tokens(ss, ab, shape, path):
         Y = host(ss.spgemm_tiled(ss.SS_SPARSE_W, M, N, Kc, tv, tm, d, dsx, dsw, y_dtype=y,
                                  workspace=None if path == "auto" else False))
         exp = oracle.spgemm("W", vals, meta, dense, Kc, ab, sx, sw, y)
-        if ab == "i8":
-            assert np.array_equal(Y, exp), y
-        elif y == "bf16":
-            assert rel_fro(bf16_to_f64(Y), bf16_to_f64(exp)) <= TOL
-        else:
-            assert rel_fro(Y, exp) <= TOL
+        assert_product(Y, exp, "W", vals, meta, dense, Kc, ab, sx, sw, y, TOL)
 
 
 def test_activation_sparse_path_tiled_bf16(ss):
@@ -225,7 +209,7 @@ def test_activation_sparse_path_tiled_bf16(ss):
     Y = host(ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, K, tv, tm, dev_bf16(wb), None, None, "f32"))
     ov, om, _ = oracle.prune24_act(X, "bf16")
     exp = oracle.spgemm("X", ov, om, wb, K, "bf16", None, None, "f32")
-    assert rel_fro(Y, exp) <= TOL
+    assert_product(Y, exp, "X", ov, om, wb, K, "bf16", None, None, "f32", TOL)
 
 
 # K = 4096 / 6000 / 18944 hold one / two / no groups per wave in registers (8-bit codes); K = 100 and 1004
@@ -280,7 +264,7 @@ def test_activation_sparse_layer_one_pass(ss, out):
         ow, osw = oracle.quant_lift_act(W, 2, out)
     Y = host(ss.spgemm_tiled(ss.SS_SPARSE_X, M, N, K, tv, tm, wd, sx, sw, "f32"))
     exp = oracle.spgemm("X", ov, om, ow, K, out, osx, osw, "f32")
-    assert rel_fro(Y, exp) <= TOL
+    assert_product(Y, exp, "X", ov, om, ow, K, out, osx, osw, "f32", TOL)
 
 
 SLIDE_TILED_SHAPES = [(1, 8), (5, 40), (3, 1001), (16, 512), (130, 520), (257, 1000), (3, 18944), (2, 60000)]
