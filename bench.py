@@ -438,10 +438,13 @@ def main(argv=None):
     if not args.no_suite:
         extra = layer_rows(ss, torch, dev, gen, args, detail)
         out.update(extra)
-        suite(ss, torch, dev, gen, detail)
+        suite(ss, torch, dev, gen, detail, check=not args.no_cpu)
     out["cpu_baseline"] = cpu
     out["parity_vs_oracle"] = None if parity is None else {
         k: parity[k] for k in ("ok", "codes_bit_exact", "max_rel_fro", "max_elem_over_bound", "sample")}
+    if parity is not None:
+        checked = _parity_checks({k: v for k, v in detail.items() if k != "parity_vs_oracle"})
+        out["parity_vs_oracle"]["other_rows"] = f"{sum(checked)} of {len(checked)} sampled checks ok"
     if args.detail:
         try:
             os.makedirs(os.path.dirname(args.detail), exist_ok=True)
@@ -470,7 +473,7 @@ def layer_rows(ss, torch, dev, gen, args, detail):
     res = {}
     for (n, q, M) in ((2, "fp8", 4096), (4, "i8", 4096), (4, "fp8", 4096), (4, "i8", 16384), (4, "fp8", 16384)):
         log(f"[bench] layer n={n} {q} M={M}")
-        lay = Layer(ss, torch, dev, gen, M, n, q, NBUF)
+        lay = Layer(ss, torch, dev, gen, M, n, q, NBUF, keep_w=not args.no_cpu)
         sc = [lay.calls(b) for b in range(NBUF)]
         dc = [lay.dense_calls(b) for b in range(NBUF)]
         ms, _ = time_steps(torch, sc, args.steps, 2)
@@ -484,14 +487,16 @@ def layer_rows(ss, torch, dev, gen, args, detail):
         speed = None if msd is None else msd / ms
         theo = n / (n - 1)
         key = f"{'24' if n == 2 else '68'}_{q}_{M}"
+        par = None if args.no_cpu else layer_parity(torch, lay, n, q)
         detail[f"layer_{key}"] = row(f"layer_{key}", pattern="2:4" if n == 2 else "6:8", q=q, tokens=M,
                                      ms_per_step=ms, dense_ms_per_step=msd, tokens_per_s=M / (ms * 1e-3),
                                      vs_dense=speed, efficiency=None if speed is None else speed / theo,
-                                     per_call_us=pc, gemm_frac=fr,
+                                     per_call_us=pc, gemm_frac=fr, parity_vs_oracle=par,
                                      dense_library="torch._int_mm (int32 out, no rescale)" if q == "i8" else
                                      "torch._scaled_mm (bf16 out)")
         res[f"l{key}"] = {"tps": round(M / (ms * 1e-3)), "vs_dense": None if speed is None else round(speed, 3),
-                          "gemm_frac_max": round(max(fr.values()), 3)}
+                          "gemm_frac_max": round(max(fr.values()), 3),
+                          "parity": None if par is None else all(v["ok"] for v in par.values())}
         del lay, sc, dc
         torch.cuda.empty_cache()
     return res
@@ -568,6 +573,96 @@ def cpu_leg(torch, lay, M, n_tok, n_ch, seed=7):
     return parity, cpu
 
 
+def sampled_parity(side, n, q, Kc, w_rows, x_rows, y_gpu, sx_gpu=None, sw_gpu=None, xq_gpu=None):
+    """The oracle on one benchmark row's own inputs, on a sample: ``w_rows`` the sampled output channels' float32
+    weights, ``x_rows`` the sampled tokens' bf16 bits, ``y_gpu`` the GPU's bf16 outputs at [tokens, channels],
+    and (when given) the GPU's scales and codes of the same rows. Side "W": weights pruned (2:4, or the
+    (2n-2):2n decomposition) and tokens quantised (+ lifted); side "X": tokens pruned 2:4 online, weights
+    quantised per channel. Scales and codes bit for bit; the product INT8 bit for bit, FP8 within 1e-2 relative
+    Frobenius error and element by element within 4e-5 sum|terms| + 2^-7 |y|."""
+    import numpy as np
+    import oracle
+    if side == "W":
+        ow = oracle.prune24(w_rows, q) if n == 2 else oracle.slide_decompose(w_rows, n, q)
+        ox = oracle.quant_lift_act(x_rows, n, q)
+        sp_v, sp_m, dense, s_sp, s_dn = ow[0], ow[1], ox[0], ow[2], ox[1]
+        y = oracle.spgemm("W", ow[0], ow[1], ox[0], Kc, q, ox[1], ow[2], "bf16")
+        codes = [(sx_gpu, ox[1]), (sw_gpu, ow[2]), (xq_gpu, None if xq_gpu is None else ox[0])]
+    else:
+        ox = oracle.prune24_act(x_rows, q)
+        ow = oracle.quant_lift_act(w_rows, 2, q)
+        sp_v, sp_m, dense, s_sp, s_dn = ox[0], ox[1], ow[0], ox[2], ow[1]
+        y = oracle.spgemm("X", ox[0], ox[1], ow[0], Kc, q, ox[2], ow[1], "bf16")
+        codes = [(sx_gpu, ox[2]), (sw_gpu, ow[1])]
+    codes_ok = True
+    for g, e in codes:
+        if g is None:
+            continue
+        g, e = np.asarray(g), np.asarray(e)
+        codes_ok &= bool(np.array_equal(g, e) if g.dtype == np.float32 else np.array_equal(g.view(np.uint8),
+                                                                                             e.view(np.uint8)))
+    yr, yv = _bf16(y), _bf16(y_gpu)
+    if q == "i8":
+        exact = bool(np.array_equal(np.asarray(y_gpu, np.uint16), np.asarray(y, np.uint16)))
+        return {"ok": bool(codes_ok and exact), "codes_bit_exact": bool(codes_ok), "product_bit_exact": exact,
+                "sample": f"{yr.shape[0]} tokens x {yr.shape[1]} channels"}
+    dec = oracle.e4m3_decode
+    a = np.abs(oracle.decompress24(dec(sp_v)[:, : Kc // 2], sp_m, Kc))
+    b = np.abs(dec(dense))[:, :Kc]
+    terms = (b @ a.T) * np.asarray(s_dn, np.float64)[:, None] * np.asarray(s_sp, np.float64)[None, :]
+    if side == "X":
+        terms = terms.T
+    den = np.linalg.norm(yr)
+    fro = float(np.linalg.norm(yv - yr) / (den if den > 0 else 1.0))
+    elem = float(np.max(np.abs(yv - yr) / np.maximum(4e-5 * terms + 2.0 ** -7 * np.abs(yr), 1e-30)))
+    return {"ok": bool(codes_ok and fro <= 1e-2 and elem <= 1.0), "codes_bit_exact": bool(codes_ok),
+            "max_rel_fro": fro, "max_elem_over_bound": elem, "sample": f"{yr.shape[0]} tokens x {yr.shape[1]} channels"}
+
+
+def _parity_checks(o):
+    """The ``ok`` of every sampled_parity result in the detail record (the headline's own is in cpu_leg)."""
+    found = []
+    if isinstance(o, dict):
+        for k, v in o.items():
+            if k == "parity_vs_oracle" and isinstance(v, dict):
+                found += [v["ok"]] if "ok" in v else [x["ok"] for x in v.values()]
+            elif k != "parity_vs_oracle":
+                found += _parity_checks(v)
+    elif isinstance(o, list):
+        for v in o:
+            found += _parity_checks(v)
+    return found
+
+
+def _pick(N, k, rng, edge=64):
+    """Sampled indices: the first and last ``edge`` (tile edges, the ragged end) and ``k`` random ones."""
+    import numpy as np
+    if N <= 2 * edge + k:
+        return np.arange(N)
+    mid = rng.choice(np.arange(edge, N - edge), k, replace=False)
+    return np.unique(np.concatenate([np.arange(edge), np.arange(N - edge, N), mid]))
+
+
+def layer_parity(torch, lay, n, q, seed=11):
+    """sampled_parity on each linear of a Layer (set 0 of its timed steps)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, L in lay.lin.items():
+        s = L["sets"][0]
+        toks = _pick(lay.M, 16, rng, edge=8)
+        chans = _pick(L["N"], 64, rng)
+        td = torch.from_numpy(toks).to(s["X"].device)
+        cd = torch.from_numpy(chans).to(s["X"].device)
+        out[name] = sampled_parity(
+            "W", n, q, L["Kc"], L["W"].index_select(0, cd).cpu().numpy(),
+            s["X"].index_select(0, td).view(torch.int16).cpu().numpy().view(np.uint16),
+            s["Y"].index_select(0, td).index_select(1, cd).view(torch.int16).cpu().numpy().view(np.uint16),
+            s["sx"].index_select(0, td).cpu().numpy(), L["sw"].index_select(0, cd).cpu().numpy(),
+            s["xq"].index_select(0, td).view(torch.uint8).cpu().numpy())
+    return out
+
+
 def _bf16(bits):
     import numpy as np
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -577,9 +672,12 @@ def _bf16(bits):
 # the other rows
 
 
-def suite(ss, torch, dev, gen, detail):
-    """Rows beyond the Llama layers (stderr + detail file)."""
+def suite(ss, torch, dev, gen, detail, check=True):
+    """Rows beyond the Llama layers (stderr + detail file); with ``check``, the Qwen-shaped and sparse-activation
+    rows also carry sampled_parity on their own inputs."""
+    import numpy as np
     import synth
+    rng = np.random.default_rng(13)
 
     def randn(shape, std=1.0, dtype=torch.float32):
         return (torch.randn(shape, generator=gen, device=dev) * std).to(dtype)
@@ -592,6 +690,9 @@ def suite(ss, torch, dev, gen, detail):
             W = randn((Nout, K), 0.02)
             tv, tm, sw = ss.slide_decompose_tiled(W, n, "i8")
             wq, swd = ss.quant_lift_act(W, 2, "i8")
+            chans = _pick(Nout, 64, rng)
+            cd = torch.from_numpy(chans).to(dev)
+            Wh = W.index_select(0, cd).cpu().numpy() if check else None
             del W
             Kc = ss.lifted_k(K, n)
             wbytes = tv.numel() + tm.numel() + 4 * Nout
@@ -627,6 +728,13 @@ def suite(ss, torch, dev, gen, detail):
                     sp = (t_dq + t_dn) / (t_q + t_sp)
                     r.update({"dense_gemm_us": t_dn, "vs_dense": sp, "efficiency": sp / (n / (n - 1)),
                               "gemm_vs_dense": t_dn / t_sp})
+                if check:
+                    td = torch.from_numpy(_pick(M, 16, rng, edge=8)).to(dev)
+                    r["parity_vs_oracle"] = sampled_parity(
+                        "W", n, "i8", Kc, Wh, X.index_select(0, td).view(torch.int16).cpu().numpy().view(np.uint16),
+                        Y.index_select(0, td).index_select(1, cd).view(torch.int16).cpu().numpy().view(np.uint16),
+                        sx.index_select(0, td).cpu().numpy(), sw.index_select(0, cd).cpu().numpy(),
+                        xq.index_select(0, td).view(torch.uint8).cpu().numpy())
                 if M <= 4:  # the same layer in one launch: quant+lift inside the few-token product
                     t_f = median_us(torch, [lambda o=o: ss.quant_lift_spgemm_decode(X, n, o[0], o[1], o[2], Nout, "i8",
                                                                                     "bf16", out=Y) for o in ops])
@@ -650,7 +758,8 @@ def suite(ss, torch, dev, gen, detail):
     M, K, Nout = 8192, 4096, 4096
     Xs = [randn((M, K), 1.0, torch.bfloat16)]
     Xs += [Xs[0].clone() for _ in range(rotation(2 * M * K) - 1)]
-    wq, swd = ss.quant_lift_act(randn((Nout, K), 0.02), 2, "fp8")
+    Wf = randn((Nout, K), 0.02)
+    wq, swd = ss.quant_lift_act(Wf, 2, "fp8")
     sx = torch.empty(M, dtype=torch.float32, device=dev)
     nv, nm = ss.tiled_bytes(M, K, "fp8")
     tv = torch.empty(nv, dtype=torch.uint8, device=dev)
@@ -659,6 +768,14 @@ def suite(ss, torch, dev, gen, detail):
     xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
     t_pr = median_us(torch, [lambda X=X: ss.prune24_act_tiled(X, "fp8", out=(tv, tm, sx)) for X in Xs])
     t_sp = median_us(torch, [lambda: ss.spgemm_tiled(ss.SS_SPARSE_X, M, Nout, K, tv, tm, wq, sx, swd, "bf16", out=Y)])
+    par = None
+    if check:  # before the dense comparator's quantiser rewrites sx
+        td = torch.from_numpy(_pick(M, 16, rng, edge=8)).to(dev)
+        cd = torch.from_numpy(_pick(Nout, 64, rng)).to(dev)
+        par = sampled_parity("X", 2, "fp8", K, Wf.index_select(0, cd).cpu().numpy(),
+                             Xs[0].index_select(0, td).view(torch.int16).cpu().numpy().view(np.uint16),
+                             Y.index_select(0, td).index_select(1, cd).view(torch.int16).cpu().numpy().view(np.uint16),
+                             sx.index_select(0, td).cpu().numpy(), swd.index_select(0, cd).cpu().numpy())
     t_q = median_us(torch, [lambda X=X: ss.quant_lift_act(X, 2, "fp8", out=(xq, sx)) for X in Xs])
     try:
         t_dn = median_us(torch, [lambda: torch._scaled_mm(xq, wq.t(), scale_a=sx[:, None], scale_b=swd[None, :],
@@ -671,8 +788,8 @@ def suite(ss, torch, dev, gen, detail):
         prune_frac=pb / t_pr / 1e3 / HBM_PEAK_GBS, sparse_gemm_us=t_sp,
         gemm_frac=product_ops(M, Nout, K) / t_sp / 1e6 / DENSE_PEAK_T["fp8"], dense_quant_us=t_q,
         dense_fp8_gemm_us=t_dn, vs_dense=None if t_dn is None else (t_q + t_dn) / (t_pr + t_sp),
-        input_copies=len(Xs))
-    del Xs, wq, swd, sx, tv, tm, Y, xq
+        input_copies=len(Xs), parity_vs_oracle=par)
+    del Xs, Wf, wq, swd, sx, tv, tm, Y, xq
     torch.cuda.empty_cache()
 
     # quant+lift bandwidth on 2048 and 16384 tokens (K = 4096), inputs rotated out of the Infinity Cache
