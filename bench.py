@@ -164,8 +164,46 @@ def median_us(torch, fns, min_ms=20.0, samples=5):
     return statistics.median(out)
 
 
-def rotation(nbytes, floor=2 * MALL_BYTES, cap=8):
-    """Buffer copies so that ``nbytes`` per copy add up to at least ``floor`` bytes."""
+def median_us_graph(torch, fns, calls=256, min_ms=20.0, samples=5):
+    """Per-call time (us) with the host out of the loop: ``calls`` calls (round robin over ``fns``) captured
+    once in a HIP graph, replayed back to back; the median of ``samples`` samples of at least ``min_ms``. For
+    calls of a few microseconds, where launching through Python takes longer than the kernel. The graph's
+    first replay is compared with the eager result by the caller (see graph_check)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fns[i % len(fns)]()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(min_ms / max(e0.elapsed_time(e1), 1e-3)))
+    out = []
+    for _ in range(samples):
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / (reps * calls) * 1e3)
+    del g
+    return statistics.median(out)
+
+
+def rotation(nbytes, floor=2 * MALL_BYTES, cap=64):
+    """Buffer copies so that ``nbytes`` per copy add up to at least ``floor`` bytes (twice the Infinity Cache:
+    a row whose working set fits the cache would time the cache, not HBM)."""
     return max(1, min(cap, math.ceil(floor / max(nbytes, 1))))
 
 
@@ -709,13 +747,21 @@ def suite(ss, torch, dev, gen, detail, check=True):
                 need = ss.spgemm_tiled_workspace_bytes(ss.SS_SPARSE_W, M, Nout, Kc, "i8")
                 ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else False
                 t_q = median_us(torch, [lambda: ss.quant_lift_act(X, n, "i8", out=(xq, sx))])
-                t_sp = median_us(torch, [lambda o=o: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, o[0], o[1], xq, sx,
-                                                                     o[2], "bf16", out=Y, workspace=ws) for o in ops])
+                spf = [lambda o=o: ss.spgemm_tiled(ss.SS_SPARSE_W, M, Nout, Kc, o[0], o[1], xq, sx, o[2], "bf16", out=Y,
+                                                   workspace=ws) for o in ops]
+                t_sp = median_us(torch, spf)
+                gr = {}
+                if M <= 64:  # few tokens: the kernels run for microseconds, so time them without the host too
+                    yref = Y.clone()
+                    gr["quant_lift_graph_us"] = median_us_graph(torch, [lambda: ss.quant_lift_act(X, n, "i8", out=(xq, sx))])
+                    gr["sparse_gemm_graph_us"] = median_us_graph(torch, spf)
+                    gr["graph_equals_eager"] = bool(torch.equal(Y.view(torch.int16), yref.view(torch.int16)))
+                    gr["weight_stream_graph_GBs"] = wbytes / gr["sparse_gemm_graph_us"] / 1e3
                 t_dq = median_us(torch, [lambda: ss.quant_lift_act(X, 2, "i8", out=(xd, sxd))])
                 r = {"pattern": f"{2 * n - 2}:{2 * n}", "layer": name, "M": M, "K": K, "K_prime": Kc, "N": Nout,
                      "quant_lift_us": t_q, "sparse_gemm_us": t_sp, "weight_copies": nrot,
                      "sparse_TOPS_dense_equiv": 2.0 * M * Nout * Kc / t_sp / 1e6,
-                     "weight_stream_GBs": wbytes / t_sp / 1e3, "dense_quant_us": t_dq}
+                     "weight_stream_GBs": wbytes / t_sp / 1e3, "dense_quant_us": t_dq, **gr}
                 if M > 16:  # hipBLASLt int8 needs M > 16 through torch._int_mm
                     try:
                         t_dn = median_us(torch, [lambda d=d: torch._int_mm(xd, d.t()) for d in dops])
@@ -736,9 +782,12 @@ def suite(ss, torch, dev, gen, detail, check=True):
                         sx.index_select(0, td).cpu().numpy(), sw.index_select(0, cd).cpu().numpy(),
                         xq.index_select(0, td).view(torch.uint8).cpu().numpy())
                 if M <= 4:  # the same layer in one launch: quant+lift inside the few-token product
-                    t_f = median_us(torch, [lambda o=o: ss.quant_lift_spgemm_decode(X, n, o[0], o[1], o[2], Nout, "i8",
-                                                                                    "bf16", out=Y) for o in ops])
-                    r.update({"fused_us": t_f, "fused_weight_stream_GBs": wbytes / t_f / 1e3})
+                    ff = [lambda o=o: ss.quant_lift_spgemm_decode(X, n, o[0], o[1], o[2], Nout, "i8", "bf16", out=Y)
+                          for o in ops]
+                    t_f = median_us(torch, ff)
+                    t_fg = median_us_graph(torch, ff)
+                    r.update({"fused_us": t_f, "fused_weight_stream_GBs": wbytes / t_f / 1e3, "fused_graph_us": t_fg,
+                              "fused_weight_stream_graph_GBs": wbytes / t_fg / 1e3})
                 tot.setdefault(M, [0.0, 0.0])
                 tot[M][0] += t_q + t_sp
                 tot[M][1] += (t_dq + t_dn) if t_dn is not None else float("nan")
@@ -802,9 +851,14 @@ def suite(ss, torch, dev, gen, detail, check=True):
             nr = rotation(byts)
             bufs = [(randn((M, K), 1.0, torch.bfloat16), torch.empty((M, Kc), dtype=torch.int8, device=dev),
                      torch.empty(M, dtype=torch.float32, device=dev)) for _ in range(nr)]
-            t = median_us(torch, [lambda b=b: ss.quant_lift_act(b[0], n, "i8", out=(b[1], b[2])) for b in bufs])
+            qf = [lambda b=b: ss.quant_lift_act(b[0], n, "i8", out=(b[1], b[2])) for b in bufs]
+            t = median_us(torch, qf)
+            gr = {}
+            if M <= 4096:  # a few microseconds per call: also timed without the host in the loop
+                tg = median_us_graph(torch, qf)
+                gr = {"graph_us": tg, "graph_GBs": byts / tg / 1e3, "graph_frac": byts / tg / 1e3 / HBM_PEAK_GBS}
             ql.append(row("quant_lift_int8", M=M, K=K, n=n, K_prime=Kc, us=t, GBs=byts / t / 1e3,
-                          frac=byts / t / 1e3 / HBM_PEAK_GBS, buffer_sets=nr, working_set_MB=nr * byts / 1e6))
+                          frac=byts / t / 1e3 / HBM_PEAK_GBS, buffer_sets=nr, working_set_MB=nr * byts / 1e6, **gr))
             del bufs
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)

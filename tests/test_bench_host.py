@@ -53,7 +53,7 @@ def test_rotation_covers_twice_the_infinity_cache():
     b = _bench()
     for nbytes in (1, 29_000_000, 100 << 20, 300 << 20, 1 << 30):
         k = b.rotation(nbytes)
-        assert k >= 1 and (k * nbytes >= 2 * b.MALL_BYTES or k == 8)
+        assert k >= 1 and (k * nbytes >= 2 * b.MALL_BYTES or k == 64)
         assert k == 1 or (k - 1) * nbytes < 2 * b.MALL_BYTES
 
 
