@@ -13,6 +13,7 @@
 #include "ss_kernels.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace ss {
 namespace {
@@ -206,6 +207,24 @@ __global__ __launch_bounds__(kBlock) void quant_lift_long_kernel(const TIn* __re
   }
 }
 
+// Workgroups of the persistent form that fit on one CU at once (registers and LDS), at most 8. The persistent
+// grid is that many per CU, so every workgroup is resident from the start: a grid larger than what fits
+// runs its last workgroups as a partly filled extra round.
+template <typename TIn, bool FP8, int N, int VPT>
+int resident_per_cu(size_t lds) {
+  static std::atomic<int64_t> cache{-1};  // (lds << 8) | count, for the last LDS size asked
+  const int64_t c = cache.load(std::memory_order_relaxed);
+  if (c >= 0 && (size_t)(c >> 8) == lds) return (int)(c & 0xFF);
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_lift_kernel<TIn, FP8, N, VPT, true>, kBlock, lds) !=
+          hipSuccess ||
+      n <= 0)
+    n = 1;
+  n = std::min(n, 8);
+  cache.store(((int64_t)lds << 8) | n, std::memory_order_relaxed);
+  return n;
+}
+
 template <typename TIn, bool FP8, int N>
 hipError_t launch_n(const TIn* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq, int64_t ldq, int64_t Kc, float* sx,
                     hipStream_t st) {
@@ -225,10 +244,9 @@ hipError_t launch_n(const TIn* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq
   // One row per workgroup keeps the most loads in flight for batches up to a few
   // thousand rows; larger batches use persistent workgroups that prefetch.
   const bool pipe = M > 16 * (int64_t)num_cus_p();
-  const unsigned grid = (unsigned)(pipe ? 8 * (int64_t)num_cus_p() : M);
   const int m = (int)M, k = (int)K, kc = (int)Kc;
 #define SS_QL(V_) \
-  do { if (pipe) hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, true>), dim3(grid), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); else hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, false>), dim3(grid), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); } while (0)
+  do { if (pipe) hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, true>), dim3((unsigned)(resident_per_cu<TIn, FP8, N, V_>(lds) * num_cus_p())), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); else hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, false>), dim3((unsigned)M), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); } while (0)
   if (vpt <= 1) SS_QL(1);
   else if (vpt <= 2) SS_QL(2);
   else if (vpt <= 4) SS_QL(4);
