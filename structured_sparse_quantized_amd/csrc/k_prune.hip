@@ -292,6 +292,9 @@ __global__ __launch_bounds__(512) void prune24_act_tiled_bf16_kernel(const uint1
 }
 
 
+// Persistent grids hold as many workgroups per CU as fit at once (registers; at most 8), so every workgroup
+// is resident from the start: a fixed 8 per CU ran the last ones as a partly filled extra round (the FP8
+// activation prune of 8192 x 4096 fits 7: 1.05x).
 template <typename TIn, int OUT>
 static hipError_t launch_p24_tiled(const TIn* X, int64_t ldx, int64_t M, int64_t K, int64_t Kc, uint8_t* tv,
                                    uint8_t* tm, float* sx, hipStream_t st) {
@@ -301,13 +304,15 @@ static hipError_t launch_p24_tiled(const TIn* X, int64_t ldx, int64_t M, int64_t
   const int64_t upt = (units + kBlock - 1) / kBlock;
   const int64_t rows = (M + 15) / 16 * 16;
   const bool pipe = rows > 16 * (int64_t)num_cus_p();
-  const unsigned grid = (unsigned)(pipe ? 8 * (int64_t)num_cus_p() : rows);
+  const unsigned grid = (unsigned)rows;
   const int m = (int)M, k = (int)K, kc = (int)Kc;
 #define SS_PT(U_)                                                                                                      \
   do {                                                                                                                 \
     if (pipe)                                                                                                          \
-      hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, true, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k,  \
-                         tv, (int64_t)KSP, tm, (int64_t)0, kc, sx);                                                    \
+      hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, true, true>),                                                   \
+                         dim3((unsigned)(std::min(occupancy_p((const void*)prune24_kernel<TIn, OUT, U_, true, true>,    \
+                                                              kBlock, 0), 8) * num_cus_p())),                         \
+                         dim3(kBlock), 0, st, X, ldx, m, k, tv, (int64_t)KSP, tm, (int64_t)0, kc, sx);                \
     else                                                                                                               \
       hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, false, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k, \
                          tv, (int64_t)KSP, tm, (int64_t)0, kc, sx);                                                    \
@@ -460,10 +465,9 @@ static hipError_t launch_out(const TIn* X, int64_t ldx, int64_t M, int64_t K, ui
     return hipGetLastError();
   }
   const bool pipe = M > 16 * (int64_t)num_cus_p();
-  const unsigned grid = (unsigned)(pipe ? 8 * (int64_t)num_cus_p() : M);
   const int m = (int)M, k = (int)K, kc = (int)Kc;
 #define SS_P(U_) \
-  do { if (pipe) hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, true>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k, v, ldv_bytes, meta, ldm, kc, scale); else hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, false>), dim3(grid), dim3(kBlock), 0, st, X, ldx, m, k, v, ldv_bytes, meta, ldm, kc, scale); } while (0)
+  do { if (pipe) hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, true>), dim3((unsigned)(std::min(occupancy_p((const void*)prune24_kernel<TIn, OUT, U_, true>, kBlock, 0), 8) * num_cus_p())), dim3(kBlock), 0, st, X, ldx, m, k, v, ldv_bytes, meta, ldm, kc, scale); else hipLaunchKernelGGL((prune24_kernel<TIn, OUT, U_, false>), dim3((unsigned)M), dim3(kBlock), 0, st, X, ldx, m, k, v, ldv_bytes, meta, ldm, kc, scale); } while (0)
   if (upt <= 1) SS_P(1);
   else if (upt <= 2) SS_P(2);
   else SS_P(4);

@@ -13,7 +13,6 @@
 #include "ss_kernels.h"
 
 #include <algorithm>
-#include <atomic>
 
 namespace ss {
 namespace {
@@ -207,24 +206,6 @@ __global__ __launch_bounds__(kBlock) void quant_lift_long_kernel(const TIn* __re
   }
 }
 
-// Workgroups of the persistent form that fit on one CU at once (registers and LDS), at most 8. The persistent
-// grid is that many per CU, so every workgroup is resident from the start: a grid larger than what fits
-// runs its last workgroups as a partly filled extra round.
-template <typename TIn, bool FP8, int N, int VPT>
-int resident_per_cu(size_t lds) {
-  static std::atomic<int64_t> cache{-1};  // (lds << 8) | count, for the last LDS size asked
-  const int64_t c = cache.load(std::memory_order_relaxed);
-  if (c >= 0 && (size_t)(c >> 8) == lds) return (int)(c & 0xFF);
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, quant_lift_kernel<TIn, FP8, N, VPT, true>, kBlock, lds) !=
-          hipSuccess ||
-      n <= 0)
-    n = 1;
-  n = std::min(n, 8);
-  cache.store(((int64_t)lds << 8) | n, std::memory_order_relaxed);
-  return n;
-}
-
 template <typename TIn, bool FP8, int N>
 hipError_t launch_n(const TIn* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq, int64_t ldq, int64_t Kc, float* sx,
                     hipStream_t st) {
@@ -242,11 +223,13 @@ hipError_t launch_n(const TIn* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Xq
     return hipGetLastError();
   }
   // One row per workgroup keeps the most loads in flight for batches up to a few
-  // thousand rows; larger batches use persistent workgroups that prefetch.
+  // thousand rows; larger batches use persistent workgroups that prefetch, as many per CU as fit at once
+  // (registers and LDS; at most 8): a grid larger than what fits runs its last workgroups as a partly filled
+  // extra round (a fixed 8 per CU was 1.02x slower on 16384 x 14336, 1.07x on the 6:8 lift at 16384 tokens).
   const bool pipe = M > 16 * (int64_t)num_cus_p();
   const int m = (int)M, k = (int)K, kc = (int)Kc;
 #define SS_QL(V_) \
-  do { if (pipe) hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, true>), dim3((unsigned)(resident_per_cu<TIn, FP8, N, V_>(lds) * num_cus_p())), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); else hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, false>), dim3((unsigned)M), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); } while (0)
+  do { if (pipe) hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, true>), dim3((unsigned)(std::min(occupancy_p((const void*)quant_lift_kernel<TIn, FP8, N, V_, true>, kBlock, lds), 8) * num_cus_p())), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); else hipLaunchKernelGGL((quant_lift_kernel<TIn, FP8, N, V_, false>), dim3((unsigned)M), dim3(kBlock), lds, st, X, ldx, m, k, Xq, ldq, kc, sx); } while (0)
   if (vpt <= 1) SS_QL(1);
   else if (vpt <= 2) SS_QL(2);
   else if (vpt <= 4) SS_QL(4);
