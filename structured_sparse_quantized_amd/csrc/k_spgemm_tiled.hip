@@ -542,7 +542,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_kernel(int R, int C, int KS
     // padded steps (>= KS) hold zero values; their dense slices re-read step KS-1
     auto load_step = [&](int slot, int k) {
       const int kb = min(k, KS - 1);
-      A[slot] = *reinterpret_cast<const tiled::v4i*>(pa + (int64_t)k * 1024);
+      // the weights stream through once per call: non-temporal loads (1.04-1.10x at 1-16 tokens on
+      // Qwen2.5-7B-shaped layers; the token rows, read by every workgroup, stay cached)
+      A[slot] = __builtin_nontemporal_load(reinterpret_cast<const tiled::v4i*>(pa + (int64_t)k * 1024));
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
         B[slot][c][0] = *reinterpret_cast<const tiled::v4i*>(pb[c] + (int64_t)kb * 128);
@@ -790,7 +792,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fused_decode_kernel(int R, int M, 
     MV mcur, mnxt;
     auto load_step = [&](int slot, int k) {
       const int kb = min(k, KS - 1);
-      A[slot] = *reinterpret_cast<const tiled::v4i*>(pa + (int64_t)k * 1024);
+      A[slot] = __builtin_nontemporal_load(reinterpret_cast<const tiled::v4i*>(pa + (int64_t)k * 1024));
       B[slot][0] = *reinterpret_cast<const SS_LDS tiled::v4i*>(pb + kb * 128);
       B[slot][1] = *reinterpret_cast<const SS_LDS tiled::v4i*>(pb + kb * 128 + 64);
     };
